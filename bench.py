@@ -1,0 +1,205 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one chunkwise prefill pass (gate + intra-chunk + inter-chunk, all
+in libkda's HIP kernels) over the mid-size synthetic workload: B=1, H=32,
+T=4096, d_k=d_v=128, bf16 q/k/v/z, fp32 beta/A/state, g_min=-5.  Inputs are
+resident in HBM before timing; a 1 GiB write between steps evicts them from
+the 256 MB Infinity Cache so each step reads HBM (the write is outside the
+per-step event pair).  Prints ONE JSON line with the prefill tokens/s as
+``value``, a ``roofline`` object for the prefill pass, the fp64 CPU oracle
+timed on the host (``cpu_baseline``), and a ``decode`` object with the decode
+steps/s of the B=256 workload (1,000 back-to-back in-place steps).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+CHUNK = 16
+
+
+def prefill_alg_bytes(B, T, H, d, es=2, with_s0=False):
+    """q, k, v, z, o (es bytes each) + beta (fp32) per token-head, S_T (and S0)."""
+    per_tok = (4 * d + d) * es + 4
+    return B * T * H * per_tok + B * H * d * d * 4 * (2 if with_s0 else 1)
+
+
+def prefill_alg_flops(B, T, H, d):
+    """Chunk-form flops (triangular-aware), summed over chunks of 16 (last short)."""
+    total = 0
+    n_full, rem = divmod(T, CHUNK)
+    for C, n in ((CHUNK, n_full), (rem, 1 if rem else 0)):
+        per = (6 * C * d * d + C * (C - 1) * d + C * (C + 1) * d + C * (C - 1) * 2 * d
+               + C * (C + 1) * d + d * d)
+        total += per * n
+    return total * B * H
+
+
+def decode_alg_bytes(B, H, d, es=2):
+    """S read + write (fp32) + q, k, v, z, o (es) + beta per (b, h)."""
+    return B * H * (2 * d * d * 4 + 5 * d * es + 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the KDA units (b, h) are independent and shard "
+              "without communication, so run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_recurrence_05_amd as kda
+    from linear_attention_recurrence_05_amd.inputs import (DECODE_CONFIG, PREFILL_CONFIGS,
+                                                            config_inputs, decode_state,
+                                                            decode_step_inputs)
+
+    dev = torch.device("cuda:0")
+    kda.lib()
+    cfg = PREFILL_CONFIGS[1]
+    B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.dk
+    x = config_inputs(1, dev)
+    o = torch.empty(B, T, H, d, dtype=cfg.dtype, device=dev)
+    ST = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    nb = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, cfg.dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_chunk_prefill(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
+                              x["S0"], o, ST, ws, stream)
+
+    for _ in range(args.warmup):
+        flush.zero_()
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        flush.zero_()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    ms = sum(times_ms) / len(times_ms)
+    # back-to-back (cache-warm) for reference
+    torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(args.steps):
+        step()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+
+    tokens = B * T
+    alg_b = prefill_alg_bytes(B, T, H, d)
+    alg_f = prefill_alg_flops(B, T, H, d)
+    gbs = alg_b / (ms * 1e-3) / 1e9
+    tflops = alg_f / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "KDA prefill tokens/s (decode steps/s in 'decode'); % of MFMA/HBM roofline",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "ms_per_step_median": times_ms[len(times_ms) // 2],
+        "ms_per_step_warm": warm_ms,
+        "wall_s_timed_region": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1); v,z N(0,1); beta=sigmoid(N(0,1)); A~U(-1,1))",
+        "config": {"workload": "mid_prefill_B1_H32_T4096_d128_bf16", "B": B, "T": T, "H": H,
+                   "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": -5.0, "S0": "zeros",
+                   "parallelism": "single GPU", "workspace_bytes": nb},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "prefill pass (all of its kernels)",
+                     "alg_bytes_per_step": alg_b,
+                     "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+                     "alg_flops_per_step": alg_f},
+    }
+
+    if not args.no_decode:
+        c = DECODE_CONFIG
+        gen, A, S = decode_state(c.B, c.H, c.dk, c.dv, seed=c.seed, s0_std=c.s0_std, device=dev)
+        n = args.decode_steps
+        stg = decode_step_inputs(gen, c.B, c.H, c.dk, c.dv, c.dtype, dev, steps=n)
+        od = torch.empty(c.B, c.H, c.dv, dtype=c.dtype, device=dev)
+        S_save = S.clone()
+
+        def run_decode():
+            for i in range(n):
+                kda.kda_decode_step(stg["q"][i], stg["k"][i], stg["v"][i], stg["z"][i],
+                                    stg["beta"][i], A, -5.0, S, od, stream)
+
+        run_decode()   # warm-up pass
+        reps = []
+        for _ in range(3):
+            S.copy_(S_save)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_decode()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1))
+        dms = sorted(reps)[1] / n
+        db = decode_alg_bytes(c.B, c.H, c.dk)
+        dgbs = db / (dms * 1e-3) / 1e9
+        line["decode"] = {
+            "metric": "KDA decode steps/s", "value": 1e3 / dms, "unit": "steps/s",
+            "ms_per_step": dms, "steps": n, "repetitions": 3,
+            "config": {"workload": "decode_B256_H32_d128_bf16_state_fp32", "B": c.B, "H": c.H,
+                       "d_k": c.dk, "d_v": c.dv},
+            "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dgbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "decode_kernel", "alg_bytes_per_step": db},
+        }
+        del stg, S, S_save
+
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        xc = {kk: (vv.cpu() if hasattr(vv, "cpu") else vv) for kk, vv in x.items()}
+        t0 = time.perf_counter()
+        oracle.prefill(xc["q"], xc["k"], xc["v"], xc["z"], xc["beta"], xc["A"], xc["g_min"],
+                       xc["S0"], nthreads=threads)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": tokens / dt, "unit": "tokens/s", "cores": min(threads, B * H),
+            "kind": "oracle",
+            "sample": f"the whole workload (B={B}, T={T}, H={H}, d={d}) once, fp64 token-by-token "
+                      f"recurrence, OpenMP over the {B * H} heads, {threads} threads available",
+            "seconds": dt,
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) implementation of the Kimi
+ * Delta Attention (KDA) gated delta-rule recurrence.
+ *
+ * The operation (per batch row b and head h, state S in R^{dk x dv}, row
+ * index = key channel):
+ *
+ *   g_t = g_min * Sigmoid(exp(A_h) * z_t)        lower-bounded log-decay, dk
+ *   a_t = exp(g_t)                               channel-wise retention
+ *   S_t = (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t
+ *
+ * Sources: dev.to "Kimi K3 Architecture: Scaling 2.8T Parameters for
+ * Long-Context Multimodal MoE", section "The Sequence Bottleneck: Hybrid KDA
+ * and Gated MLA" (state shape, retention and delta-strength domains, the gate
+ * equation, g_min = -5, 16-token tiles, chunkwise parallel execution);
+ * terrencekim.net "Kimi K3 - Sparsity Mechanics ...", section 2, Temporal
+ * Sequence card (fixed-size associative memory, Householder-style delta
+ * update, channel-wise forget gate).  The pages state the update in words;
+ * the algebraic form above is the reading implemented here: decay, then
+ * erase-and-write, output from the updated state, no 1/sqrt(d) scale, no
+ * output gate or normalisation.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensor arguments are DEVICE pointers, caller-owned; the library never
+ *   allocates, frees or synchronises.  Calls enqueue work on `stream`
+ *   (a hipStream_t; NULL = the default stream) and return at once.
+ * - Layouts are contiguous row-major:
+ *     q, k, z   [B, T, H, d_k]      v, o [B, T, H, d_v]
+ *     beta      [B, T, H]  fp32     A    [H] fp32
+ *     S0, S_T   [B, H, d_k, d_v] fp32 (row = key channel)
+ *   Decode uses T = 1: q, k, z [B, H, d_k], v, o [B, H, d_v], beta [B, H].
+ * - `dt` gives the element type of q, k, v, z and o (KDA_F32 or KDA_BF16);
+ *   beta, A, g_min and the state are always fp32.  Accumulation is fp32.
+ * - Supported head sizes: (d_k, d_v) in {(32, 32), (128, 128)}.
+ * - beta is used as given (expected in (0, 1)); q and k are used as given
+ *   (no normalisation inside).  g_min must lie in [-5, 0]: the chunked form
+ *   rescales 16-token tiles by factors up to exp(-16 g_min), which must stay
+ *   finite in fp32/bf16 (exp(80) < FLT_MAX).
+ * - Alignment: q, k, v, z, o, the decode state S and the workspace must be
+ *   16-byte aligned (they are read with 16-byte vector accesses); beta, A,
+ *   S0, S_T and the diagnostic outputs need 4-byte alignment.
+ * - Every argument is validated on the host BEFORE any HIP call; on error
+ *   nothing is enqueued, the status is returned and a detail string is kept
+ *   for kda_last_error() (thread-local).  No entry point aborts, exits or
+ *   throws across the ABI.  A failed kernel launch returns KDA_ERR_HIP.
+ * - Results are bitwise deterministic for identical inputs and launch
+ *   (no atomics, fixed reduction orders).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+/* Tokens per chunk of the chunkwise prefill (the pages' 16-token tiles). */
+#define KDA_CHUNK 16
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL            */
+    KDA_ERR_INVALID_SHAPE = 2,       /* B, T or H < 1, or sizes overflow      */
+    KDA_ERR_INVALID_VALUE = 3,       /* g_min outside [-5, 0] or not finite   */
+    KDA_ERR_UNSUPPORTED = 4,         /* head size or dtype not supported      */
+    KDA_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned      */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace below the queried size      */
+    KDA_ERR_ALIASING = 7,            /* an output overlaps an input illegally */
+    KDA_ERR_HIP = 8                  /* the HIP runtime reported an error     */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static, human-readable name of a status code ("KDA_OK", ...). */
+const char *kda_status_string(kda_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none).
+ * The pointer stays valid until the next libkda call on this thread. */
+const char *kda_last_error(void);
+
+/* Bytes of device workspace kda_chunk_prefill needs for these sizes.
+ * 0 means the call needs none (workspace may then be NULL).  Returns 0 for
+ * arguments kda_chunk_prefill would reject. */
+size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v,
+                                         kda_dtype dt);
+
+/* Chunkwise prefill over T tokens (any T >= 1; chunks of KDA_CHUNK tokens
+ * start at t = 0 and the last may be short).  Computes o for every token and,
+ * if S_T != NULL, the final state.
+ *   S0 == NULL      : the initial state is zero.
+ *   S_T may alias S0 exactly (in-place continuation); no other overlap of
+ *   outputs (o, S_T, workspace) with inputs is allowed.
+ *   workspace       : device memory of at least
+ *                     kda_chunk_prefill_workspace_bytes(...) bytes, used as
+ *                     scratch for this call only (may be NULL if that is 0).
+ * The execution plan (one fused kernel, or an intra-chunk kernel writing the
+ * workspace followed by an inter-chunk kernel) is a function of the sizes.
+ * For tests and tuning the environment variable KDA_PREFILL_PLAN overrides
+ * it: "split", or "fused:<n>" with n value columns per workgroup
+ * (16, 32, 64, or 128 <= d_v; fp32 with d = 128: at most 64).  The workspace
+ * query honours the same variable, so read both under one setting.
+ * The chained result of two calls (the second with S0 = the first's S_T)
+ * equals one call over the concatenated tokens up to rounding. */
+kda_status kda_chunk_prefill(const void *q, const void *k, const void *v,
+                             const void *z, const float *beta, const float *A,
+                             float g_min, const float *S0, void *o, float *S_T,
+                             int B, int T, int H, int d_k, int d_v, kda_dtype dt,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* One recurrent decode step: for every (b, h) the state S [B, H, d_k, d_v]
+ * (fp32) is read once and overwritten in place with S_t; o receives
+ * S_t^T q_t.  o must not overlap S or the inputs. */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const void *z, const float *beta, const float *A,
+                           float g_min, float *S, void *o, int B, int H,
+                           int d_k, int d_v, kda_dtype dt, void *stream);
+
+/* Diagnostic export of the gate stage: G [B, T, H, d_k] fp32 receives the
+ * chunk-local inclusive cumulative log-decay
+ *   G_t = sum of g_s over s from the start of t's KDA_CHUNK-token chunk to t,
+ * (dev.to page, "The Sequence Bottleneck": per-16-token cumulative log-decay
+ * in (-80, 0) for g_min = -5).  G must not overlap z. */
+kda_status kda_gate_chunk_cumsum(const void *z, const float *A, float g_min,
+                                 float *G, int B, int T, int H, int d_k,
+                                 kda_dtype dt, void *stream);
+
+/* Diagnostic export of the intra-chunk stage, computed by the same device
+ * code the prefill runs.  For chunk n of (b, h), with G the chunk-local
+ * cumulative log-decay, Kt = k e^{G}, Kh = k e^{-G}, Qt = q e^{G} (rows =
+ * the chunk's tokens, L <= KDA_CHUNK of them; rows past L are zero-padded):
+ *   Tm    [B, H, NC, 16, 16] fp32 : (I + tril_{-1}(Diag(beta) Kt Kh^T))^{-1} Diag(beta)
+ *   Aqk   [B, H, NC, 16, 16] fp32 : tril_0(Qt Kh^T)
+ *   gamma [B, H, NC, d_k]    fp32 : e^{G at the chunk's last token}
+ * where NC = ceil(T / KDA_CHUNK).  Tm and Aqk are the products as the MFMA
+ * path forms them (operands in the input precision), before any cast. */
+kda_status kda_intra_chunk(const void *q, const void *k, const void *z,
+                           const float *beta, const float *A, float g_min,
+                           float *Tm, float *Aqk, float *gamma, int B, int T,
+                           int H, int d_k, kda_dtype dt, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,30 @@
+"""Python binding of libkda, the gfx950 KDA gated delta-rule recurrence.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/kda.h``.  PyTorch supplies device memory
+and streams.  If ``libkda.so`` has not been built, importing works but every
+call raises :class:`KdaLibraryMissing` -- there is no fallback path.
+
+Functions named like the C entry points take torch tensors in the layouts
+``kda.h`` documents and pass their device pointers through unchanged:
+
+    kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace, stream)
+    kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream)
+    kda_gate_chunk_cumsum(z, A, g_min, G, stream)
+    kda_intra_chunk(q, k, z, beta, A, g_min, Tm, Aqk, gamma, stream)
+    kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype)
+
+``chunk_prefill`` and ``decode_step`` additionally allocate the outputs (and
+the workspace) with ``torch.empty`` before calling the same entry points.
+"""
+from __future__ import annotations
+
+from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KdaError, KdaLibraryMissing, abi_version,
+                   chunk_prefill, decode_step, kda_chunk_prefill,
+                   kda_chunk_prefill_workspace_bytes, kda_decode_step, kda_gate_chunk_cumsum,
+                   kda_intra_chunk, lib, library_path, status_string)
+
+__all__ = ["KDA_BF16", "KDA_CHUNK", "KDA_F32", "KdaError", "KdaLibraryMissing", "abi_version",
+           "chunk_prefill", "decode_step", "kda_chunk_prefill",
+           "kda_chunk_prefill_workspace_bytes", "kda_decode_step", "kda_gate_chunk_cumsum",
+           "kda_intra_chunk", "lib", "library_path", "status_string"]

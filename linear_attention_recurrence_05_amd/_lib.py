@@ -1,0 +1,168 @@
+"""ctypes marshalling for libkda (see ``include/kda.h`` for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import library_path
+
+KDA_F32 = 0
+KDA_BF16 = 1
+KDA_CHUNK = 16
+
+_STATUS = ["KDA_OK", "KDA_ERR_NULL_POINTER", "KDA_ERR_INVALID_SHAPE", "KDA_ERR_INVALID_VALUE",
+           "KDA_ERR_UNSUPPORTED", "KDA_ERR_MISALIGNED", "KDA_ERR_WORKSPACE_TOO_SMALL",
+           "KDA_ERR_ALIASING", "KDA_ERR_HIP"]
+
+
+class KdaLibraryMissing(RuntimeError):
+    """libkda.so is not built; there is no fallback implementation."""
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, detail: str, where: str):
+        self.status = status
+        name = _STATUS[status] if 0 <= status < len(_STATUS) else f"status {status}"
+        super().__init__(f"{where}: {name}: {detail}")
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+_SIGNATURES = {
+    "kda_abi_version": ([], ctypes.c_int),
+    "kda_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "kda_last_error": ([], ctypes.c_char_p),
+    "kda_chunk_prefill_workspace_bytes": ([_i, _i, _i, _i, _i, _i], ctypes.c_size_t),
+    "kda_chunk_prefill": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6
+                          + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "kda_decode_step": ([_vp] * 6 + [ctypes.c_float, _vp, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
+    "kda_gate_chunk_cumsum": ([_vp, _vp, ctypes.c_float, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
+    "kda_intra_chunk": ([_vp] * 5 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 5 + [_vp],
+                        ctypes.c_int),
+}
+
+
+def lib():
+    """The loaded libkda (raises KdaLibraryMissing if it was never built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise KdaLibraryMissing(
+                f"{path} not found: build it with `python -m linear_attention_recurrence_05_amd.build`")
+        L = ctypes.CDLL(path)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().kda_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KdaError(status, lib().kda_last_error().decode(), where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v/z/o must be bfloat16 or float32, got {t.dtype}")
+
+
+def _require_contiguous(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+    return int(lib().kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, code))
+
+
+def kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace=None, stream=None):
+    """C entry point kda_chunk_prefill on torch tensors (layouts of kda.h)."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0, o=o, S_T=S_T)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                 float(g_min), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
+                                 _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "kda_chunk_prefill")
+
+
+def kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream=None):
+    """C entry point kda_decode_step on torch tensors; S is updated in place."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S=S, o=o)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                               float(g_min), _ptr(S), _ptr(o), B, H, dk, dv, _dtype_code(q),
+                               _stream(stream))
+    _check(st, "kda_decode_step")
+
+
+def kda_gate_chunk_cumsum(z, A, g_min, G, stream=None):
+    _require_contiguous(z=z, A=A, G=G)
+    B, T, H, dk = z.shape
+    st = lib().kda_gate_chunk_cumsum(_ptr(z), _ptr(A), float(g_min), _ptr(G), B, T, H, dk,
+                                     _dtype_code(z), _stream(stream))
+    _check(st, "kda_gate_chunk_cumsum")
+
+
+def kda_intra_chunk(q, k, z, beta, A, g_min, Tm, Aqk, gamma, stream=None):
+    _require_contiguous(q=q, k=k, z=z, beta=beta, A=A, Tm=Tm, Aqk=Aqk, gamma=gamma)
+    B, T, H, dk = q.shape
+    st = lib().kda_intra_chunk(_ptr(q), _ptr(k), _ptr(z), _ptr(beta), _ptr(A), float(g_min),
+                               _ptr(Tm), _ptr(Aqk), _ptr(gamma), B, T, H, dk, _dtype_code(q),
+                               _stream(stream))
+    _check(st, "kda_intra_chunk")
+
+
+# ----------------------------------------------------------------- allocating helpers
+
+def chunk_prefill(q, k, v, z, beta, A, g_min=-5.0, S0=None, want_state=True, stream=None):
+    """Allocate o (and S_T, workspace) with torch.empty and run kda_chunk_prefill.
+
+    Returns (o, S_T or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
+    nbytes = kda_chunk_prefill_workspace_bytes(B, T, H, dk, dv, q.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, ws, stream)
+    return o, S_T
+
+
+def decode_step(q, k, v, z, beta, A, S, g_min=-5.0, stream=None):
+    """Allocate o and run kda_decode_step (S updated in place).  Returns o."""
+    o = torch.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=q.dtype, device=q.device)
+    kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream)
+    return o

@@ -1,0 +1,208 @@
+// kda_api.hip -- the C ABI declared in include/kda.h: argument validation
+// (entirely on the host, before any HIP call), error reporting and dispatch
+// to the kernel launchers.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+kda_status ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+struct Range {
+    const char* name;
+    const void* p;
+    size_t bytes;
+    unsigned align;   // required alignment in bytes
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned(const void* p, unsigned a) { return ((uintptr_t)p & (uintptr_t)(a - 1)) == 0; }
+
+kda_status check_common(int d_k, int d_v, kda_dtype dt, float g_min) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "dtype %d is not KDA_F32 or KDA_BF16", (int)dt);
+    if (!(d_k == d_v && (d_k == 32 || d_k == 128)))
+        return fail(KDA_ERR_UNSUPPORTED, "(d_k, d_v) = (%d, %d); supported: (32, 32), (128, 128)", d_k, d_v);
+    if (!std::isfinite(g_min) || g_min < -5.0f || g_min > 0.0f)
+        return fail(KDA_ERR_INVALID_VALUE, "g_min = %g outside [-5, 0]", (double)g_min);
+    return KDA_OK;
+}
+
+// Checks a list of tensor ranges for NULL (when required) and alignment.
+kda_status check_ptrs(const Range* r, int n, const bool* required) {
+    for (int i = 0; i < n; ++i) {
+        if (!r[i].p) {
+            if (required[i]) return fail(KDA_ERR_NULL_POINTER, "%s is NULL", r[i].name);
+            continue;
+        }
+        if (!aligned(r[i].p, r[i].align))
+            return fail(KDA_ERR_MISALIGNED, "%s is not %u-byte aligned", r[i].name, r[i].align);
+    }
+    return KDA_OK;
+}
+
+kda_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape check shared by prefill-style calls; returns element counts.
+kda_status check_shape(int B, int T, int H, int d, size_t& n_tok_el, size_t& n_tok) {
+    if (B < 1 || T < 1 || H < 1) return fail(KDA_ERR_INVALID_SHAPE, "B=%d T=%d H=%d must all be >= 1", B, T, H);
+    const unsigned long long tok = (unsigned long long)B * (unsigned long long)T * (unsigned long long)H;
+    if ((long long)B * H > (1LL << 26) || tok > (1ULL << 40))
+        return fail(KDA_ERR_INVALID_SHAPE, "B*T*H = %llu is too large", tok);
+    n_tok = (size_t)tok;
+    n_tok_el = n_tok * (size_t)d;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER";
+        case KDA_ERR_INVALID_SHAPE: return "KDA_ERR_INVALID_SHAPE";
+        case KDA_ERR_INVALID_VALUE: return "KDA_ERR_INVALID_VALUE";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+        case KDA_ERR_ALIASING: return "KDA_ERR_ALIASING";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, kda_dtype dt) {
+    size_t a, b;
+    if (check_common(d_k, d_v, dt, -5.0f) != KDA_OK || check_shape(B, T, H, d_k, a, b) != KDA_OK) return 0;
+    return kda::choose_plan(B, T, H, d_k, dt == KDA_BF16).ws_bytes;
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* z,
+                             const float* beta, const float* A, float g_min, const float* S0,
+                             void* o, float* S_T, int B, int T, int H, int d_k, int d_v,
+                             kda_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    size_t nel, ntok;
+    if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t st_bytes = (size_t)B * H * d_k * d_v * sizeof(float);
+    const kda::PlanInfo plan = kda::choose_plan(B, T, H, d_k, dt == KDA_BF16);
+    const Range r[] = {{"q", q, nel * es, 16},          {"k", k, nel * es, 16},
+                       {"v", v, nel * es, 16},          {"z", z, nel * es, 16},
+                       {"beta", beta, ntok * 4, 4},     {"A", A, (size_t)H * 4, 4},
+                       {"S0", S0, st_bytes, 4},         {"o", o, nel * es, 16},
+                       {"S_T", S_T, st_bytes, 4},       {"workspace", workspace, plan.ws_bytes, 16}};
+    const bool req[] = {true, true, true, true, true, true, false, true, false, plan.ws_bytes > 0};
+    if ((s = check_ptrs(r, 10, req)) != KDA_OK) return s;
+    if (workspace_bytes < plan.ws_bytes)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    plan.ws_bytes);
+    // outputs (o, S_T, workspace) against every other range; S_T == S0 exactly is allowed
+    for (int out : {7, 8, 9}) {
+        for (int i = 0; i < 10; ++i) {
+            if (i == out) continue;
+            if (out == 8 && i == 6 && S_T == S0) continue;
+            if (overlap(r[out], r[i]))
+                return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
+        }
+    }
+    kda::PrefillArgs a{q, k, v, z, beta, A, g_min, S0, o, S_T, B, T, H, d_k, dt == KDA_BF16};
+    return hip_status(kda::launch_prefill(a, plan, workspace, (hipStream_t)stream), "kda_chunk_prefill launch");
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* z,
+                           const float* beta, const float* A, float g_min, float* S, void* o,
+                           int B, int H, int d_k, int d_v, kda_dtype dt, void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    size_t nel, ntok;
+    if ((s = check_shape(B, 1, H, d_k, nel, ntok)) != KDA_OK) return s;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const Range r[] = {{"q", q, nel * es, 16},      {"k", k, nel * es, 16},   {"v", v, nel * es, 16},
+                       {"z", z, nel * es, 16},      {"beta", beta, ntok * 4, 4},
+                       {"A", A, (size_t)H * 4, 4},  {"S", S, (size_t)B * H * d_k * d_v * sizeof(float), 16},
+                       {"o", o, nel * es, 16}};
+    const bool req[] = {true, true, true, true, true, true, true, true};
+    if ((s = check_ptrs(r, 8, req)) != KDA_OK) return s;
+    for (int out : {6, 7})
+        for (int i = 0; i < 8; ++i)
+            if (i != out && overlap(r[out], r[i]))
+                return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
+    kda::DecodeArgs a{q, k, v, z, beta, A, g_min, S, o, B, H, d_k, dt == KDA_BF16};
+    return hip_status(kda::launch_decode(a, (hipStream_t)stream), "kda_decode_step launch");
+}
+
+kda_status kda_gate_chunk_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,
+                                 int H, int d_k, kda_dtype dt, void* stream) {
+    kda_status s = check_common(d_k, d_k, dt, g_min);
+    if (s != KDA_OK) return s;
+    size_t nel, ntok;
+    if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const Range r[] = {{"z", z, nel * es, 16}, {"A", A, (size_t)H * 4, 4}, {"G", G, nel * 4, 4}};
+    const bool req[] = {true, true, true};
+    if ((s = check_ptrs(r, 3, req)) != KDA_OK) return s;
+    if (overlap(r[2], r[0]) || overlap(r[2], r[1])) return fail(KDA_ERR_ALIASING, "G overlaps an input");
+    return hip_status(kda::launch_gate_cumsum(z, A, g_min, G, B, T, H, d_k, dt == KDA_BF16, (hipStream_t)stream),
+                      "kda_gate_chunk_cumsum launch");
+}
+
+kda_status kda_intra_chunk(const void* q, const void* k, const void* z, const float* beta,
+                           const float* A, float g_min, float* Tm, float* Aqk, float* gamma, int B,
+                           int T, int H, int d_k, kda_dtype dt, void* stream) {
+    kda_status s = check_common(d_k, d_k, dt, g_min);
+    if (s != KDA_OK) return s;
+    size_t nel, ntok;
+    if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t nchunk = (size_t)B * H * ((T + KDA_CHUNK - 1) / KDA_CHUNK);
+    const Range r[] = {{"q", q, nel * es, 16},       {"k", k, nel * es, 16},         {"z", z, nel * es, 16},
+                       {"beta", beta, ntok * 4, 4}, {"A", A, (size_t)H * 4, 4},    {"Tm", Tm, nchunk * 1024, 4},
+                       {"Aqk", Aqk, nchunk * 1024, 4}, {"gamma", gamma, nchunk * d_k * 4, 4}};
+    const bool req[] = {true, true, true, true, true, true, true, true};
+    if ((s = check_ptrs(r, 8, req)) != KDA_OK) return s;
+    for (int out : {5, 6, 7})
+        for (int i = 0; i < 8; ++i)
+            if (i != out && overlap(r[out], r[i]))
+                return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
+    return hip_status(kda::launch_intra_diag(q, k, z, beta, A, g_min, Tm, Aqk, gamma, B, T, H, d_k,
+                                             dt == KDA_BF16, (hipStream_t)stream),
+                      "kda_intra_chunk launch");
+}
+
+}  // extern "C"

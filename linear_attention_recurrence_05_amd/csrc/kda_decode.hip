@@ -1,0 +1,128 @@
+// kda_decode.hip -- one recurrent KDA decode step, state updated in place.
+//
+// Per (b, h), with S' = Diag(a) S (a = exp(g_min Sigmoid(e^{A_h} z))):
+//   p = S'^T k,  r = S'^T q          (two reductions over key channels)
+//   e = beta (v - p)                 (delta-rule correction, d_v values)
+//   S <- S' + k e^T                  (= (I - beta k k^T) S' + beta k v^T)
+//   o  = S^T q = r + (q . k) e
+// (dev.to "Kimi K3 Architecture ...", "The Sequence Bottleneck": state shape,
+// retention/delta domains and the gate equation; terrencekim.net "Kimi K3 -
+// Sparsity Mechanics ...", section 2: fixed-size state, constant decode
+// memory.)
+//
+// The step is HBM-bound (S is read and written once: 2 * 4 * d_k * d_v bytes
+// against ~7 d_k d_v flops), so the kernel is laid out for streaming: one
+// workgroup per (b, h); each thread owns 4 adjacent value columns of
+// RPT = d_k / 8 key rows, so every wave instruction moves 1 KiB (d = 128) of
+// S with 16-byte accesses.  S is held in registers between the read and the
+// write, the two reductions come from the same read, and the update is
+// written back with non-temporal stores.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <typename E, int D>
+__global__ __launch_bounds__(2 * D) void decode_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
+    float g_min, float* __restrict__ S, E* __restrict__ o, int H) {
+    constexpr int NT = 2 * D;          // threads
+    constexpr int CG = D / 4;          // column groups of 4 (float4)
+    constexpr int RG = NT / CG;        // row groups (= 8)
+    constexpr int RPT = D / RG;        // rows per thread
+    constexpr int NWAVE = NT / kWave;
+    static_assert(RG == 8, "layout assumes 8 row groups");
+
+    __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
+    __shared__ float s_red[NWAVE][CG][9];
+
+    const int tid = threadIdx.x;
+    const size_t unit = blockIdx.x;    // b * H + h
+    const int h = (int)(unit % (size_t)H);
+    const size_t vec = unit * (size_t)D;
+
+    if (tid < D) {
+        GateConsts gc = make_gate(A[h], g_min);
+        float zz = to_f32(z[vec + tid]);
+        s_alpha[tid] = gate_alpha(gc, gate_sigmoid(gc, zz));
+        s_k[tid] = to_f32(k[vec + tid]);
+        s_q[tid] = to_f32(q[vec + tid]);
+        s_v[tid] = to_f32(v[vec + tid]);
+    }
+    __syncthreads();
+
+    const int cg = tid % CG, rg = tid / CG;
+    f32x4* Sv = reinterpret_cast<f32x4*>(S + unit * (size_t)D * D);
+    f32x4 st[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&Sv[(rg + RG * i) * CG + cg]);
+
+    float red[9];
+#pragma unroll
+    for (int x = 0; x < 9; ++x) red[x] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int c = rg + RG * i;
+        const float a = s_alpha[c], kc = s_k[c], qc = s_q[c];
+        st[i] *= a;                                  // S' = Diag(a) S
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            red[x] += kc * st[i][x];                 // p = S'^T k
+            red[4 + x] += qc * st[i][x];             // r = S'^T q
+        }
+        red[8] += qc * kc;                           // q . k (same in every column group)
+    }
+    // reduce over the row groups: first inside the wave (lanes with the same
+    // column group), then across waves through LDS, in a fixed order.
+#pragma unroll
+    for (int off = CG; off < kWave; off <<= 1)
+#pragma unroll
+        for (int x = 0; x < 9; ++x) red[x] += __shfl_xor(red[x], off);
+    const int wave = tid / kWave, lane = tid % kWave;
+    if (lane < CG) {
+#pragma unroll
+        for (int x = 0; x < 9; ++x) s_red[wave][lane][x] = red[x];
+    }
+    __syncthreads();
+    float tot[9];
+#pragma unroll
+    for (int x = 0; x < 9; ++x) {
+        tot[x] = s_red[0][cg][x];
+#pragma unroll
+        for (int w = 1; w < NWAVE; ++w) tot[x] += s_red[w][cg][x];
+    }
+    const float b = beta[unit];
+    f32x4 e;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) e[x] = b * (s_v[4 * cg + x] - tot[x]);
+    if (rg == 0) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o[vec + 4 * cg + x] = from_f32<E>(tot[4 + x] + tot[8] * e[x]);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int c = rg + RG * i;
+        const float kc = s_k[c];
+        f32x4 nv = st[i] + kc * e;                   // S = S' + k e^T
+        __builtin_nontemporal_store(nv, &Sv[c * CG + cg]);
+    }
+}
+
+template <typename E, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+    const size_t units = (size_t)a.B * a.H;
+    hipLaunchKernelGGL((decode_kernel<E, D>), dim3((unsigned)units), dim3(2 * D), 0, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.z, a.beta, a.A,
+                       a.g_min, a.S, (E*)a.o, a.H);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+    if (a.is_bf16) {
+        return a.d == 128 ? launch_decode_t<bf16, 128>(a, stream) : launch_decode_t<bf16, 32>(a, stream);
+    }
+    return a.d == 128 ? launch_decode_t<float, 128>(a, stream) : launch_decode_t<float, 32>(a, stream);
+}
+
+}  // namespace kda

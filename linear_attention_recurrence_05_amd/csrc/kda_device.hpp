@@ -1,0 +1,155 @@
+// kda_device.hpp -- device-side building blocks for the gfx950 KDA kernels:
+// element types, bf16 conversion, MFMA wrappers, lane-layout helpers and the
+// gate arithmetic.
+//
+// Lane layouts (wave64).  A 16x16 fp32 MFMA result ("acc layout") puts in
+// lane l the column j = l % 16 and rows 4*(l/16) + {0,1,2,3}.  Throughout,
+// g = l / 16 is the lane group and the MFMA K index held by a lane is chosen
+// so that the acc layout of one product can feed the next product as its B
+// operand without moving data between lanes (the K order of a contraction is
+// free as long as both operands use the same one).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 16;     // tokens per chunk (the pages' 16-token tiles)
+constexpr int kWave = 64;
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ scalars
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Element <-> fp32.  bf16 is stored as its 16-bit pattern.
+template <typename E> __device__ __forceinline__ float to_f32(E x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+template <typename E> __device__ __forceinline__ E from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// Round to nearest even (the hardware conversion on gfx950).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Gate constants of one head: x = e^{A_h} z, g = g_min Sigmoid(x), a = e^g.
+struct GateConsts {
+    float neg_ea_log2e;    // -e^{A_h} log2(e): exp2(z * this) = e^{-x}
+    float gmin_log2e;      // g_min log2(e):    exp2(s * this) = e^{g}
+    float gmin;
+};
+
+__device__ __forceinline__ GateConsts make_gate(float A_h, float g_min) {
+    GateConsts c;
+    c.neg_ea_log2e = -__expf(A_h) * kLog2e;
+    c.gmin_log2e = g_min * kLog2e;
+    c.gmin = g_min;
+    return c;
+}
+
+// Sigmoid(e^{A_h} z) = 1 / (1 + e^{-x}); overflow of e^{-x} gives 0 and
+// underflow gives 1, which are the limits.
+__device__ __forceinline__ float gate_sigmoid(const GateConsts& c, float z) {
+    return fast_rcp(1.0f + fast_exp2(z * c.neg_ea_log2e));
+}
+
+// Retention a = exp(g_min * s) for a sigmoid value s.
+__device__ __forceinline__ float gate_alpha(const GateConsts& c, float s) {
+    return fast_exp2(s * c.gmin_log2e);
+}
+
+// ------------------------------------------------------------------ buffers
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// and stores past it are dropped (hardware range check on the VGPR offset),
+// which is how short chunks and padded rows are handled without branches.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+template <typename T> __device__ __forceinline__ T buf_load(Rsrc r, int off);
+template <> __device__ __forceinline__ uint32_t buf_load<uint32_t>(Rsrc r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ u32x2 buf_load<u32x2>(Rsrc r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ u32x4 buf_load<u32x4>(Rsrc r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ unsigned short buf_load<unsigned short>(Rsrc r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u16(Rsrc r, int off, unsigned short x) {
+    __builtin_amdgcn_raw_buffer_store_b16(x, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u32(Rsrc r, int off, uint32_t x) {
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, off, 0, 0);
+}
+
+// ------------------------------------------------------------------ lanes
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+// Value of lane `src` (0..3) of this lane's quad (DPP quad_perm broadcast).
+template <int src>
+__device__ __forceinline__ float quad_bcast(float x) {
+    constexpr int ctrl = src | (src << 2) | (src << 4) | (src << 6);
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl,
+                                                              0xF, 0xF, true));
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// 16x16x32 bf16 -> fp32.  A: lane l holds row l%16, eight K values of group
+// l/16; B: lane l holds column l%16, the same eight K values.
+__device__ __forceinline__ f32x4 mma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x16 bf16 -> fp32 (four K values per lane).
+__device__ __forceinline__ f32x4 mma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+// 16x16x4 fp32 (one K value per lane).
+__device__ __forceinline__ f32x4 mma_f32_k4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 pack4(f32x4 x) {
+    bf16x4 r;
+    r[0] = (bf16)x[0]; r[1] = (bf16)x[1]; r[2] = (bf16)x[2]; r[3] = (bf16)x[3];
+    return r;
+}
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+    r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+    r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+    return r;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace kda

@@ -1,0 +1,114 @@
+"""GPU self-consistency properties of libkda that hold at any size."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import linear_attention_recurrence_05_amd as kda
+from linear_attention_recurrence_05_amd.inputs import decode_step_inputs, prefill_inputs
+
+from gpu_common import TOL, need_gpu, plan, rel_err, say
+
+pytestmark = pytest.mark.gpu
+PLANS = ["split", "fused:16", "fused:64"]
+
+
+def run(x, S0="keep"):
+    s0 = x["S0"] if isinstance(S0, str) else S0
+    o, ST = kda.chunk_prefill(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"], s0)
+    torch.cuda.synchronize()
+    return o, ST
+
+
+def slice_t(x, a, b):
+    return {k: (v[:, a:b].contiguous() if k in ("q", "k", "v", "z", "beta") else v) for k, v in x.items()}
+
+
+@pytest.mark.parametrize("p", PLANS)
+def test_bitwise_deterministic(p):
+    dev = need_gpu()
+    x = prefill_inputs(2, 200, 4, 128, 128, torch.bfloat16, seed=11, s0_std=0.1, device=dev)
+    with plan(p):
+        o1, S1 = run(x)
+        o2, S2 = run(x)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("p", PLANS)
+def test_continuation_on_chunk_boundary_is_exact(p):
+    """prefill(T1) then prefill(T2, S0 = S_T1) == prefill(T1 + T2) bitwise when
+    T1 is a multiple of 16 (the chunk grid is the same)."""
+    dev = need_gpu()
+    x = prefill_inputs(1, 160, 3, 128, 128, torch.bfloat16, seed=12, s0_std=0.1, device=dev)
+    with plan(p):
+        o, ST = run(x)
+        oa, Sa = run(slice_t(x, 0, 64))
+        ob, Sb = run(slice_t(x, 64, 160), S0=Sa)
+    assert torch.equal(oa, o[:, :64]) and torch.equal(ob, o[:, 64:]) and torch.equal(Sb, ST)
+
+
+def test_continuation_off_boundary_is_close():
+    dev = need_gpu()
+    x = prefill_inputs(1, 150, 2, 32, 32, torch.float32, seed=13, s0_std=0.1, device=dev)
+    o, ST = run(x)
+    oa, Sa = run(slice_t(x, 0, 37))
+    ob, Sb = run(slice_t(x, 37, 150), S0=Sa)
+    e = max(rel_err(torch.cat([oa, ob], 1), o.cpu().double().numpy()),
+            rel_err(Sb, ST.cpu().double().numpy()))
+    say(f"continuation off the chunk grid: {e:.2e}")
+    assert e < 1e-5
+
+
+@pytest.mark.parametrize("p", PLANS)
+def test_state_in_place(p):
+    """S_T aliasing S0 gives the same result as separate buffers."""
+    dev = need_gpu()
+    x = prefill_inputs(2, 70, 3, 128, 128, torch.bfloat16, seed=14, s0_std=0.1, device=dev)
+    with plan(p):
+        o, ST = run(x)
+        S = x["S0"].clone()
+        o2 = torch.empty_like(o)
+        nb = kda.kda_chunk_prefill_workspace_bytes(2, 70, 3, 128, 128, torch.bfloat16)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        kda.kda_chunk_prefill(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], -5.0, S, o2, S, ws)
+        torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, ST)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_decode_steps_equal_prefill(d):
+    """16 decode steps from S0 == a 16-token prefill from S0 (fp32 inputs)."""
+    dev = need_gpu()
+    x = prefill_inputs(2, 16, 3, d, d, torch.float32, seed=15, s0_std=0.1, device=dev)
+    o, ST = run(x)
+    S = x["S0"].clone()
+    outs = []
+    for t in range(16):
+        outs.append(kda.decode_step(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(),
+                                    x["v"][:, t].contiguous(), x["z"][:, t].contiguous(),
+                                    x["beta"][:, t].contiguous(), x["A"], S))
+    torch.cuda.synchronize()
+    od = torch.stack(outs, 1)
+    e = max(rel_err(od, o.cpu().double().numpy()), rel_err(S, ST.cpu().double().numpy()))
+    say(f"decode x16 vs prefill d={d}: {e:.2e}")
+    assert e < 1e-4
+
+
+@pytest.mark.parametrize("p", PLANS)
+def test_nan_stays_in_its_head(p):
+    dev = need_gpu()
+    x = prefill_inputs(2, 48, 4, 128, 128, torch.bfloat16, seed=16, s0_std=0.1, device=dev)
+    with plan(p):
+        o, ST = run(x)
+        xv = dict(x)
+        xv["v"] = x["v"].clone()
+        xv["v"][1, 20, 2, 5] = float("nan")
+        o2, ST2 = run(xv)
+    bad = torch.zeros(2, 4, dtype=torch.bool)
+    bad[1, 2] = True
+    for b in range(2):
+        for h in range(4):
+            if bad[b, h]:
+                assert not torch.isfinite(o2[b, :, h]).all()
+            else:
+                assert torch.equal(o2[b, :, h], o[b, :, h]) and torch.equal(ST2[b, h], ST[b, h])
