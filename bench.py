@@ -50,6 +50,20 @@ def decode_alg_bytes(B, H, d, es=2):
     return B * H * (2 * d * d * 4 + 5 * d * es + 4)
 
 
+def measured_traffic(key):
+    """HBM bytes per launch recorded under profiles/traffic.json (calibrated
+    FETCH_SIZE + WRITE_SIZE), or None if the record is missing or the kernel
+    sources changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read()
+                                    for s in rec["sources"])).hexdigest()[:16]
+        return rec[key] if h == rec["kernel_sources_sha256_16"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -58,7 +72,14 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", choices=["mid", "batched"], default="mid",
+                    help="prefill workload: mid = B1 H32 T4096 (the headline), "
+                         "batched = B8 H32 T32768 with a carried state")
+    ap.add_argument("--plan", default=None,
+                    help="force the prefill plan (sets KDA_PREFILL_PLAN: split | fused:<ncol>)")
     args = ap.parse_args()
+    if args.plan:
+        os.environ["KDA_PREFILL_PLAN"] = args.plan
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KDA units (b, h) are independent and shard "
               "without communication, so run with --gpus 1.", file=sys.stderr)
@@ -73,9 +94,10 @@ def main():
 
     dev = torch.device("cuda:0")
     kda.lib()
-    cfg = PREFILL_CONFIGS[1]
+    cfg_index = 1 if args.workload == "mid" else 2
+    cfg = PREFILL_CONFIGS[cfg_index]
     B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.dk
-    x = config_inputs(1, dev)
+    x = config_inputs(cfg_index, dev)
     o = torch.empty(B, T, H, d, dtype=cfg.dtype, device=dev)
     ST = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
     nb = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, cfg.dtype)
@@ -114,7 +136,7 @@ def main():
     warm_ms = w0.elapsed_time(w1) / args.steps
 
     tokens = B * T
-    alg_b = prefill_alg_bytes(B, T, H, d)
+    alg_b = prefill_alg_bytes(B, T, H, d, with_s0=x["S0"] is not None)
     alg_f = prefill_alg_flops(B, T, H, d)
     gbs = alg_b / (ms * 1e-3) / 1e9
     tflops = alg_f / (ms * 1e-3) / 1e12
@@ -134,12 +156,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1); v,z N(0,1); beta=sigmoid(N(0,1)); A~U(-1,1))",
-        "config": {"workload": "mid_prefill_B1_H32_T4096_d128_bf16", "B": B, "T": T, "H": H,
-                   "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": -5.0, "S0": "zeros",
-                   "parallelism": "single GPU", "workspace_bytes": nb},
+        "config": {"workload": f"{args.workload}_prefill_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T,
+                   "H": H, "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": -5.0,
+                   "S0": "zeros" if x["S0"] is None else "N(0, 0.01)",
+                   "parallelism": "single GPU", "plan": "split" if nb else "fused",
+                   "workspace_bytes": nb},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "prefill pass (all of its kernels)",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(f"prefill_{args.workload}_pass_bytes_{'split' if nb else 'fused'}"),
+                     "traffic_unit": "bytes per pass",
+                     "kernel": "prefill pass (intra_kernel + inter_kernel)" if nb else "prefill pass (fused_kernel)",
                      "alg_bytes_per_step": alg_b,
                      "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
                      "alg_flops_per_step": alg_f},
@@ -178,24 +204,31 @@ def main():
             "config": {"workload": "decode_B256_H32_d128_bf16_state_fp32", "B": c.B, "H": c.H,
                        "d_k": c.dk, "d_v": c.dv},
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dgbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": dgbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_B256_H32_d128_bf16_step_bytes"),
+                         "traffic_unit": "bytes per step",
                          "kernel": "decode_kernel", "alg_bytes_per_step": db},
         }
         del stg, S, S_save
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "mid":
         import oracle
         threads = len(os.sched_getaffinity(0))
         xc = {kk: (vv.cpu() if hasattr(vv, "cpu") else vv) for kk, vv in x.items()}
-        t0 = time.perf_counter()
-        oracle.prefill(xc["q"], xc["k"], xc["v"], xc["z"], xc["beta"], xc["A"], xc["g_min"],
-                       xc["S0"], nthreads=threads)
-        dt = time.perf_counter() - t0
+        reps, t0 = 0, time.perf_counter()
+        while True:   # the whole workload, repeated until about 10 s of CPU work
+            oracle.prefill(xc["q"], xc["k"], xc["v"], xc["z"], xc["beta"], xc["A"], xc["g_min"],
+                           xc["S0"], nthreads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or reps >= 200:
+                break
         line["cpu_baseline"] = {
-            "value": tokens / dt, "unit": "tokens/s", "cores": min(threads, B * H),
+            "value": reps * tokens / dt, "unit": "tokens/s", "cores": min(threads, B * H),
             "kind": "oracle",
-            "sample": f"the whole workload (B={B}, T={T}, H={H}, d={d}) once, fp64 token-by-token "
-                      f"recurrence, OpenMP over the {B * H} heads, {threads} threads available",
+            "sample": f"the whole workload (B={B}, T={T}, H={H}, d={d}) {reps} times, fp64 "
+                      f"token-by-token recurrence, OpenMP over the {B * H} heads, "
+                      f"{threads} threads available",
             "seconds": dt,
         }
     print(json.dumps(line), flush=True)

@@ -24,6 +24,9 @@ def hipcc_command(out: str) -> list[str]:
     return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 VALU ops are kept out of every HIP build
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in arch VGPRs: the state is scaled by VALU every
+            # chunk, and VALU cannot read accumulation registers
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"),
             "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
 

@@ -29,7 +29,7 @@
 //       accumulator layout of S (and of U) is directly the B operand of the
 //       next product, so the serial chain never touches LDS.
 //   kernels: "split" = an intra kernel over all chunks writing factor blocks
-//       to a workspace + an inter kernel streaming them back with a 3-deep
+//       to a workspace + an inter kernel streaming them back with a 2-deep
 //       register prefetch; "fused" = one kernel per (b, h, column tile) with
 //       four producer waves filling one half of a double-buffered LDS ring
 //       while the consumer waves run the state chain over the other half.
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(NW * 64) void inter_kernel(const char* __restrict__
                                                         float* ST, int B, int T, int H,
                                                         int n_first, int n_count, int nct) {
     using Bk = Blk<E, D>;
-    constexpr int PF = 3;
+    constexpr int PF = 2;
     int u, ct;
     if (!map_unit(nct, B * H, u, ct)) return;
     const int b = u / H, h = u % H;
