@@ -34,6 +34,9 @@
  * - `dt` gives the element type of q, k, v, z and o (KDA_F32 or KDA_BF16);
  *   beta, A, g_min and the state are always fp32.  Accumulation is fp32.
  * - Supported head sizes: (d_k, d_v) in {(32, 32), (128, 128)}.
+ * - Size limits (KDA_ERR_INVALID_SHAPE beyond them): B * H <= 2^26,
+ *   B * T * H <= 2^40, H * d_k <= 2^24 (the kernels address 32 consecutive
+ *   tokens of one head with 32-bit byte offsets).
  * - beta is used as given (expected in (0, 1)); q and k are used as given
  *   (no normalisation inside).  g_min must lie in [-5, 0]: the chunked form
  *   rescales 16-token tiles by factors up to exp(-16 g_min), which must stay
@@ -64,7 +67,7 @@ extern "C" {
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL            */
-    KDA_ERR_INVALID_SHAPE = 2,       /* B, T or H < 1, or sizes overflow      */
+    KDA_ERR_INVALID_SHAPE = 2,       /* B, T or H < 1, or a size limit broken */
     KDA_ERR_INVALID_VALUE = 3,       /* g_min outside [-5, 0] or not finite   */
     KDA_ERR_UNSUPPORTED = 4,         /* head size or dtype not supported      */
     KDA_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned      */
@@ -103,9 +106,14 @@ size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v,
  * The execution plan (one fused kernel, or an intra-chunk kernel writing the
  * workspace followed by an inter-chunk kernel) is a function of the sizes.
  * For tests and tuning the environment variable KDA_PREFILL_PLAN overrides
- * it: "split", or "fused:<n>" with n value columns per workgroup
- * (16, 32, 64, or 128 <= d_v; fp32 with d = 128: at most 64).  The workspace
- * query honours the same variable, so read both under one setting.
+ * it: "split" (default inter-chunk variant), "split:<n>:<b>" (n value
+ * columns per inter-chunk workgroup, b 16-column blocks per state chain:
+ * b in {1, 2}, n / (16 b) in {1, 2} or, for d = 128 and b = 1, 4; b = 2 not
+ * for fp32 with d = 128; "split:16:0" streams each chain's operands straight
+ * from memory into registers), or "fused:<n>" with n value columns per workgroup
+ * (16, 32, 64, or 128 <= d_v; fp32 with d = 128: at most 64).  An override
+ * that names no compiled variant is ignored.  The workspace query honours
+ * the same variable, so read both under one setting.
  * The chained result of two calls (the second with S0 = the first's S_T)
  * equals one call over the concatenated tokens up to rounding. */
 kda_status kda_chunk_prefill(const void *q, const void *k, const void *v,

@@ -77,6 +77,8 @@ kda_status check_shape(int B, int T, int H, int d, size_t& n_tok_el, size_t& n_t
     const unsigned long long tok = (unsigned long long)B * (unsigned long long)T * (unsigned long long)H;
     if ((long long)B * H > (1LL << 26) || tok > (1ULL << 40))
         return fail(KDA_ERR_INVALID_SHAPE, "B*T*H = %llu is too large", tok);
+    if ((long long)H * d > (1LL << 24))
+        return fail(KDA_ERR_INVALID_SHAPE, "H*d = %lld is too large (limit 2^24)", (long long)H * d);
     n_tok = (size_t)tok;
     n_tok_el = n_tok * (size_t)d;
     return KDA_OK;

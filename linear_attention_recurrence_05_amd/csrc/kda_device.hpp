@@ -138,10 +138,16 @@ __device__ __forceinline__ f32x4 mma_f32_k4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x4 pack4(f32x4 x) {
-    bf16x4 r;
-    r[0] = (bf16)x[0]; r[1] = (bf16)x[1]; r[2] = (bf16)x[2]; r[3] = (bf16)x[3];
+__device__ __forceinline__ bf16x2 pack2(float a, float b) {
+    bf16x2 r;
+    r[0] = (bf16)a; r[1] = (bf16)b;
     return r;
+}
+// Built from two 2-element conversions (one v_cvt_pk_bf16_f32 each).
+__device__ __forceinline__ bf16x4 pack4(f32x4 x) {
+    const u32x2 w = {__builtin_bit_cast(uint32_t, pack2(x[0], x[1])),
+                     __builtin_bit_cast(uint32_t, pack2(x[2], x[3]))};
+    return __builtin_bit_cast(bf16x4, w);
 }
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
     bf16x8 r;

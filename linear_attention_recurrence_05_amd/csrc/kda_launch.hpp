@@ -38,6 +38,7 @@ enum class Plan {
 struct PlanInfo {
     Plan plan;
     int ncol;            // value columns per inter/fused workgroup
+    int nb;              // split plan: 16-column blocks per state chain
     size_t ws_bytes;     // workspace needed
 };
 

@@ -29,10 +29,12 @@
 //       accumulator layout of S (and of U) is directly the B operand of the
 //       next product, so the serial chain never touches LDS.
 //   kernels: "split" = an intra kernel over all chunks writing factor blocks
-//       to a workspace + an inter kernel streaming them back with a 2-deep
-//       register prefetch; "fused" = one kernel per (b, h, column tile) with
+//       to a workspace + an inter kernel whose loader waves stream them into
+//       an LDS ring ahead of the state chain; "fused" = one kernel per
+//       (b, h, column tile) with
 //       four producer waves filling one half of a double-buffered LDS ring
 //       while the consumer waves run the state chain over the other half.
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -109,6 +111,14 @@ __device__ __forceinline__ f32x4 widen4(V4<E> x) {
     return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
 }
 
+// Code-motion fence: memory operations issued before it stay before it (an
+// empty asm with a memory clobber stops IR-level sinking; sched_barrier stops
+// the machine scheduler).  It does not wait for them to complete.
+__device__ __forceinline__ void pin_issued() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -139,11 +149,12 @@ __device__ __forceinline__ ChunkPos chunk_pos(int b, int h, int n, int T, int H)
 
 // Buffer over the chunk's rows of a [.., T, H, D] tensor of element size es:
 // from row 0 of the chunk to the end of its last valid row, so every access
-// to a row past the chunk's end falls outside and reads 0 / is dropped.
+// to a row past the chunk's end falls outside and reads 0 / is dropped.  A
+// chunk past the end of the sequence (L <= 0) gets an empty buffer.
 template <int D>
 __device__ __forceinline__ Rsrc chunk_rsrc(const void* base, const ChunkPos& c, int es) {
-    return make_rsrc((const char*)base + c.row0 * es,
-                     (uint32_t)(((size_t)(c.L - 1) * c.rstride + D) * es));
+    const size_t bytes = c.L > 0 ? ((size_t)(c.L - 1) * c.rstride + D) * es : 0;
+    return make_rsrc((const char*)base + c.row0 * es, (uint32_t)bytes);
 }
 
 // Raw producer inputs of one chunk, kept in registers so the next chunk's
@@ -404,23 +415,30 @@ __device__ __forceinline__ void cops_load(COps<E, D>& c, const Src& src) {
 }
 
 // V of one chunk for NB 16-column blocks, accumulator layout (rows 4g + p),
-// kept in the input type until use; rows past the chunk's end read 0.
-template <typename E, int D, int NB>
-__device__ __forceinline__ void v_load(V4<E> (&V)[NB], const E* __restrict__ v, const ChunkPos& c,
-                                       int col0) {
-    constexpr int ES = (int)sizeof(E);
+// kept as the raw loaded words (a bf16 pattern in the low 16 bits, or fp32
+// bits) and widened only when the chunk is consumed, so the loads stay in
+// flight across the chunk steps in between; rows past the chunk's end read 0.
+template <int D, int NB>
+__device__ __forceinline__ void v_load(u32x4 (&V)[NB], const void* __restrict__ v, int es,
+                                       const ChunkPos& c, int col0) {
     const int lane = lane_id(), j = lane & 15, g = lane >> 4;
-    const Rsrc rv = chunk_rsrc<D>(v, c, ES);
-    const int rowb = (int)(c.rstride * ES);
-    const int base = 4 * g * rowb + (col0 + j) * ES;
+    const Rsrc rv = chunk_rsrc<D>(v, c, es);
+    const int rowb = (int)(c.rstride * es);
+    const int base = 4 * g * rowb + (col0 + j) * es;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int off = base + p * rowb + 16 * nb * ES;
-            if constexpr (ES == 2) V[nb][p] = __builtin_bit_cast(E, buf_load<unsigned short>(rv, off));
-            else V[nb][p] = __builtin_bit_cast(E, buf_load<uint32_t>(rv, off));
+            const int off = base + p * rowb + 16 * nb * es;
+            V[nb][p] = es == 2 ? (uint32_t)buf_load<unsigned short>(rv, off)
+                               : buf_load<uint32_t>(rv, off);
         }
+}
+
+template <typename E>
+__device__ __forceinline__ f32x4 v_widen(u32x4 x) {
+    if constexpr (std::is_same<E, bf16>::value) x <<= 16;
+    return __builtin_bit_cast(f32x4, x);
 }
 
 // O of one chunk; stores to rows past the chunk's end are dropped.
@@ -446,12 +464,12 @@ __device__ __forceinline__ void o_store(const f32x4 (&O)[NB], E* __restrict__ o,
 // One chunk of the state chain for NB 16-column blocks of S.
 template <typename E, int D, int NB>
 __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D / 16],
-                                           const V4<E> (&Vr)[NB], f32x4 (&O)[NB]) {
+                                           const f32x4 (&Vf)[NB], f32x4 (&O)[NB]) {
     using B = Blk<E, D>;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         f32x4 x = zero4(), o = zero4();
-        const f32x4 V = widen4<E>(Vr[nb]);
+        const f32x4 V = Vf[nb];
         if constexpr (B::kBF16) {
 #pragma unroll
             for (int s = 0; s < B::NSLOT; ++s) {
@@ -604,52 +622,301 @@ __global__ __launch_bounds__(256) void intra_kernel(const E* __restrict__ q, con
     }
 }
 
-// Inter kernel (split plan): one workgroup of NW waves per (b, h, column tile
-// of NW*NB*16 columns) streams the factor blocks of chunks [n_first,
-// n_first + n_count) and carries the state.  The operands of the next
-// PF chunks are kept in flight in a register ring.
-template <typename E, int D, int NB, int NW>
-__global__ __launch_bounds__(NW * 64) void inter_kernel(const char* __restrict__ ws,
-                                                        const E* __restrict__ v,
-                                                        const float* S0, E* __restrict__ o,
-                                                        float* ST, int B, int T, int H,
-                                                        int n_first, int n_count, int nct) {
+// Workgroup barrier usable from role-specific code paths: every wave of the
+// workgroup executes the same number of these, from whichever branch.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Inter kernel (split plan): one workgroup per (b, h, tile of NCOL = 16 NB
+// NCW value columns) over chunks [n_first, n_first + n_count).  Waves
+// 0 .. NCW-1 each carry the state of NB 16-column blocks; the other NL waves
+// stream the factor blocks (and, where the LDS holds them, the V tiles) into
+// an LDS ring of NPAIR entries of two chunks ("pairs"), shared by the NCW
+// chains, which read their operands from LDS one chunk ahead of their use.
+// Every chain reads the whole factor block of each chunk, so NB > 1 trades
+// MFMA work per wave for less LDS traffic per column.
+//
+// Synchronisation is by LDS flags, not workgroup barriers, so the chains run
+// unaligned (their LDS bursts interleave) and never wait for each other:
+//   ready[e]  index of the last pair published in entry e (loader -> chains);
+//             a loader stores it after its data stores have completed;
+//   done[e]   number of (chain, pair) completions of entry e (chains ->
+//             loaders); a chain adds 1 after its last use of the pair.
+// Pair p goes to entry p mod NPAIR and belongs to loader p mod NL, which
+// writes it once done[e] counts NCW completions of every earlier occupant.
+// A chain in pair s also reads the first chunk of pair s + 1; two entries
+// suffice for that, so no wait can close a cycle.  Every wait is bounded
+// (kSpinLimit polls); a bound that ran out would only corrupt results, the
+// kernel still ends.
+constexpr int kSpinLimit = 1 << 22;
+
+__device__ __forceinline__ void spin_until_ge(const int* flag, int target) {
+    for (int it = 0; it < kSpinLimit; ++it) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    // later LDS reads stay after the poll that released them
+    asm volatile("" ::: "memory");
+}
+
+template <typename E, int D, int NCW_, int NB_>
+struct InterCfg {
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int NCW = NCW_, NB = NB_;
+    static constexpr int NCOL = 16 * NB * NCW;                   // value columns per workgroup
+    static constexpr int LDS_MAX = 160 * 1024 - 256;             // room for the flags
+    // V tiles of one pair: 32-bit word w of the tile's row r (two bf16 or one
+    // fp32 column) at word w * VSTR + r; the padding makes the loaders'
+    // word stores conflict-free across the 64 LDS banks
+    static constexpr int VSTR = 2 * kChunk + 2;
+    static constexpr int VBYTES = NCOL * ES / 4 * VSTR * 4;
+    static constexpr int ENT_V = 2 * Blk<E, D>::BYTES + VBYTES;
+    static constexpr bool VLDS = LDS_MAX / ENT_V >= 2;           // V staged in the ring
+    static constexpr int ENT = VLDS ? ENT_V : 2 * Blk<E, D>::BYTES;
+    static constexpr int NPAIR = LDS_MAX / ENT < 4 ? LDS_MAX / ENT : 4;
+    // loader waves: workgroups of at most four waves keep one wave per SIMD
+    // (the chains get the whole register file)
+    static constexpr int NL = NCW >= 4 ? 3 : 4 - NCW;
+    static constexpr int THREADS = (NCW + NL) * kWave;
+    static_assert(NCOL <= D, "column tile wider than the head");
+    static_assert(NPAIR >= 2, "the ring needs two entries of two factor blocks");
+    static_assert(!VLDS || (2 * kChunk * NCOL * ES / 16) % kWave == 0, "V pieces per loader lane");
+    static_assert(VBYTES % 16 == 0, "ring entries stay 16-byte aligned");
+};
+
+template <typename E, int D, int NCW, int NB>
+__global__ __launch_bounds__((InterCfg<E, D, NCW, NB>::THREADS)) void inter_kernel(
+    const char* __restrict__ ws, const E* __restrict__ v, const float* S0, E* __restrict__ o,
+    float* ST, int B, int T, int H, int n_first, int n_count, int nct) {
     using Bk = Blk<E, D>;
-    constexpr int PF = 2;
+    using Cfg = InterCfg<E, D, NCW, NB>;
+    constexpr int NPAIR = Cfg::NPAIR, NL = Cfg::NL, ENT = Cfg::ENT, ES = Cfg::ES;
+    constexpr int NCOL = Cfg::NCOL;
+    constexpr bool VLDS = Cfg::VLDS;
+    constexpr int PAIR16 = 2 * Bk::BYTES / 16;        // 16-byte pieces of factor blocks per pair
+    constexpr int PER_LANE = (PAIR16 + kWave - 1) / kWave;
+    constexpr int RP = NCOL * ES / 16;                // 16-byte pieces per V row of the tile
+    constexpr int VPL = VLDS ? 2 * kChunk * RP / kWave : 0;
+    constexpr int EPP = 16 / ES;                      // elements per piece
+    __shared__ __attribute__((aligned(16))) char ring[NPAIR * ENT];
+    __shared__ int ready[NPAIR], done[NPAIR];
+    int u, ct;
+    if (!map_unit(nct, B * H, u, ct)) return;   // uniform over the workgroup
+    const int b = u / H, h = u % H;
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int tile0 = ct * NCOL;
+    const int NS = (n_count + 1) / 2;
+    const char* blk0 = ws + (size_t)u * n_count * Bk::BYTES;
+    const Rsrc rws = make_rsrc(blk0, (uint32_t)((size_t)n_count * Bk::BYTES));
+    if (w == 0 && lane < NPAIR) {
+        ready[lane] = -1;
+        done[lane] = 0;
+    }
+    wg_barrier();   // the only barrier: flags initialised
+
+    if (w >= NCW) {
+        // ------------------------------------------------ loader waves
+        const int L = w - NCW;
+        u32x4 buf[PER_LANE];
+        u32x4 vbuf[VPL > 0 ? VPL : 1];
+        auto issue = [&](int p) {
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int piece = i * kWave + lane;
+                buf[i] = buf_load<u32x4>(rws, (p * PAIR16 + piece) * 16);   // past the end: 0
+            }
+            if constexpr (VLDS) {
+                // rows t0 .. t0+31 of the tile's columns; rows past T read 0
+                const int t0 = (n_first + 2 * p) * kChunk;
+                const int Lr = min(2 * kChunk, T - t0);
+                const size_t rs = (size_t)H * D;
+                const size_t row0 = ((size_t)b * T + t0) * H + h;
+                const Rsrc rv = make_rsrc(v + row0 * D + tile0,
+                                          Lr > 0 ? (uint32_t)(((size_t)(Lr - 1) * rs + NCOL) * ES) : 0u);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int q = i * kWave + lane, r = q / RP, c = q % RP;
+                    vbuf[i] = buf_load<u32x4>(rv, (int)((r * rs + c * EPP) * ES));
+                }
+            }
+        };
+        auto write = [&](int p) {
+            char* dst = ring + (p % NPAIR) * ENT;
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int piece = i * kWave + lane;
+                if (piece < PAIR16) *reinterpret_cast<u32x4*>(dst + piece * 16) = buf[i];
+            }
+            if constexpr (VLDS) {
+                // V area: word-major (word w of row r at w * VSTR + r), so a
+                // chain reads the four rows of its column as 16 bytes
+                uint32_t* vd = reinterpret_cast<uint32_t*>(dst + 2 * Bk::BYTES);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int q = i * kWave + lane, r = q / RP, c = q % RP;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vd[(4 * c + e) * Cfg::VSTR + r] = vbuf[i][e];
+                }
+            }
+        };
+        if (L < NS) issue(L);
+        for (int p = L; p < NS; p += NL) {
+            const int e = p % NPAIR;
+            if (p >= NPAIR) spin_until_ge(&done[e], NCW * (p / NPAIR));
+            write(p);
+            // publish: the data stores complete before the flag store
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __hip_atomic_store(&ready[e], p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (p + NL < NS) issue(p + NL);
+        }
+        return;
+    }
+    // ---------------------------------------------------- state chains
+    // Straight-line loop body (the odd last chunk runs after the loop), so
+    // no load is waited for before its use.
+    const int j = lane & 15, g = lane >> 4;
+    const int col0 = tile0 + 16 * NB * w;
+    auto blk = [&](int nl) { return LdsSrc{ring + ((nl >> 1) % NPAIR) * ENT + (nl & 1) * Bk::BYTES}; };
+    // V of chunk nl for the NB blocks: from the ring, or (where it does not
+    // fit) the raw words loaded from memory two chunks ahead
+    auto v_ring = [&](int nl, f32x4 (&V)[NB]) {
+        const uint32_t* base = reinterpret_cast<const uint32_t*>(ring + ((nl >> 1) % NPAIR) * ENT +
+                                                                 2 * Bk::BYTES) +
+                               (nl & 1) * kChunk + 4 * g;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int vcol = 16 * (NB * w + nb) + j;   // column within the tile
+            const uint32_t* at = base + (ES == 2 ? vcol >> 1 : vcol) * Cfg::VSTR;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(at);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(at + 2);
+            u32x4 x = {lo[0], lo[1], hi[0], hi[1]};
+            if constexpr (ES == 2) {
+                x <<= 16 * (1 - (vcol & 1));   // bf16 of this column to the high half
+                x &= 0xFFFF0000u;
+            }
+            V[nb] = __builtin_bit_cast(f32x4, x);
+        }
+    };
+    auto release = [&](int s) {   // this chain is done with pair s
+        asm volatile("" ::: "memory");
+        if (lane == 0) __hip_atomic_fetch_add(&done[s % NPAIR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    f32x4 S[NB][D / 16];
+    state_load<D, NB>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
+    u32x4 vr[2][NB];
+    if constexpr (!VLDS) {
+        v_load<D, NB>(vr[0], v, ES, chunk_pos<D>(b, h, n_first, T, H), col0);
+        v_load<D, NB>(vr[1], v, ES, chunk_pos<D>(b, h, n_first + 1, T, H), col0);
+    }
+    COps<E, D> ca, cb;
+    f32x4 va[NB], vb[NB];
+    spin_until_ge(&ready[0], 0);
+    cops_load<E, D>(ca, blk(0));
+    if constexpr (VLDS) v_ring(0, va);
+    const int NFULL = n_count >> 1;
+    for (int s = 0; s < NFULL; ++s) {
+        const int n0 = n_first + 2 * s;
+        f32x4 O[NB];
+        cops_load<E, D>(cb, blk(2 * s + 1));
+        if constexpr (VLDS) {
+            v_ring(2 * s + 1, vb);
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) va[nb] = v_widen<E>(vr[0][nb]);
+        }
+        // keep the reads of the next chunk's operands ahead of this chunk's
+        // work (IR sinking and the scheduler would otherwise move them to
+        // their use); the loads stay in flight until their first use.  The
+        // fp32 operands are twice as large: there both sets would not fit
+        // the registers, and the reads are left to the scheduler.
+        if constexpr (ES == 2) pin_issued();
+        chunk_step<E, D, NB>(ca, S, va, O);
+        o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n0, T, H), col0);
+        if constexpr (!VLDS) v_load<D, NB>(vr[0], v, ES, chunk_pos<D>(b, h, n0 + 2, T, H), col0);
+        if (s + 1 < NS) spin_until_ge(&ready[(s + 1) % NPAIR], s + 1);
+        cops_load<E, D>(ca, blk(2 * s + 2));   // pair s + 1 (stale if there is none; unused)
+        if constexpr (VLDS) {
+            v_ring(2 * s + 2, va);
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) vb[nb] = v_widen<E>(vr[1][nb]);
+        }
+        if constexpr (ES == 2) pin_issued();
+        chunk_step<E, D, NB>(cb, S, vb, O);
+        release(s);
+        o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n0 + 1, T, H), col0);
+        if constexpr (!VLDS) v_load<D, NB>(vr[1], v, ES, chunk_pos<D>(b, h, n0 + 3, T, H), col0);
+    }
+    if (n_count & 1) {
+        f32x4 O[NB];
+        if constexpr (!VLDS) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) va[nb] = v_widen<E>(vr[0][nb]);
+        }
+        chunk_step<E, D, NB>(ca, S, va, O);
+        o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n_first + n_count - 1, T, H), col0);
+    }
+    if (ST) state_store<D, NB>(S, ST + (size_t)u * D * D, col0);
+}
+
+// Inter kernel, direct variant (split plan): one wave per (b, h, 16-column
+// block) over chunks [n_first, n_first + n_count), no LDS and no barriers.
+// The operands of chunk n + PF are loaded from memory (the factor-block
+// workspace and V) into a register ring of depth PF while chunk n runs; the
+// loop is unrolled by PF so every ring slot is a fixed set of registers and
+// every wait for a load is exact.  Blocks past the segment read as zeros and
+// are never used.
+template <typename E, int D, int PF>
+__global__ __launch_bounds__(64) void inter_direct_kernel(const char* __restrict__ ws,
+                                                          const E* __restrict__ v,
+                                                          const float* S0, E* __restrict__ o,
+                                                          float* ST, int B, int T, int H,
+                                                          int n_first, int n_count, int nct) {
+    using Bk = Blk<E, D>;
+    constexpr int ES = (int)sizeof(E);
     int u, ct;
     if (!map_unit(nct, B * H, u, ct)) return;
     const int b = u / H, h = u % H;
-    const int w = wave_id();
-    const int col0 = ct * (NW * NB * 16) + w * NB * 16;
-    f32x4 S[NB][D / 16];
-    state_load<D, NB>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
-
+    const int col0 = ct * 16;
     const char* blk0 = ws + (size_t)u * n_count * Bk::BYTES;
-    COps<E, D> ring[PF];
-    V4<E> vr[PF][NB];
+    auto src = [&](int nl) {
+        return BufSrc{make_rsrc(blk0 + (size_t)nl * Bk::BYTES, nl < n_count ? (uint32_t)Bk::BYTES : 0u)};
+    };
+    f32x4 S[1][D / 16];
+    state_load<D, 1>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
+    COps<E, D> c[PF];
+    u32x4 vr[PF][1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-        if (i < n_count) {
-            cops_load<E, D>(ring[i], BufSrc{make_rsrc(blk0 + (size_t)i * Bk::BYTES, Bk::BYTES)});
-            v_load<E, D, NB>(vr[i], v, chunk_pos<D>(b, h, n_first + i, T, H), col0);
-        }
+        cops_load<E, D>(c[i], src(i));
+        v_load<D, 1>(vr[i], v, ES, chunk_pos<D>(b, h, n_first + i, T, H), col0);
     }
-    for (int base = 0; base < n_count; base += PF) {
+    int n = 0;
+    for (; n + PF <= n_count; n += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            const int nl = base + i;
-            if (nl < n_count) {
-                f32x4 O[NB];
-                chunk_step<E, D, NB>(ring[i], S, vr[i], O);
-                o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n_first + nl, T, H), col0);
-                if (nl + PF < n_count) {
-                    cops_load<E, D>(ring[i], BufSrc{make_rsrc(blk0 + (size_t)(nl + PF) * Bk::BYTES, Bk::BYTES)});
-                    v_load<E, D, NB>(vr[i], v, chunk_pos<D>(b, h, n_first + nl + PF, T, H), col0);
-                }
-            }
+            f32x4 Vf[1] = {v_widen<E>(vr[i][0])};
+            f32x4 O[1];
+            chunk_step<E, D, 1>(c[i], S, Vf, O);
+            o_store<E, D, 1>(O, o, chunk_pos<D>(b, h, n_first + n + i, T, H), col0);
+            cops_load<E, D>(c[i], src(n + i + PF));
+            v_load<D, 1>(vr[i], v, ES, chunk_pos<D>(b, h, n_first + n + i + PF, T, H), col0);
         }
     }
-    if (ST) state_store<D, NB>(S, ST + (size_t)u * D * D, col0);
+#pragma unroll
+    for (int i = 0; i < PF - 1; ++i) {
+        if (n + i < n_count) {
+            f32x4 Vf[1] = {v_widen<E>(vr[i][0])};
+            f32x4 O[1];
+            chunk_step<E, D, 1>(c[i], S, Vf, O);
+            o_store<E, D, 1>(O, o, chunk_pos<D>(b, h, n_first + n + i, T, H), col0);
+        }
+    }
+    if (ST) state_store<D, 1>(S, ST + (size_t)u * D * D, col0);
 }
 
 // Producer waves per fused workgroup: 4, unless the double-buffered ring of
@@ -661,14 +928,6 @@ struct FusedCfg {
     static constexpr int RING = 2 * NPROD * Bk::BYTES;
     static constexpr int LDS = RING + NPROD * Bk::SCR_BYTES;
 };
-
-// Workgroup barrier usable from role-specific code paths: every wave of the
-// workgroup executes the same number of these, from whichever branch.
-__device__ __forceinline__ void wg_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // Fused kernel: one workgroup of 8 waves per (b, h, column tile of
 // NCW*NB*16 columns).  Waves 0..NPROD-1 produce; waves 4..4+NCW-1 consume.
@@ -728,17 +987,18 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
     // ---------------------------------------------------- consumer wave
     const int col0 = ct * (NCW * NB * 16) + cw * NB * 16;
     f32x4 S[NB][D / 16];
-    V4<E> Vc[NPROD][NB], Vn[NPROD][NB];
+    constexpr int ES = (int)sizeof(E);
+    u32x4 Vc[NPROD][NB], Vn[NPROD][NB];
     state_load<D, NB>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
 #pragma unroll
     for (int cc = 0; cc < NPROD; ++cc)
-        if (cc < NC) v_load<E, D, NB>(Vc[cc], v, chunk_pos<D>(b, h, cc, T, H), col0);
+        if (cc < NC) v_load<D, NB>(Vc[cc], v, ES, chunk_pos<D>(b, h, cc, T, H), col0);
     wg_barrier();
     for (int m = 0; m < NM; ++m) {
 #pragma unroll
         for (int cc = 0; cc < NPROD; ++cc) {
             const int nn = (m + 1) * NPROD + cc;
-            if (nn < NC) v_load<E, D, NB>(Vn[cc], v, chunk_pos<D>(b, h, nn, T, H), col0);
+            if (nn < NC) v_load<D, NB>(Vn[cc], v, ES, chunk_pos<D>(b, h, nn, T, H), col0);
         }
 #pragma unroll
         for (int cc = 0; cc < NPROD; ++cc) {
@@ -747,7 +1007,10 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
                 COps<E, D> c;
                 cops_load<E, D>(c, LdsSrc{smem + ((m & 1) * NPROD + cc) * Bk::BYTES});
                 f32x4 O[NB];
-                chunk_step<E, D, NB>(c, S, Vc[cc], O);
+                f32x4 Vf[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) Vf[nb] = v_widen<E>(Vc[cc][nb]);
+                chunk_step<E, D, NB>(c, S, Vf, O);
                 o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n, T, H), col0);
             }
         }
@@ -774,12 +1037,33 @@ constexpr int kSegChunks = 1024;
 // Plan override for tests and tuning: KDA_PREFILL_PLAN = "fused:<ncol>"
 // (ncol in {16, 32, 64, 128}, at most d) or "split".  Unset or anything
 // else: chosen from the sizes.
-static bool plan_override(int d, PlanInfo& p) {
+// Split-plan inter variants that are compiled: ncol value columns per
+// workgroup in 16-column blocks, nb blocks per state chain.
+static bool split_variant_ok(int d, bool is_bf16, int ncol, int nb) {
+    if (nb == 0) return ncol == 16;   // direct variant
+    if (nb != 1 && nb != 2) return false;
+    if (nb == 2 && d == 128 && !is_bf16) return false;
+    const int ncw = ncol / (16 * nb);
+    if (ncw * 16 * nb != ncol || ncol > d) return false;
+    return ncw == 1 || ncw == 2 || (ncw == 4 && d == 128 && nb == 1);
+}
+
+static bool plan_override(int d, bool is_bf16, PlanInfo& p) {
     const char* env = std::getenv("KDA_PREFILL_PLAN");
     if (!env) return false;
     if (std::strcmp(env, "split") == 0) {
         p.plan = Plan::kSplit;
         return true;
+    }
+    if (std::strncmp(env, "split:", 6) == 0) {
+        int ncol = 0, nb = 0;
+        if (std::sscanf(env + 6, "%d:%d", &ncol, &nb) == 2 && split_variant_ok(d, is_bf16, ncol, nb)) {
+            p.plan = Plan::kSplit;
+            p.ncol = ncol;
+            p.nb = nb;
+            return true;
+        }
+        return false;
     }
     if (std::strncmp(env, "fused:", 6) == 0) {
         const int n = std::atoi(env + 6);
@@ -798,7 +1082,9 @@ PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16) {
     const long units = (long)B * H;
     const int NC = (T + kChunk - 1) / kChunk;
     p.plan = Plan::kSplit;
-    const bool forced = plan_override(d, p);
+    p.ncol = 0;
+    p.nb = 1;
+    const bool forced = plan_override(d, is_bf16, p);
     if (forced && p.plan == Plan::kFused) return p;
     if (!forced && units >= 128) {
         p.plan = Plan::kFused;
@@ -807,7 +1093,10 @@ PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16) {
         return p;
     }
     p.plan = Plan::kSplit;
-    p.ncol = 16;
+    if (p.ncol == 0) {   // default inter variant
+        p.ncol = d >= 64 ? 64 : d;
+        p.nb = 1;
+    }
     const int seg = NC < kSegChunks ? NC : kSegChunks;
     p.ws_bytes = (size_t)units * seg * factor_block_bytes(d, is_bf16);
     if (NC > kSegChunks) p.ws_bytes += (size_t)units * d * d * sizeof(float);
@@ -816,6 +1105,50 @@ PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16) {
 
 static unsigned grid_units(int units, int nct) {
     return (unsigned)(((units + 7) / 8) * 8 * nct);
+}
+
+template <typename E, int D, int NCW, int NB>
+static hipError_t launch_inter_v(const char* ws, const E* v, const float* s_in, E* o, float* s_out,
+                                 const PrefillArgs& a, int n_first, int n_count,
+                                 hipStream_t stream) {
+    using Cfg = InterCfg<E, D, NCW, NB>;
+    const int nct = D / Cfg::NCOL;
+    hipLaunchKernelGGL((inter_kernel<E, D, NCW, NB>), dim3(grid_units(a.B * a.H, nct)),
+                       dim3(Cfg::THREADS), 0, stream, ws, v, s_in, o, s_out, a.B, a.T, a.H, n_first,
+                       n_count, nct);
+    return hipGetLastError();
+}
+
+// Inter-kernel variant of a split plan: p.ncol value columns per workgroup,
+// p.nb 16-column blocks per state chain (see split_variant_ok).
+template <typename E, int D>
+static hipError_t launch_inter(const PlanInfo& p, const char* ws, const E* v, const float* s_in,
+                               E* o, float* s_out, const PrefillArgs& a, int n_first, int n_count,
+                               hipStream_t stream) {
+    if (p.nb == 0) {   // direct variant: one wave per 16-column block
+        hipLaunchKernelGGL((inter_direct_kernel<E, D, 2>), dim3(grid_units(a.B * a.H, D / 16)),
+                           dim3(64), 0, stream, ws, v, s_in, o, s_out, a.B, a.T, a.H, n_first,
+                           n_count, D / 16);
+        return hipGetLastError();
+    }
+#define KDA_INTER(NCW, NB)                                                                    \
+    if (p.ncol == 16 * (NCW) * (NB) && p.nb == (NB))                                           \
+        return launch_inter_v<E, D, (NCW), (NB)>(ws, v, s_in, o, s_out, a, n_first, n_count, stream);
+    if constexpr (D == 128) {
+        KDA_INTER(4, 1)
+        KDA_INTER(2, 1)
+        KDA_INTER(1, 1)
+        if constexpr (sizeof(E) == 2) {
+            KDA_INTER(2, 2)
+            KDA_INTER(1, 2)
+        }
+    } else {
+        KDA_INTER(2, 1)
+        KDA_INTER(1, 1)
+        KDA_INTER(1, 2)
+    }
+#undef KDA_INTER
+    return hipErrorInvalidValue;
 }
 
 template <typename E, int D>
@@ -851,7 +1184,6 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PlanInfo& p, void
     const int seg = NC < kSegChunks ? NC : kSegChunks;
     float* carry = a.S_T;
     if (NC > seg && !carry) carry = (float*)(fws + (size_t)units * seg * blk_bytes);
-    const int nct = D / 16;
     for (int n_first = 0; n_first < NC; n_first += seg) {
         const int n_count = (NC - n_first) < seg ? (NC - n_first) : seg;
         const size_t nchunks = (size_t)units * n_count;
@@ -863,10 +1195,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PlanInfo& p, void
         const float* s_in = n_first == 0 ? a.S0 : carry;
         const bool last = n_first + n_count >= NC;
         float* s_out = last ? a.S_T : carry;
-        hipLaunchKernelGGL((inter_kernel<E, D, 1, 1>), dim3(grid_units(units, nct)), dim3(64), 0,
-                           stream, (const char*)fws, v, s_in, o, s_out, a.B, a.T, a.H, n_first,
-                           n_count, nct);
-        e = hipGetLastError();
+        e = launch_inter<E, D>(p, fws, v, s_in, o, s_out, a, n_first, n_count, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
