@@ -108,11 +108,10 @@ size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v,
  * For tests and tuning the environment variable KDA_PREFILL_PLAN overrides
  * it: "split" (default inter-chunk variant), "split:<n>:<b>" (n value
  * columns per inter-chunk workgroup, b 16-column blocks per state chain:
- * b in {1, 2}, n / (16 b) in {1, 2} or, for d = 128 and b = 1, 4; b = 2 not
- * for fp32 with d = 128; "split:16:0" streams each chain's operands straight
- * from memory into registers), or "fused:<n>" with n value columns per workgroup
- * (16, 32, 64, or 128 <= d_v; fp32 with d = 128: at most 64).  An override
- * that names no compiled variant is ignored.  The workspace query honours
+ * b = 1 with n in {16, 32} or, for bf16 with d = 128, 64; b = 2 for bf16
+ * with d = 128, n in {32, 64}), or "fused:<n>" with n value columns per
+ * workgroup (16, 32, 64, or 128 <= d_v; fp32 with d = 128: at most 64).  An
+ * override that names no compiled variant is ignored.  The workspace query honours
  * the same variable, so read both under one setting.
  * The chained result of two calls (the second with S0 = the first's S_T)
  * equals one call over the concatenated tokens up to rounding. */

@@ -32,7 +32,7 @@ struct PrefillArgs {
 // How a prefill is executed.
 enum class Plan {
     kFused,   // gate + intra + inter in one launch; one workgroup per (b, h, column tile)
-    kSplit,   // intra kernel over all chunks -> workspace, then inter kernel
+    kSplit,   // intra kernel over all chunk pairs -> workspace, then inter kernel
 };
 
 struct PlanInfo {
@@ -42,13 +42,24 @@ struct PlanInfo {
     size_t ws_bytes;     // workspace needed
 };
 
+// Chunks per split-plan segment (even, so no pair of chunks straddles two
+// segments): the workspace holds this many chunks' factors per head; longer
+// sequences run as consecutive segments carrying the state.
+constexpr int kSegChunks = 1024;
+static_assert(kSegChunks % 2 == 0, "segments hold whole pairs of chunks");
+
 // Chosen execution plan for these sizes (pure function of the sizes).
 PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16);
-// Bytes of one chunk's factor block.
-size_t factor_block_bytes(int d, bool is_bf16);
+// Bytes of one two-chunk factor block of the split plan.
+size_t pair_block_bytes(int d, bool is_bf16);
+// Whether the split plan compiles an inter kernel with ncol value columns per
+// workgroup and nb 16-column blocks per state chain.
+bool pair_variant_ok(int d, bool is_bf16, int ncol, int nb);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
+// Split plan: pair intra kernel -> workspace -> pair inter kernel, per segment.
+hipError_t launch_split(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
 hipError_t launch_gate_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,
                               int H, int d, bool is_bf16, hipStream_t stream);
 hipError_t launch_intra_diag(const void* q, const void* k, const void* z, const float* beta,

@@ -1,0 +1,811 @@
+// kda_pair.hip -- split-plan prefill for gfx950: the state chain advances two
+// 16-token chunks per step.
+//
+// Source of the method: dev.to "Kimi K3 Architecture: Scaling 2.8T Parameters
+// for Long-Context Multimodal MoE", section "The Sequence Bottleneck: Hybrid
+// KDA and Gated MLA" (lower-bounded gate, 16-token tiles whose cumulative
+// log-decay stays inside (-80, 0), chunkwise parallel form).  The two-chunk
+// step is an exact regrouping of two single-chunk steps (kda_chunk.hpp); the
+// chunks keep their own 16-token factorisation, so every factor stays inside
+// the bounds the 16-token tiles guarantee.
+//
+// For consecutive chunks a, b and the state S at the start of a:
+//   x_a = Kt_a S,                      U_a = Tm_a (V_a - x_a)
+//   S'  = Diag(gam_a) S + Kd_a^T U_a   (state at the start of b)
+//   x_b = Kt_b S' = (Kt_b Diag(gam_a)) S + M_kb U_a,   M_kb = Kt_b Kd_a^T
+//   U_b = Tm_b (V_b - x_b)
+//   O_a = Qt_a S + Aqk_a U_a
+//   O_b = (Qt_b Diag(gam_a)) S + M_qb U_a + Aqk_b U_b, M_qb = Qt_b Kd_a^T
+//   S  <- Diag(gam_a gam_b) S + [Kd_a Diag(gam_b); Kd_b]^T [U_a; U_b]
+// The cross terms are formed from bounded factors: Kt_b Kd_a^T =
+// (Kt_b Diag(gam_a)) Kh_a^T with Kh_a = Kd_a Diag(gam_a)^{-1} = k_a e^{-G}.
+// Per pair the chain packs S once, scales it once, and updates it with
+// K = 32 products.
+#include "kda_chunk.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+// ------------------------------------------------------------ pair block
+//
+// Operands of one pair in the lane layouts the chain reads (E elements):
+//   KA, KB, QA, QB  Kt_a, Kt_b Diag(gam_a), Qt_a, Qt_b Diag(gam_a) in the
+//                   A-row layout of Blk (16 rows x D, K = key channels)
+//   KD2             S-update A operand, K = 32 tokens: tile m, lane (c, g)
+//                   holds [Kd_a[4g+i][16m+c] gam_b[16m+c], Kd_b[4g+i][16m+c]],
+//                   i = 0..3 (this K order makes [U_a; U_b] in accumulator
+//                   layout its B operand)
+//   TMA, TMB, AQA, MKB  16x16 A operands for K = 16: lane (r, c/4) holds
+//                   row r, columns 4(c/4) .. 4(c/4)+3
+//   OB2             [M_qb | Aqk_b] as a K = 32 A operand: lane (r, g) holds
+//                   M_qb[r][4g+i], then Aqk_b[r][4g+i]
+//   GAB             gam_a gam_b (fp32, D)
+template <typename E, int D>
+struct PBlk {
+    using B1 = Blk<E, D>;
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int NSLOT = B1::NSLOT, MT = B1::MT, OPB = B1::OPB;
+    static constexpr int AROW = NSLOT * 1024;
+    static constexpr int KA = 0;
+    static constexpr int KB = KA + AROW;
+    static constexpr int QA = KB + AROW;
+    static constexpr int QB = QA + AROW;
+    static constexpr int KD2 = QB + AROW;
+    static constexpr int TMA = KD2 + MT * kWave * 2 * OPB;
+    static constexpr int TMB = TMA + kWave * OPB;
+    static constexpr int AQA = TMB + kWave * OPB;
+    static constexpr int MKB = AQA + kWave * OPB;
+    static constexpr int OB2 = MKB + kWave * OPB;
+    static constexpr int GAB = OB2 + kWave * 2 * OPB;
+    static constexpr int BYTES = GAB + D * 4;
+    static_assert(BYTES % 16 == 0, "pair block must be 16-byte granular");
+    // KD2 entry of lane (cl, g) of tile m (swizzled like the single-chunk Kd tile)
+    __device__ static __forceinline__ int kd2_offset(int m, int g, int cl) {
+        return KD2 + m * kWave * 2 * OPB + (g * 16 + (cl ^ (m & 15))) * 2 * OPB;
+    }
+    // element (r, c) of a K = 16 A operand at `base`
+    __device__ static __forceinline__ int a16_offset(int base, int r, int c) {
+        return base + ((c >> 2) * 16 + r) * OPB + (c & 3) * ES;
+    }
+    // element (r, c) of M_qb (which = 0) or Aqk_b (which = 1) in OB2
+    __device__ static __forceinline__ int ob2_offset(int r, int c, int which) {
+        return OB2 + ((c >> 2) * 16 + r) * 2 * OPB + (4 * which + (c & 3)) * ES;
+    }
+};
+
+template <typename E>
+using V8 = typename std::conditional<std::is_same<E, bf16>::value, bf16x8,
+                                     float __attribute__((ext_vector_type(8)))>::type;
+
+// ------------------------------------------------------------ producer
+//
+// Per-wave LDS staging of the pair producer: two A-row work areas (R1, R2),
+// Kh_a and Kh_b (A-row), Akk (16x16 fp32) and the small operands
+// [TMA, BYTES) of the pair block.
+template <typename E, int D>
+struct PStage {
+    using P = PBlk<E, D>;
+    static constexpr int R1 = 0;
+    static constexpr int R2 = R1 + P::AROW;
+    static constexpr int KHA = R2 + P::AROW;
+    static constexpr int KHB = KHA + P::AROW;
+    static constexpr int AKK = KHB + P::AROW;
+    static constexpr int SMALL = AKK + 16 * 16 * 4;           // holds P[TMA, BYTES)
+    static constexpr int BYTES = SMALL + (P::BYTES - P::TMA);
+    __device__ static __forceinline__ int small(int pblk_off) { return SMALL + pblk_off - P::TMA; }
+};
+
+// Copies `bytes` (a multiple of 16) from LDS to global memory.
+__device__ __forceinline__ void copy_out(char* __restrict__ dst, const char* src, int bytes) {
+    const uint4* s = reinterpret_cast<const uint4*>(src);
+    uint4* d = reinterpret_cast<uint4*>(dst);
+#pragma unroll 4
+    for (int x = lane_id(); x < bytes / 16; x += kWave) d[x] = s[x];
+}
+
+// Writes NCL values of one row of the lane's key columns into an A-row area.
+template <typename E, int D>
+__device__ __forceinline__ void arow_put(char* area, int c0, int r, const float* x) {
+    using B = Blk<E, D>;
+    const int off = B::arow_offset(c0, r);
+    if constexpr (B::NCL == 2 && B::kBF16) {
+        *reinterpret_cast<bf16x2*>(area + off) = bf16x2{(bf16)x[0], (bf16)x[1]};
+    } else if constexpr (B::NCL == 2) {
+        *reinterpret_cast<f32x2*>(area + off) = f32x2{x[0], x[1]};
+    } else {
+        *reinterpret_cast<E*>(area + off) = from_f32<E>(x[0]);
+    }
+}
+
+// 16x16 products of two A-row areas (K = D): acc[i][j] = sum_c A[i][c] Bm[j][c].
+template <typename E, int D>
+__device__ __forceinline__ f32x4 arow_gram(const char* A, const char* Bm) {
+    using B = Blk<E, D>;
+    const int lane = lane_id(), ci = lane & 15, g = lane >> 4;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < B::NSLOT; ++s) {
+        const int off = B::arow_chunk(s, g, ci);
+        const V16<E> a = *reinterpret_cast<const V16<E>*>(A + off);
+        const V16<E> b = *reinterpret_cast<const V16<E>*>(Bm + off);
+        if constexpr (B::kBF16) {
+            acc = mma_bf16_k32(a, b, acc);
+        } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) acc = mma_f32_k4(a[p], b[p], acc);
+        }
+    }
+    return acc;
+}
+
+// Gate of one chunk for the lane's key columns: P_r = e^{G_r} (inclusive
+// prefix of the retentions), Qs_r = e^{G_15 - G_r} (exclusive suffix), gam =
+// e^{G_15}.  Padded rows (r >= L) have retention 1.
+template <typename E, int D>
+__device__ __forceinline__ void pair_gate(const ProdIn<E, D>& in, const GateConsts& gc,
+                                          float (&P)[16][Blk<E, D>::NCL],
+                                          float (&Qs)[16][Blk<E, D>::NCL],
+                                          float (&gam)[Blk<E, D>::NCL]) {
+    using B = Blk<E, D>;
+    constexpr int NCL = B::NCL;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float zf[NCL];
+        unpack_seg<E, NCL, B::NWORD>(in.z[r], zf);
+#pragma unroll
+        for (int e = 0; e < NCL; ++e) {
+            const float a = r < in.L ? gate_alpha(gc, gate_sigmoid(gc, zf[e])) : 1.f;
+            Qs[r][e] = a;
+            P[r][e] = r == 0 ? a : P[r - 1][e] * a;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < NCL; ++e) {
+        gam[e] = P[15][e];
+        float run = 1.f;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) {
+            const float a = Qs[r][e];
+            Qs[r][e] = run;
+            run *= a;
+        }
+    }
+}
+
+// Akk (masked, times beta of its row) -> the fp32 scratch; returns nothing.
+__device__ __forceinline__ void put_akk(float* akk_s, const f32x4& akk, float bj) {
+    const int lane = lane_id(), ci = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = 4 * g + p;
+        const float br = __shfl(bj, r);
+        akk_s[r * 16 + ci] = ci < r ? br * akk[p] : 0.f;
+    }
+}
+
+// Tm = (I + Akk)^{-1} Diag(beta) by forward substitution (lane j < 16 solves
+// column j), written as a K = 16 A operand at `dst` (LDS).
+template <typename E, int D>
+__device__ __forceinline__ void put_tm(const float* akk_s, float bj, char* dst) {
+    using P = PBlk<E, D>;
+    const int lane = lane_id();
+    if (lane < 16) {
+        const int j = lane;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= akk_s[r * 16 + i] * x[i];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<E*>(dst + P::a16_offset(0, r, j)) = from_f32<E>(x[r] * bj);
+    }
+}
+
+// Gate + intra-chunk stage of chunks a, b of one pair (one wave), written to
+// the pair block at `out` (global memory) through the wave's staging `st`.
+template <typename E, int D>
+__device__ __forceinline__ void pair_produce(const ProdIn<E, D>& a, const ProdIn<E, D>& b,
+                                             const GateConsts& gc, char* __restrict__ st,
+                                             char* __restrict__ out) {
+    using B = Blk<E, D>;
+    using P = PBlk<E, D>;
+    using Sg = PStage<E, D>;
+    constexpr int NCL = B::NCL;
+    const int lane = lane_id(), ci = lane & 15, g = lane >> 4;
+    const bool owner = lane < B::NACT;
+    const int c0 = (lane % B::NACT) * NCL;
+    float* akk_s = reinterpret_cast<float*>(st + Sg::AKK);
+
+    // ------------------------------------------------ chunk a
+    float P_[16][NCL], Qs[16][NCL], gamA[NCL], gamB[NCL];
+    float kdA[16][NCL];
+    pair_gate<E, D>(a, gc, P_, Qs, gamA);
+    {
+        float rg[NCL];
+#pragma unroll
+        for (int e = 0; e < NCL; ++e) rg[e] = fast_rcp(gamA[e]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float kf[NCL], qf[NCL], kt[NCL], qt[NCL], kh[NCL];
+            unpack_seg<E, NCL, B::NWORD>(a.k[r], kf);
+            unpack_seg<E, NCL, B::NWORD>(a.q[r], qf);
+#pragma unroll
+            for (int e = 0; e < NCL; ++e) {
+                kt[e] = kf[e] * P_[r][e];
+                qt[e] = qf[e] * P_[r][e];
+                kdA[r][e] = kf[e] * Qs[r][e];
+                kh[e] = kdA[r][e] * rg[e];
+            }
+            if (owner) {
+                arow_put<E, D>(st + Sg::R1, c0, r, kt);
+                arow_put<E, D>(st + Sg::R2, c0, r, qt);
+                arow_put<E, D>(st + Sg::KHA, c0, r, kh);
+            }
+        }
+    }
+    wave_sync_lds();
+    {
+        const f32x4 akk = arow_gram<E, D>(st + Sg::R1, st + Sg::KHA);
+        const f32x4 aqk = arow_gram<E, D>(st + Sg::R2, st + Sg::KHA);
+        put_akk(akk_s, akk, a.bj);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = 4 * g + p;
+            *reinterpret_cast<E*>(st + Sg::small(P::a16_offset(P::AQA, r, ci))) =
+                from_f32<E>(ci <= r ? aqk[p] : 0.f);
+        }
+    }
+    wave_sync_lds();
+    put_tm<E, D>(akk_s, a.bj, st + Sg::small(P::TMA));
+    copy_out(out + P::KA, st + Sg::R1, P::AROW);
+    copy_out(out + P::QA, st + Sg::R2, P::AROW);
+    wave_sync_lds();   // R1, R2 and the Akk scratch are free again
+
+    // ------------------------------------------------ chunk b
+    pair_gate<E, D>(b, gc, P_, Qs, gamB);
+    {
+        float rg[NCL];
+#pragma unroll
+        for (int e = 0; e < NCL; ++e) rg[e] = fast_rcp(gamB[e]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float kf[NCL], qf[NCL], kt[NCL], qt[NCL], kh[NCL];
+            unpack_seg<E, NCL, B::NWORD>(b.k[r], kf);
+            unpack_seg<E, NCL, B::NWORD>(b.q[r], qf);
+#pragma unroll
+            for (int e = 0; e < NCL; ++e) {
+                kt[e] = kf[e] * P_[r][e];
+                qt[e] = qf[e] * P_[r][e];
+                const float kd = kf[e] * Qs[r][e];
+                kh[e] = kd * rg[e];
+                Qs[r][e] = kd;                       // Kd_b
+            }
+            if (owner) {
+                arow_put<E, D>(st + Sg::R1, c0, r, kt);   // Kt_b, unscaled
+                arow_put<E, D>(st + Sg::R2, c0, r, qt);   // Qt_b, unscaled
+                arow_put<E, D>(st + Sg::KHB, c0, r, kh);
+            }
+        }
+    }
+    // S-update operand and the pair decay go straight to the block
+    if (owner) {
+#pragma unroll
+        for (int e = 0; e < NCL; ++e) {
+            const int col = c0 + e;
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                V8<E> x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[i] = from_f32<E>(kdA[4 * gg + i][e] * gamB[e]);
+                    x[4 + i] = from_f32<E>(Qs[4 * gg + i][e]);
+                }
+                *reinterpret_cast<V8<E>*>(out + P::kd2_offset(col / 16, gg, col % 16)) = x;
+            }
+            reinterpret_cast<float*>(st + Sg::small(P::GAB))[col] = gamA[e] * gamB[e];
+        }
+    }
+    wave_sync_lds();
+    {
+        const f32x4 akk = arow_gram<E, D>(st + Sg::R1, st + Sg::KHB);
+        const f32x4 aqk = arow_gram<E, D>(st + Sg::R2, st + Sg::KHB);
+        put_akk(akk_s, akk, b.bj);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = 4 * g + p;
+            *reinterpret_cast<E*>(st + Sg::small(P::ob2_offset(r, ci, 1))) =
+                from_f32<E>(ci <= r ? aqk[p] : 0.f);
+        }
+    }
+    wave_sync_lds();   // Kt_b, Qt_b read: replace them by the gam_a-scaled copies
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float kf[NCL], qf[NCL], kt[NCL], qt[NCL];
+        unpack_seg<E, NCL, B::NWORD>(b.k[r], kf);
+        unpack_seg<E, NCL, B::NWORD>(b.q[r], qf);
+#pragma unroll
+        for (int e = 0; e < NCL; ++e) {
+            kt[e] = kf[e] * P_[r][e] * gamA[e];
+            qt[e] = qf[e] * P_[r][e] * gamA[e];
+        }
+        if (owner) {
+            arow_put<E, D>(st + Sg::R1, c0, r, kt);
+            arow_put<E, D>(st + Sg::R2, c0, r, qt);
+        }
+    }
+    wave_sync_lds();
+    {
+        // M_kb = (Kt_b Diag(gam_a)) Kh_a^T, M_qb = (Qt_b Diag(gam_a)) Kh_a^T
+        const f32x4 mkb = arow_gram<E, D>(st + Sg::R1, st + Sg::KHA);
+        const f32x4 mqb = arow_gram<E, D>(st + Sg::R2, st + Sg::KHA);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = 4 * g + p;
+            *reinterpret_cast<E*>(st + Sg::small(P::a16_offset(P::MKB, r, ci))) = from_f32<E>(mkb[p]);
+            *reinterpret_cast<E*>(st + Sg::small(P::ob2_offset(r, ci, 0))) = from_f32<E>(mqb[p]);
+        }
+    }
+    put_tm<E, D>(akk_s, b.bj, st + Sg::small(P::TMB));
+    wave_sync_lds();
+    copy_out(out + P::KB, st + Sg::R1, P::AROW);
+    copy_out(out + P::QB, st + Sg::R2, P::AROW);
+    copy_out(out + P::TMA, st + Sg::SMALL, P::BYTES - P::TMA);
+}
+
+// Pair intra kernel: one wave per pair (chunks n_first + 2p, n_first + 2p + 1
+// of every sequence; a chunk past the sequence's end is empty), writing the
+// pair blocks of the segment to `ws` ([B*H][NP] blocks).
+template <typename E, int D>
+__global__ __launch_bounds__(64) void pair_intra_kernel(const E* __restrict__ q,
+                                                        const E* __restrict__ k,
+                                                        const E* __restrict__ z,
+                                                        const float* __restrict__ beta,
+                                                        const float* __restrict__ A, float g_min,
+                                                        char* __restrict__ ws, int B, int T, int H,
+                                                        int n_first, int NP) {
+    using P = PBlk<E, D>;
+    __shared__ __attribute__((aligned(16))) char st[PStage<E, D>::BYTES];
+    const size_t id = blockIdx.x;
+    if (id >= (size_t)B * H * NP) return;
+    const int p = (int)(id % NP);
+    const int u = (int)(id / NP);
+    const int b = u / H, h = u % H;
+    const int n = n_first + 2 * p;
+    ProdIn<E, D> ca, cb;
+    prod_load<E, D>(ca, q, k, z, beta, chunk_pos<D>(b, h, n, T, H));
+    prod_load<E, D>(cb, q, k, z, beta, chunk_pos<D>(b, h, n + 1, T, H));
+    pair_produce<E, D>(ca, cb, make_gate(A[h], g_min), st, ws + id * (size_t)P::BYTES);
+}
+
+// ------------------------------------------------------------ chain
+
+// Pair operands in the chain's registers.
+template <typename E, int D>
+struct POps {
+    using P = PBlk<E, D>;
+    V16<E> ka[P::NSLOT], kb[P::NSLOT], qa[P::NSLOT], qb[P::NSLOT];
+    V8<E> kd2[P::MT];
+    V4<E> tma, tmb, aqa, mkb;
+    V8<E> ob2;
+    f32x4 gab[P::MT];
+};
+
+// The operands read first (Kt_a, Kt_b Diag(gam_a)): loaded one pair ahead.
+template <typename E, int D>
+__device__ __forceinline__ void pops_load_k(POps<E, D>& c, const char* blk) {
+    using P = PBlk<E, D>;
+    const int lane = lane_id(), g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int s = 0; s < P::NSLOT; ++s) {
+        const int off = P::B1::arow_chunk(s, g, r);
+        c.ka[s] = *reinterpret_cast<const V16<E>*>(blk + P::KA + off);
+        c.kb[s] = *reinterpret_cast<const V16<E>*>(blk + P::KB + off);
+    }
+}
+
+// Operands of the state chain, in the order it uses them.
+template <typename E, int D>
+__device__ __forceinline__ void pops_load_chain(POps<E, D>& c, const char* blk) {
+    using P = PBlk<E, D>;
+    const int lane = lane_id(), g = lane >> 4, r = lane & 15;
+    c.tma = *reinterpret_cast<const V4<E>*>(blk + P::TMA + lane * P::OPB);
+    c.mkb = *reinterpret_cast<const V4<E>*>(blk + P::MKB + lane * P::OPB);
+    c.tmb = *reinterpret_cast<const V4<E>*>(blk + P::TMB + lane * P::OPB);
+#pragma unroll
+    for (int m = 0; m < P::MT; ++m) {
+        c.gab[m] = *reinterpret_cast<const f32x4*>(blk + P::GAB + (16 * m + 4 * g) * 4);
+        c.kd2[m] = *reinterpret_cast<const V8<E>*>(blk + P::kd2_offset(m, g, r));
+    }
+}
+
+// Operands of the outputs only (used after the state update).
+template <typename E, int D>
+__device__ __forceinline__ void pops_load_out(POps<E, D>& c, const char* blk) {
+    using P = PBlk<E, D>;
+    const int lane = lane_id(), g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int s = 0; s < P::NSLOT; ++s) {
+        const int off = P::B1::arow_chunk(s, g, r);
+        c.qa[s] = *reinterpret_cast<const V16<E>*>(blk + P::QA + off);
+        c.qb[s] = *reinterpret_cast<const V16<E>*>(blk + P::QB + off);
+    }
+    c.aqa = *reinterpret_cast<const V4<E>*>(blk + P::AQA + lane * P::OPB);
+    c.ob2 = *reinterpret_cast<const V8<E>*>(blk + P::OB2 + lane * 2 * P::OPB);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// One pair of the state chain for NB 16-column blocks of S.  Va, Vb: V of
+// chunks a, b (accumulator layout); Oa, Ob receive the outputs.  The chain
+// (x, U, state update) is issued first; the outputs, which read the old
+// state, come last so their products fill the MFMA pipe behind the chain.
+template <typename E, int D, int NB>
+__device__ __forceinline__ void pair_step(const POps<E, D>& c, f32x4 (&S)[NB][D / 16],
+                                          const f32x4 (&Va)[NB], const f32x4 (&Vb)[NB],
+                                          f32x4 (&Oa)[NB], f32x4 (&Ob)[NB]) {
+    using P = PBlk<E, D>;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (P::B1::kBF16) {
+            bf16x8 sb[P::NSLOT];
+            f32x4 xa = zero4(), xb = zero4();
+#pragma unroll
+            for (int s = 0; s < P::NSLOT; ++s) {
+                sb[s] = pack8(S[nb][2 * s], S[nb][2 * s + 1]);
+                xa = mma_bf16_k32(c.ka[s], sb[s], xa);
+                xb = mma_bf16_k32(c.kb[s], sb[s], xb);
+            }
+            // every 16x16x16 product below starts from a zero accumulator: an
+            // MFMA of one shape must not take as srcC the in-flight result of
+            // an MFMA of another shape (16x16x32 -> 16x16x16 chains read stale
+            // srcC on gfx950)
+            const bf16x4 ua = pack4(mma_bf16_k16(c.tma, pack4(Va[nb] - xa), zero4()));
+            const f32x4 xbc = mma_bf16_k16(c.mkb, ua, zero4());
+            const bf16x4 ub = pack4(mma_bf16_k16(c.tmb, pack4(Vb[nb] - xb - xbc), zero4()));
+            const bf16x8 u2 = cat8(ua, ub);
+#pragma unroll
+            for (int m = 0; m < P::MT; ++m)
+                S[nb][m] = mma_bf16_k32(c.kd2[m], u2, S[nb][m] * c.gab[m]);
+            f32x4 oa = zero4(), ob = zero4();
+#pragma unroll
+            for (int s = 0; s < P::NSLOT; ++s) {
+                oa = mma_bf16_k32(c.qa[s], sb[s], oa);
+                ob = mma_bf16_k32(c.qb[s], sb[s], ob);
+            }
+            Oa[nb] = oa + mma_bf16_k16(c.aqa, ua, zero4());
+            Ob[nb] = ob + mma_bf16_k32(c.ob2, u2, zero4());
+        } else {
+            f32x4 xa = zero4(), xb = zero4(), oa = zero4(), ob = zero4();
+#pragma unroll
+            for (int m = 0; m < P::MT; ++m)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    xa = mma_f32_k4(c.ka[m][p], S[nb][m][p], xa);
+                    xb = mma_f32_k4(c.kb[m][p], S[nb][m][p], xb);
+                    oa = mma_f32_k4(c.qa[m][p], S[nb][m][p], oa);
+                    ob = mma_f32_k4(c.qb[m][p], S[nb][m][p], ob);
+                }
+            const f32x4 ya = Va[nb] - xa;
+            f32x4 ua = zero4();
+#pragma unroll
+            for (int p = 0; p < 4; ++p) ua = mma_f32_k4(c.tma[p], ya[p], ua);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) xb = mma_f32_k4(c.mkb[p], ua[p], xb);
+            const f32x4 yb = Vb[nb] - xb;
+            f32x4 ub = zero4();
+#pragma unroll
+            for (int p = 0; p < 4; ++p) ub = mma_f32_k4(c.tmb[p], yb[p], ub);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                oa = mma_f32_k4(c.aqa[p], ua[p], oa);
+                ob = mma_f32_k4(c.ob2[p], ua[p], ob);
+                ob = mma_f32_k4(c.ob2[4 + p], ub[p], ob);
+            }
+            Oa[nb] = oa;
+            Ob[nb] = ob;
+#pragma unroll
+            for (int m = 0; m < P::MT; ++m) {
+                f32x4 sm = S[nb][m] * c.gab[m];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    sm = mma_f32_k4(c.kd2[m][p], ua[p], sm);
+                    sm = mma_f32_k4(c.kd2[m][4 + p], ub[p], sm);
+                }
+                S[nb][m] = sm;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ pair inter kernel
+//
+// One workgroup per (b, h, tile of NCOL = 16 NB NCW value columns) over the
+// pairs of chunks [n_first, n_first + n_count).  Waves 0 .. NCW-1 each carry
+// the state of NB 16-column blocks; the other NL waves stream the pair blocks
+// (and, where the LDS holds them, the V tiles) into an LDS ring of NPAIR
+// entries shared by the chains.  A chain reads the pair it computes and the
+// first operands of the next pair, so two entries are in use per chain.
+//
+// Ring entries are handed over by LDS flags, not workgroup barriers, so the
+// chains run unaligned and never wait for each other:
+//   ready[e]  index of the last pair published in entry e (loader -> chains);
+//             a loader stores it after its data stores have completed;
+//   done[e][w]  index of the last pair chain w released from entry e
+//             (chains -> loaders); stored after the chain's last read of it.
+// Pair p goes to entry p mod NPAIR and belongs to loader p mod NL, which
+// writes it once every chain has released pair p - NPAIR.
+// The slowest chain at pair t waits only for pair t + 1, whose entry was last
+// held by pair t + 1 - NPAIR <= t - 1, which every chain has released; so no
+// wait closes a cycle.  Every wait is bounded (spin_until_ge).
+template <typename E, int D, int NCW_, int NB_>
+struct PairCfg {
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int NCW = NCW_, NB = NB_;
+    static constexpr int NCOL = 16 * NB * NCW;                   // value columns per workgroup
+    static constexpr int LDS_MAX = 160 * 1024 - 256;             // room for the flags
+    // V tiles of one pair: 32-bit word w of the tile's row r (two bf16 or one
+    // fp32 column) at word w * VSTR + r; the padding makes the loaders'
+    // word stores conflict-free across the 64 LDS banks
+    static constexpr int VSTR = 2 * kChunk + 2;
+    static constexpr int VBYTES = NCOL * ES / 4 * VSTR * 4;
+    static constexpr int ENT = PBlk<E, D>::BYTES + VBYTES;
+    static constexpr int NPAIR = LDS_MAX / ENT < 4 ? LDS_MAX / ENT : 4;
+    // loader waves: workgroups of at most four waves keep one wave per SIMD
+    // (the chains get the whole register file)
+    static constexpr int NL = NCW >= 4 ? 3 : 4 - NCW;
+    static constexpr int THREADS = (NCW + NL) * kWave;
+    static_assert(NCOL <= D, "column tile wider than the head");
+    static_assert(NPAIR >= 2, "the ring needs two pair entries");
+    static_assert((2 * kChunk * NCOL * ES / 16) % kWave == 0, "V pieces per loader lane");
+    static_assert(VBYTES % 16 == 0, "ring entries stay 16-byte aligned");
+};
+
+template <typename E, int D, int NCW, int NB>
+__global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_kernel(
+    const char* __restrict__ ws, const E* __restrict__ v, const float* S0, E* __restrict__ o,
+    float* ST, int B, int T, int H, int n_first, int n_count, int nct) {
+    using P = PBlk<E, D>;
+    using Cfg = PairCfg<E, D, NCW, NB>;
+    constexpr int NPAIR = Cfg::NPAIR, NL = Cfg::NL, ENT = Cfg::ENT, ES = Cfg::ES;
+    constexpr int NCOL = Cfg::NCOL;
+    constexpr int BLK16 = P::BYTES / 16;              // 16-byte pieces of one pair block
+    constexpr int PER_LANE = (BLK16 + kWave - 1) / kWave;
+    constexpr int RP = NCOL * ES / 16;                // 16-byte pieces per V row of the tile
+    constexpr int VPL = 2 * kChunk * RP / kWave;
+    constexpr int EPP = 16 / ES;                      // elements per piece
+    __shared__ __attribute__((aligned(16))) char ring[NPAIR * ENT];
+    __shared__ int ready[NPAIR], done[NPAIR][NCW];
+    int u, ct;
+    if (!map_unit(nct, B * H, u, ct)) return;   // uniform over the workgroup
+    const int b = u / H, h = u % H;
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int tile0 = ct * NCOL;
+    const int NP = (n_count + 1) / 2;
+    const char* blk0 = ws + (size_t)u * NP * P::BYTES;
+    const Rsrc rws = make_rsrc(blk0, (uint32_t)((size_t)NP * P::BYTES));
+    if (w == 0 && lane < NPAIR) {
+        ready[lane] = -1;
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) done[lane][c] = -1;
+    }
+    wg_barrier();   // the only barrier: flags initialised
+
+    if (w >= NCW) {
+        // ------------------------------------------------ loader waves
+        const int L = w - NCW;
+        u32x4 buf[PER_LANE];
+        u32x4 vbuf[VPL];
+        auto issue = [&](int p) {
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int piece = i * kWave + lane;
+                buf[i] = buf_load<u32x4>(rws, (p * BLK16 + piece) * 16);   // past the end: 0
+            }
+            // rows t0 .. t0+31 of the tile's columns; rows past T read 0
+            const int t0 = (n_first + 2 * p) * kChunk;
+            const int Lr = min(2 * kChunk, T - t0);
+            const size_t rs = (size_t)H * D;
+            const size_t row0 = ((size_t)b * T + t0) * H + h;
+            const Rsrc rv = make_rsrc(v + row0 * D + tile0,
+                                      Lr > 0 ? (uint32_t)(((size_t)(Lr - 1) * rs + NCOL) * ES) : 0u);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int q = i * kWave + lane, r = q / RP, c = q % RP;
+                vbuf[i] = buf_load<u32x4>(rv, (int)((r * rs + c * EPP) * ES));
+            }
+        };
+        auto write = [&](int p) {
+            char* dst = ring + (p % NPAIR) * ENT;
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int piece = i * kWave + lane;
+                if (piece < BLK16) *reinterpret_cast<u32x4*>(dst + piece * 16) = buf[i];
+            }
+            // V area: word-major (word w of row r at w * VSTR + r), so a
+            // chain reads the four rows of its column as 16 bytes
+            uint32_t* vd = reinterpret_cast<uint32_t*>(dst + P::BYTES);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int q = i * kWave + lane, r = q / RP, c = q % RP;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vd[(4 * c + e) * Cfg::VSTR + r] = vbuf[i][e];
+            }
+        };
+        if (L < NP) issue(L);
+        for (int p = L; p < NP; p += NL) {
+            const int e = p % NPAIR;
+            if (p >= NPAIR) {   // every chain has released the entry's previous pair
+#pragma unroll
+                for (int c = 0; c < NCW; ++c) spin_until_ge(&done[e][c], p - NPAIR);
+            }
+            write(p);
+            // publish: the data stores complete before the flag store
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __hip_atomic_store(&ready[e], p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (p + NL < NP) issue(p + NL);
+        }
+        return;
+    }
+    // ---------------------------------------------------- state chains
+    const int j = lane & 15, g = lane >> 4;
+    const int col0 = tile0 + 16 * NB * w;
+    auto entry = [&](int p) { return ring + (p % NPAIR) * ENT; };
+    // V of chunk half (0 = a, 1 = b) of the pair in entry `ent`, NB blocks:
+    // the raw words (read), then widened to fp32 (widen) once they are needed
+    auto v_read = [&](const char* ent, int half, u32x4 (&V)[NB]) {
+        const uint32_t* base = reinterpret_cast<const uint32_t*>(ent + P::BYTES) + half * kChunk + 4 * g;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int vcol = 16 * (NB * w + nb) + j;   // column within the tile
+            const uint32_t* at = base + (ES == 2 ? vcol >> 1 : vcol) * Cfg::VSTR;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(at);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(at + 2);
+            V[nb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+    auto v_widen2 = [&](const u32x4 (&X)[NB], f32x4 (&V)[NB]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            u32x4 x = X[nb];
+            if constexpr (ES == 2) {
+                const int vcol = 16 * (NB * w + nb) + j;
+                x <<= 16 * (1 - (vcol & 1));   // bf16 of this column to the high half
+                x &= 0xFFFF0000u;
+            }
+            V[nb] = __builtin_bit_cast(f32x4, x);
+        }
+    };
+    f32x4 S[NB][D / 16];
+    state_load<D, NB>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
+    POps<E, D> c;
+    // The loop body is one basic block (a branch inside it keeps the
+    // scheduler from overlapping a step's tail with what follows): the next
+    // pair's first operands are read speculatively at the end of a step,
+    // after its ready flag (LDS executes a wave's operations in order, so the
+    // data read after a flag that shows the pair published is that pair's);
+    // the rare re-read happens at the top of the next step.
+    spin_until_ge(&ready[0], 0);
+    pops_load_k<E, D>(c, entry(0));
+    int fl = 0;
+    for (int s = 0; s < NP; ++s) {
+        const char* ent = entry(s);
+        if (fl < s) {
+            spin_until_ge(&ready[s % NPAIR], s);
+            pops_load_k<E, D>(c, ent);
+        }
+        f32x4 Va[NB], Vb[NB], Oa[NB], Ob[NB];
+        u32x4 ra[NB], rb[NB];
+        // LDS reads in the order of first use (the wait counter is in order)
+        v_read(ent, 0, ra);
+        v_read(ent, 1, rb);
+        pops_load_chain<E, D>(c, ent);
+        pops_load_out<E, D>(c, ent);
+        // all reads are issued here, ahead of the chain (the scheduler would
+        // otherwise sink each to its use and expose its latency); the fp32
+        // operands would not fit the registers at once
+        if constexpr (ES == 2) pin_issued();
+        v_widen2(ra, Va);
+        v_widen2(rb, Vb);
+        pair_step<E, D, NB>(c, S, Va, Vb, Oa, Ob);
+        // release pair s: its reads were all issued above
+        asm volatile("" ::: "memory");
+        __hip_atomic_store(&done[s % NPAIR][w], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        fl = __hip_atomic_load(&ready[(s + 1) % NPAIR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        asm volatile("" ::: "memory");
+        pops_load_k<E, D>(c, entry(s + 1));   // (past the last pair: stale, unused)
+        const int n0 = n_first + 2 * s;
+        o_store<E, D, NB>(Oa, o, chunk_pos<D>(b, h, n0, T, H), col0);
+        o_store<E, D, NB>(Ob, o, chunk_pos<D>(b, h, n0 + 1, T, H), col0);
+    }
+    if (ST) state_store<D, NB>(S, ST + (size_t)u * D * D, col0);
+}
+
+// ------------------------------------------------------------ launch
+
+size_t pair_block_bytes(int d, bool is_bf16) {
+    if (is_bf16) return d == 128 ? (size_t)PBlk<bf16, 128>::BYTES : (size_t)PBlk<bf16, 32>::BYTES;
+    return d == 128 ? (size_t)PBlk<float, 128>::BYTES : (size_t)PBlk<float, 32>::BYTES;
+}
+
+bool pair_variant_ok(int d, bool is_bf16, int ncol, int nb) {
+    if (nb != 1 && nb != 2) return false;
+    const int ncw = ncol / (16 * nb);
+    if (ncw * 16 * nb != ncol || ncol > d) return false;
+    // two-block chains: bf16 with d = 128 (their operands and two states fill
+    // the register file); four fp32 chains would not fit a shared SIMD
+    if (nb == 2) return d == 128 && is_bf16 && (ncw == 1 || ncw == 2);
+    return ncw == 1 || ncw == 2 || (ncw == 4 && d == 128 && is_bf16);
+}
+
+static unsigned pair_grid(int units, int nct) { return (unsigned)(((units + 7) / 8) * 8 * nct); }
+
+template <typename E, int D, int NCW, int NB>
+static hipError_t launch_pair_inter_v(const char* ws, const E* v, const float* s_in, E* o,
+                                      float* s_out, const PrefillArgs& a, int n_first,
+                                      int n_count, hipStream_t stream) {
+    using Cfg = PairCfg<E, D, NCW, NB>;
+    const int nct = D / Cfg::NCOL;
+    hipLaunchKernelGGL((pair_inter_kernel<E, D, NCW, NB>), dim3(pair_grid(a.B * a.H, nct)),
+                       dim3(Cfg::THREADS), 0, stream, ws, v, s_in, o, s_out, a.B, a.T, a.H,
+                       n_first, n_count, nct);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t launch_split_t(const PrefillArgs& a, const PlanInfo& p, void* ws,
+                                 hipStream_t stream) {
+    using P = PBlk<E, D>;
+    const int units = a.B * a.H;
+    const int NC = (a.T + kChunk - 1) / kChunk;
+    const int seg = NC < kSegChunks ? NC : kSegChunks;
+    const int NPmax = (seg + 1) / 2;
+    char* fws = (char*)ws;
+    float* carry = a.S_T;
+    if (NC > seg && !carry) carry = (float*)(fws + (size_t)units * NPmax * P::BYTES);
+    const E* v = (const E*)a.v;
+    E* o = (E*)a.o;
+    for (int n_first = 0; n_first < NC; n_first += seg) {
+        const int n_count = (NC - n_first) < seg ? (NC - n_first) : seg;
+        const int NP = (n_count + 1) / 2;
+        hipLaunchKernelGGL((pair_intra_kernel<E, D>), dim3((unsigned)((size_t)units * NP)), dim3(64),
+                           0, stream, (const E*)a.q, (const E*)a.k, (const E*)a.z, a.beta, a.A,
+                           a.g_min, fws, a.B, a.T, a.H, n_first, NP);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const float* s_in = n_first == 0 ? a.S0 : carry;
+        const bool last = n_first + n_count >= NC;
+        float* s_out = last ? a.S_T : carry;
+#define KDA_PAIR_INTER(NCW, NB) \
+    e = launch_pair_inter_v<E, D, NCW, NB>(fws, v, s_in, o, s_out, a, n_first, n_count, stream)
+        if constexpr (D == 128 && sizeof(E) == 2) {
+            if (p.nb == 2 && p.ncol == 64) KDA_PAIR_INTER(2, 2);
+            else if (p.nb == 2) KDA_PAIR_INTER(1, 2);
+            else if (p.ncol == 64) KDA_PAIR_INTER(4, 1);
+            else if (p.ncol == 32) KDA_PAIR_INTER(2, 1);
+            else KDA_PAIR_INTER(1, 1);
+        } else {
+            if (p.ncol == 32) KDA_PAIR_INTER(2, 1);
+            else KDA_PAIR_INTER(1, 1);
+        }
+#undef KDA_PAIR_INTER
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_split(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream) {
+    if (a.is_bf16)
+        return a.d == 128 ? launch_split_t<bf16, 128>(a, p, ws, stream)
+                          : launch_split_t<bf16, 32>(a, p, ws, stream);
+    return a.d == 128 ? launch_split_t<float, 128>(a, p, ws, stream)
+                      : launch_split_t<float, 32>(a, p, ws, stream);
+}
+
+}  // namespace kda

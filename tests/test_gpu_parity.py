@@ -148,7 +148,7 @@ def test_intra_chunk(d, dt):
 
 # ------------------------------------------------------------------ prefill, small shapes
 
-PLANS = ["auto", "split", "split:16:0", "split:16:1", "split:32:1", "split:64:1", "split:32:2", "split:64:2",
+PLANS = ["auto", "split", "split:16:1", "split:32:1", "split:64:1", "split:32:2", "split:64:2",
          "fused:16", "fused:32", "fused:64", "fused:128"]
 SHAPES = [(2, 100, 3, True), (1, 1, 2, False), (1, 15, 1, True), (1, 17, 2, False),
           (3, 33, 1, True), (1, 64, 2, False)]
@@ -159,12 +159,12 @@ def plan_ok(p, d, dt):
     unavailable override would silently fall back to the size-chosen plan)."""
     if p.startswith("split:"):
         ncol, nb = (int(t) for t in p.split(":")[1:])
-        if nb == 0:
-            return ncol == 16
         ncw = ncol // (16 * nb)
-        if ncol > d or (nb == 2 and dt == "f32" and d == 128):
+        if ncol > d:
             return False
-        return ncw in (1, 2) or (ncw == 4 and d == 128 and nb == 1)
+        if nb == 2:
+            return d == 128 and dt == "bf16" and ncw in (1, 2)
+        return ncw in (1, 2) or (ncw == 4 and d == 128 and dt == "bf16")
     if not p.startswith("fused:"):
         return True
     n = int(p.split(":")[1])

@@ -4,7 +4,7 @@ of a different shape issued shortly before it.
 On gfx950 a 16x16x16 bf16 MFMA accumulating onto a 16x16x32 bf16 MFMA's
 result still in flight read stale srcC registers (wrong rows of some chunks,
 non-deterministically), so the prefill kernels never form such chains.  This
-test compiles the prefill source exactly as the library build does and scans
+test compiles the prefill sources exactly as the library build does and scans
 every kernel's ISA for one."""
 import os
 import re
@@ -60,13 +60,14 @@ def test_scanner_flags_a_planted_chain():
     assert mixed_shape_chains(same) == []
 
 
-def test_prefill_kernels_have_no_mixed_shape_srcc_chain(tmp_path):
+@pytest.mark.parametrize("source", ["kda_prefill.hip", "kda_pair.hip"])
+def test_prefill_kernels_have_no_mixed_shape_srcc_chain(tmp_path, source):
     cmd = kbuild.hipcc_command(str(tmp_path / "unused.so"))
-    # same flags, device-only assembly of the prefill translation unit
+    # same flags, device-only assembly of one prefill translation unit
     flags = [c for c in cmd[1:] if c not in ("-shared",) and not c.endswith(".hip")]
     out_i = flags.index("-o")
     flags = flags[:out_i] + flags[out_i + 2:]
-    src = os.path.join(kbuild.CSRC, "kda_prefill.hip")
+    src = os.path.join(kbuild.CSRC, source)
     asm = tmp_path / "prefill.s"
     subprocess.run([cmd[0], *flags, "--cuda-device-only", "-S", src, "-o", str(asm)],
                    check=True, capture_output=True)
