@@ -252,8 +252,12 @@ PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16) {
         return p;
     }
     p.plan = Plan::kSplit;
-    if (p.ncol == 0) {   // default inter variant: four chains (two for fp32)
-        p.ncol = is_bf16 && d >= 64 ? 64 : 32;
+    if (p.ncol == 0) {
+        // default inter variant: one state chain per workgroup (a CU to
+        // itself) while all chains fit on the chip's 256 CUs at once, else
+        // four chains (two for fp32) sharing each workgroup's factor stream
+        const long chains = units * (d / 16);
+        p.ncol = chains <= 256 ? 16 : (is_bf16 && d >= 64 ? 64 : 32);
         p.nb = 1;
     }
     const int seg = NC < kSegChunks ? NC : kSegChunks;
