@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 One step = one chunkwise prefill pass (gate + intra-chunk + inter-chunk, all
-in libkda's HIP kernels) over the mid-size synthetic workload: B=1, H=32,
+in libkda's HIP kernels: for this workload a pair-producer launch and a
+state-chain launch) over the mid-size synthetic workload: B=1, H=32,
 T=4096, d_k=d_v=128, bf16 q/k/v/z, fp32 beta/A/state, g_min=-5.  Inputs are
 resident in HBM before timing; a 1 GiB write between steps evicts them from
 the 256 MB Infinity Cache so each step reads HBM (the write is outside the
@@ -165,7 +166,8 @@ def main():
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"prefill_{args.workload}_pass_bytes_{'split' if nb else 'fused'}"),
                      "traffic_unit": "bytes per pass",
-                     "kernel": "prefill pass (intra_kernel + inter_kernel)" if nb else "prefill pass (fused_kernel)",
+                     "kernel": ("prefill pass (pair_intra_kernel + pair_inter_kernel)" if nb
+                                else "prefill pass (fused_kernel)"),
                      "alg_bytes_per_step": alg_b,
                      "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
                      "alg_flops_per_step": alg_f},
