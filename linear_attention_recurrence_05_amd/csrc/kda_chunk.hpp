@@ -226,7 +226,7 @@ __device__ __forceinline__ void prod_compute(const ProdIn<E, D>& in, const GateC
         unpack_seg<E, NCL, B::NWORD>(in.z[r], zf);
 #pragma unroll
         for (int e = 0; e < NCL; ++e) {
-            const float a = r < L ? gate_alpha(gc, gate_sigmoid(gc, zf[e])) : 1.f;
+            const float a = gate_alpha_row(gc, zf[e], r < L ? 1.f : 0.f);
             Qs[r][e] = a;                           // holds a_r until the suffix pass
             P[r][e] = r == 0 ? a : P[r - 1][e] * a;
         }

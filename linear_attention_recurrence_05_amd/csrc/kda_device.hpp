@@ -73,6 +73,16 @@ __device__ __forceinline__ float gate_alpha(const GateConsts& c, float s) {
     return fast_exp2(s * c.gmin_log2e);
 }
 
+// Retention of gate input z in a row that may be padding: keep = 1 for a real
+// row (the same value as gate_alpha(c, gate_sigmoid(c, z))), keep = 0 for
+// padding, whose retention is then exactly e^0 = 1.  A multiply instead of a
+// select keeps the code branch-free: the compiler turns a select between e^g
+// and 1 on the uniform row count into a branch around the exponentials,
+// which splits an unrolled loop over rows into one scheduling region per row.
+__device__ __forceinline__ float gate_alpha_row(const GateConsts& c, float z, float keep) {
+    return fast_exp2(gate_sigmoid(c, z) * keep * c.gmin_log2e);
+}
+
 // ------------------------------------------------------------------ buffers
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
@@ -108,6 +118,14 @@ __device__ __forceinline__ void buf_store_u32(Rsrc r, int off, uint32_t x) {
 // ------------------------------------------------------------------ lanes
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+// The same value, recomputed at every call: values derived from it are not
+// hoisted out of a persistent loop and kept live across its iterations
+// (which costs registers when the loop body already needs nearly all).
+__device__ __forceinline__ int fresh_lane_id() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t & (kWave - 1);   // the mask after the asm keeps the range known
+}
 // Index of this wave in its workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));

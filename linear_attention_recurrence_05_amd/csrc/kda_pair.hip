@@ -80,8 +80,11 @@ using V8 = typename std::conditional<std::is_same<E, bf16>::value, bf16x8,
 // ------------------------------------------------------------ producer
 //
 // Per-wave LDS staging of the pair producer: two A-row work areas (R1, R2),
-// Kh_a and Kh_b (A-row), Akk (16x16 fp32) and the small operands
-// [TMA, BYTES) of the pair block.
+// Kh_a and Kh_b (A-row) and the small operands [TMA, BYTES) of the pair
+// block.  The Akk scratch (16x16 fp32) of each solve shares Kh_b's area: the
+// solve of chunk a ends before Kh_b is written, and that of chunk b begins
+// after Kh_b's last read (the Gram products of chunk b), so 8 producer waves
+// fit one CU's LDS at bf16, D = 128.
 template <typename E, int D>
 struct PStage {
     using P = PBlk<E, D>;
@@ -89,8 +92,9 @@ struct PStage {
     static constexpr int R2 = R1 + P::AROW;
     static constexpr int KHA = R2 + P::AROW;
     static constexpr int KHB = KHA + P::AROW;
-    static constexpr int AKK = KHB + P::AROW;
-    static constexpr int SMALL = AKK + 16 * 16 * 4;           // holds P[TMA, BYTES)
+    static constexpr int AKK = KHB;
+    static_assert(16 * 16 * 4 <= P::AROW, "Akk scratch must fit in Kh_b's area");
+    static constexpr int SMALL = KHB + P::AROW;               // holds P[TMA, BYTES)
     static constexpr int BYTES = SMALL + (P::BYTES - P::TMA);
     __device__ static __forceinline__ int small(int pblk_off) { return SMALL + pblk_off - P::TMA; }
 };
@@ -100,7 +104,7 @@ __device__ __forceinline__ void copy_out(char* __restrict__ dst, const char* src
     const uint4* s = reinterpret_cast<const uint4*>(src);
     uint4* d = reinterpret_cast<uint4*>(dst);
 #pragma unroll 4
-    for (int x = lane_id(); x < bytes / 16; x += kWave) d[x] = s[x];
+    for (int x = fresh_lane_id(); x < bytes / 16; x += kWave) d[x] = s[x];
 }
 
 // Writes NCL values of one row of the lane's key columns into an A-row area.
@@ -121,7 +125,7 @@ __device__ __forceinline__ void arow_put(char* area, int c0, int r, const float*
 template <typename E, int D>
 __device__ __forceinline__ f32x4 arow_gram(const char* A, const char* Bm) {
     using B = Blk<E, D>;
-    const int lane = lane_id(), ci = lane & 15, g = lane >> 4;
+    const int lane = fresh_lane_id(), ci = lane & 15, g = lane >> 4;
     f32x4 acc = zero4();
 #pragma unroll
     for (int s = 0; s < B::NSLOT; ++s) {
@@ -154,7 +158,7 @@ __device__ __forceinline__ void pair_gate(const ProdIn<E, D>& in, const GateCons
         unpack_seg<E, NCL, B::NWORD>(in.z[r], zf);
 #pragma unroll
         for (int e = 0; e < NCL; ++e) {
-            const float a = r < in.L ? gate_alpha(gc, gate_sigmoid(gc, zf[e])) : 1.f;
+            const float a = gate_alpha_row(gc, zf[e], r < in.L ? 1.f : 0.f);
             Qs[r][e] = a;
             P[r][e] = r == 0 ? a : P[r - 1][e] * a;
         }
@@ -174,7 +178,7 @@ __device__ __forceinline__ void pair_gate(const ProdIn<E, D>& in, const GateCons
 
 // Akk (masked, times beta of its row) -> the fp32 scratch; returns nothing.
 __device__ __forceinline__ void put_akk(float* akk_s, const f32x4& akk, float bj) {
-    const int lane = lane_id(), ci = lane & 15, g = lane >> 4;
+    const int lane = fresh_lane_id(), ci = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int r = 4 * g + p;
@@ -188,7 +192,7 @@ __device__ __forceinline__ void put_akk(float* akk_s, const f32x4& akk, float bj
 template <typename E, int D>
 __device__ __forceinline__ void put_tm(const float* akk_s, float bj, char* dst) {
     using P = PBlk<E, D>;
-    const int lane = lane_id();
+    const int lane = fresh_lane_id();
     if (lane < 16) {
         const int j = lane;
         float x[16];
@@ -207,15 +211,21 @@ __device__ __forceinline__ void put_tm(const float* akk_s, float bj, char* dst) 
 
 // Gate + intra-chunk stage of chunks a, b of one pair (one wave), written to
 // the pair block at `out` (global memory) through the wave's staging `st`.
-template <typename E, int D>
-__device__ __forceinline__ void pair_produce(const ProdIn<E, D>& a, const ProdIn<E, D>& b,
+// `next_a()` is called once the inputs in a are no longer needed and
+// `next_b()` once those in b are (each may load the next pair's inputs into
+// them, so the loads overlap the rest of this pair's work).  They come after
+// each chunk's triangular solve, so the solve's registers are never live
+// beside both chunks' new inputs.
+template <typename E, int D, typename NextA, typename NextB>
+__device__ __forceinline__ void pair_produce(ProdIn<E, D>& a, ProdIn<E, D>& b,
                                              const GateConsts& gc, char* __restrict__ st,
-                                             char* __restrict__ out) {
+                                             char* __restrict__ out, NextA next_a,
+                                             NextB next_b) {
     using B = Blk<E, D>;
     using P = PBlk<E, D>;
     using Sg = PStage<E, D>;
     constexpr int NCL = B::NCL;
-    const int lane = lane_id(), ci = lane & 15, g = lane >> 4;
+    const int lane = fresh_lane_id(), ci = lane & 15, g = lane >> 4;
     const bool owner = lane < B::NACT;
     const int c0 = (lane % B::NACT) * NCL;
     float* akk_s = reinterpret_cast<float*>(st + Sg::AKK);
@@ -261,6 +271,10 @@ __device__ __forceinline__ void pair_produce(const ProdIn<E, D>& a, const ProdIn
     }
     wave_sync_lds();
     put_tm<E, D>(akk_s, a.bj, st + Sg::small(P::TMA));
+    // a is free from here on; the fence keeps next_a()'s loads after its
+    // last reads (hoisted, both pairs' chunk-a inputs would be live at once)
+    pin_issued();
+    next_a();
     copy_out(out + P::KA, st + Sg::R1, P::AROW);
     copy_out(out + P::QA, st + Sg::R2, P::AROW);
     wave_sync_lds();   // R1, R2 and the Akk scratch are free again
@@ -337,6 +351,7 @@ __device__ __forceinline__ void pair_produce(const ProdIn<E, D>& a, const ProdIn
             arow_put<E, D>(st + Sg::R2, c0, r, qt);
         }
     }
+    const float bjb = b.bj;
     wave_sync_lds();
     {
         // M_kb = (Kt_b Diag(gam_a)) Kh_a^T, M_qb = (Qt_b Diag(gam_a)) Kh_a^T
@@ -349,18 +364,23 @@ __device__ __forceinline__ void pair_produce(const ProdIn<E, D>& a, const ProdIn
             *reinterpret_cast<E*>(st + Sg::small(P::ob2_offset(r, ci, 0))) = from_f32<E>(mqb[p]);
         }
     }
-    put_tm<E, D>(akk_s, b.bj, st + Sg::small(P::TMB));
+    put_tm<E, D>(akk_s, bjb, st + Sg::small(P::TMB));
+    pin_issued();
+    next_b();
     wave_sync_lds();
     copy_out(out + P::KB, st + Sg::R1, P::AROW);
     copy_out(out + P::QB, st + Sg::R2, P::AROW);
     copy_out(out + P::TMA, st + Sg::SMALL, P::BYTES - P::TMA);
 }
 
-// Pair intra kernel: one wave per pair (chunks n_first + 2p, n_first + 2p + 1
-// of every sequence; a chunk past the sequence's end is empty), writing the
-// pair blocks of the segment to `ws` ([B*H][NP] blocks).
+// Pair intra kernel over the [B*H][NP] pairs of a segment (chunks
+// n_first + 2p, n_first + 2p + 1 of every sequence; a chunk past the
+// sequence's end is empty), writing their pair blocks to `ws`.  Each wave
+// produces pairs id, id + gridDim.x, ..., and loads the next pair's inputs
+// as soon as the current pair's are consumed (same registers), so the loads
+// overlap the rest of the pair's work.
 template <typename E, int D>
-__global__ __launch_bounds__(64) void pair_intra_kernel(const E* __restrict__ q,
+__global__ __launch_bounds__(64, 2) void pair_intra_kernel(const E* __restrict__ q,
                                                         const E* __restrict__ k,
                                                         const E* __restrict__ z,
                                                         const float* __restrict__ beta,
@@ -369,16 +389,53 @@ __global__ __launch_bounds__(64) void pair_intra_kernel(const E* __restrict__ q,
                                                         int n_first, int NP) {
     using P = PBlk<E, D>;
     __shared__ __attribute__((aligned(16))) char st[PStage<E, D>::BYTES];
-    const size_t id = blockIdx.x;
-    if (id >= (size_t)B * H * NP) return;
-    const int p = (int)(id % NP);
-    const int u = (int)(id / NP);
-    const int b = u / H, h = u % H;
-    const int n = n_first + 2 * p;
+    // pair (u, p): unit u = b * H + h, pair p of the segment; the wave's
+    // pairs are blockIdx.x, blockIdx.x + gridDim.x, ... in (u, p) order,
+    // stepped without a division per pair
+    const int units = B * H;
+    int u = (int)(blockIdx.x / (unsigned)NP), p = (int)(blockIdx.x % (unsigned)NP);
+    if (u >= units) return;
+    const int du = (int)(gridDim.x / (unsigned)NP), dp = (int)(gridDim.x % (unsigned)NP);
+    // chunk `half` (0: first, 1: second) of pair (pu, pp); with !live an
+    // empty chunk (no memory access: its buffers have size 0), so the loads
+    // need no branch
+    auto load = [&](int pu, int pp, int half, bool live, ProdIn<E, D>& c) {
+        ChunkPos cp = chunk_pos<D>(pu / H, pu % H, n_first + 2 * pp + half, T, H);
+        cp.L = live ? cp.L : 0;
+        prod_load<E, D>(c, q, k, z, beta, cp);
+    };
     ProdIn<E, D> ca, cb;
-    prod_load<E, D>(ca, q, k, z, beta, chunk_pos<D>(b, h, n, T, H));
-    prod_load<E, D>(cb, q, k, z, beta, chunk_pos<D>(b, h, n + 1, T, H));
-    pair_produce<E, D>(ca, cb, make_gate(A[h], g_min), st, ws + id * (size_t)P::BYTES);
+    load(u, p, 0, true, ca);
+    load(u, p, 1, true, cb);
+    for (;;) {
+        int nu = u + du, np = p + dp;
+        if (np >= NP) { np -= NP; ++nu; }
+        const bool more = nu < units;
+        char* out = ws + ((size_t)u * NP + p) * (size_t)P::BYTES;
+        pair_produce<E, D>(ca, cb, make_gate(A[u % H], g_min), st, out,
+                           [&] { load(nu, np, 0, more, ca); },
+                           [&] { load(nu, np, 1, more, cb); });
+        if (!more) break;
+        u = nu;
+        p = np;
+    }
+}
+
+// Producer waves for `pairs` pairs: as many as are resident at once on the
+// 256 CUs (registers and LDS staging decide how many per CU: 8 at bf16,
+// D = 128), each producing the same number of pairs.
+template <typename E, int D>
+static unsigned intra_grid(size_t pairs) {
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pair_intra_kernel<E, D>, 64, 0) !=
+                hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    const size_t slots = 256 * (size_t)per_cu;
+    const size_t per = (pairs + slots - 1) / slots;
+    return (unsigned)((pairs + per - 1) / per);
 }
 
 // ------------------------------------------------------------ chain
@@ -774,7 +831,7 @@ static hipError_t launch_split_t(const PrefillArgs& a, const PlanInfo& p, void* 
     for (int n_first = 0; n_first < NC; n_first += seg) {
         const int n_count = (NC - n_first) < seg ? (NC - n_first) : seg;
         const int NP = (n_count + 1) / 2;
-        hipLaunchKernelGGL((pair_intra_kernel<E, D>), dim3((unsigned)((size_t)units * NP)), dim3(64),
+        hipLaunchKernelGGL((pair_intra_kernel<E, D>), dim3(intra_grid<E, D>((size_t)units * NP)), dim3(64),
                            0, stream, (const E*)a.q, (const E*)a.k, (const E*)a.z, a.beta, a.A,
                            a.g_min, fws, a.B, a.T, a.H, n_first, NP);
         hipError_t e = hipGetLastError();
