@@ -12,6 +12,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace kda {
 
@@ -111,6 +112,9 @@ template <> __device__ __forceinline__ unsigned short buf_load<unsigned short>(R
 __device__ __forceinline__ void buf_store_u16(Rsrc r, int off, unsigned short x) {
     __builtin_amdgcn_raw_buffer_store_b16(x, r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_store_u32x4(Rsrc r, int off, u32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+}
 __device__ __forceinline__ void buf_store_u32(Rsrc r, int off, uint32_t x) {
     __builtin_amdgcn_raw_buffer_store_b32(x, r, off, 0, 0);
 }
@@ -118,6 +122,24 @@ __device__ __forceinline__ void buf_store_u32(Rsrc r, int off, uint32_t x) {
 // ------------------------------------------------------------------ lanes
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// x of lane L of each row of 16 lanes, for every lane of the row (a DPP
+// row broadcast: a VALU operand modifier, no LDS traffic)
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+    static_assert(L >= 0 && L < 16, "row lane");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x150 + L, 0xF, 0xF, false));
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, each with a compile-time index
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 // The same value, recomputed at every call: values derived from it are not
 // hoisted out of a persistent loop and kept live across its iterations
 // (which costs registers when the loop body already needs nearly all).

@@ -448,8 +448,17 @@ struct POps {
     V8<E> kd2[P::MT];
     V4<E> tma, tmb, aqa, mkb;
     V8<E> ob2;
-    f32x4 gab[P::MT];
+    f32x2 gv;   // two values of gam_a gam_b per lane (see gab_tile)
 };
+
+// gam_a gam_b of rows 16 M + 4 g + p (p = 0..3) of tile M for lane (j, g).
+// Lane (k, g) holds rows 16 (k/2) + 4 g + 2 (k%2) + {0, 1} of the vector, and
+// row broadcasts deliver them: the lane reads 8 bytes instead of 16 per tile.
+template <int M>
+__device__ __forceinline__ f32x4 gab_tile(const f32x2& gv) {
+    return f32x4{row_bcast<2 * M>(gv[0]), row_bcast<2 * M>(gv[1]),
+                 row_bcast<2 * M + 1>(gv[0]), row_bcast<2 * M + 1>(gv[1])};
+}
 
 // The operands read first (Kt_a, Kt_b Diag(gam_a)): loaded one pair ahead.
 template <typename E, int D>
@@ -472,9 +481,12 @@ __device__ __forceinline__ void pops_load_chain(POps<E, D>& c, const char* blk) 
     c.tma = *reinterpret_cast<const V4<E>*>(blk + P::TMA + lane * P::OPB);
     c.mkb = *reinterpret_cast<const V4<E>*>(blk + P::MKB + lane * P::OPB);
     c.tmb = *reinterpret_cast<const V4<E>*>(blk + P::TMB + lane * P::OPB);
+    {
+        const int mm = min(r >> 1, P::MT - 1);   // lanes past the last tile read a valid word
+        c.gv = *reinterpret_cast<const f32x2*>(blk + P::GAB + (16 * mm + 4 * g + 2 * (r & 1)) * 4);
+    }
 #pragma unroll
     for (int m = 0; m < P::MT; ++m) {
-        c.gab[m] = *reinterpret_cast<const f32x4*>(blk + P::GAB + (16 * m + 4 * g) * 4);
         c.kd2[m] = *reinterpret_cast<const V8<E>*>(blk + P::kd2_offset(m, g, r));
     }
 }
@@ -496,6 +508,61 @@ __device__ __forceinline__ void pops_load_out(POps<E, D>& c, const char* blk) {
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// The first products of a pair (bf16): S packed once, x_a = Kt_a S and
+// x_b = (Kt_b Diag(gam_a)) S.  They need only the operands read one pair
+// ahead, so the wave issues them before waiting for this pair's other reads.
+template <typename E, int D, int NB>
+__device__ __forceinline__ void pair_x(const POps<E, D>& c, const f32x4 (&S)[NB][D / 16],
+                                       bf16x8 (&sb)[NB][PBlk<E, D>::NSLOT], f32x4 (&xa)[NB],
+                                       f32x4 (&xb)[NB]) {
+    using P = PBlk<E, D>;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        xa[nb] = zero4();
+        xb[nb] = zero4();
+#pragma unroll
+        for (int s = 0; s < P::NSLOT; ++s) {
+            sb[nb][s] = pack8(S[nb][2 * s], S[nb][2 * s + 1]);
+            xa[nb] = mma_bf16_k32(c.ka[s], sb[nb][s], xa[nb]);
+            xb[nb] = mma_bf16_k32(c.kb[s], sb[nb][s], xb[nb]);
+        }
+    }
+}
+
+// The rest of a pair (bf16) after pair_x: U_a, U_b, the state update, then
+// the outputs from the packed old state.
+template <typename E, int D, int NB>
+__device__ __forceinline__ void pair_rest(const POps<E, D>& c, f32x4 (&S)[NB][D / 16],
+                                          const bf16x8 (&sb)[NB][PBlk<E, D>::NSLOT],
+                                          const f32x4 (&xa)[NB], const f32x4 (&xb)[NB],
+                                          const f32x4 (&Va)[NB], const f32x4 (&Vb)[NB],
+                                          f32x4 (&Oa)[NB], f32x4 (&Ob)[NB]) {
+    using P = PBlk<E, D>;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        // every 16x16x16 product below starts from a zero accumulator: an
+        // MFMA of one shape must not take as srcC the in-flight result of
+        // an MFMA of another shape (16x16x32 -> 16x16x16 chains read stale
+        // srcC on gfx950)
+        const bf16x4 ua = pack4(mma_bf16_k16(c.tma, pack4(Va[nb] - xa[nb]), zero4()));
+        const f32x4 xbc = mma_bf16_k16(c.mkb, ua, zero4());
+        const bf16x4 ub = pack4(mma_bf16_k16(c.tmb, pack4(Vb[nb] - xb[nb] - xbc), zero4()));
+        const bf16x8 u2 = cat8(ua, ub);
+        static_for<0, P::MT>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            S[nb][m] = mma_bf16_k32(c.kd2[m], u2, S[nb][m] * gab_tile<m>(c.gv));
+        });
+        f32x4 oa = zero4(), ob = zero4();
+#pragma unroll
+        for (int s = 0; s < P::NSLOT; ++s) {
+            oa = mma_bf16_k32(c.qa[s], sb[nb][s], oa);
+            ob = mma_bf16_k32(c.qb[s], sb[nb][s], ob);
+        }
+        Oa[nb] = oa + mma_bf16_k16(c.aqa, ua, zero4());
+        Ob[nb] = ob + mma_bf16_k32(c.ob2, u2, zero4());
+    }
 }
 
 // One pair of the state chain for NB 16-column blocks of S.  Va, Vb: V of
@@ -526,9 +593,10 @@ __device__ __forceinline__ void pair_step(const POps<E, D>& c, f32x4 (&S)[NB][D 
             const f32x4 xbc = mma_bf16_k16(c.mkb, ua, zero4());
             const bf16x4 ub = pack4(mma_bf16_k16(c.tmb, pack4(Vb[nb] - xb - xbc), zero4()));
             const bf16x8 u2 = cat8(ua, ub);
-#pragma unroll
-            for (int m = 0; m < P::MT; ++m)
-                S[nb][m] = mma_bf16_k32(c.kd2[m], u2, S[nb][m] * c.gab[m]);
+            static_for<0, P::MT>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                S[nb][m] = mma_bf16_k32(c.kd2[m], u2, S[nb][m] * gab_tile<m>(c.gv));
+            });
             f32x4 oa = zero4(), ob = zero4();
 #pragma unroll
             for (int s = 0; s < P::NSLOT; ++s) {
@@ -566,16 +634,16 @@ __device__ __forceinline__ void pair_step(const POps<E, D>& c, f32x4 (&S)[NB][D 
             }
             Oa[nb] = oa;
             Ob[nb] = ob;
-#pragma unroll
-            for (int m = 0; m < P::MT; ++m) {
-                f32x4 sm = S[nb][m] * c.gab[m];
+            static_for<0, P::MT>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                f32x4 sm = S[nb][m] * gab_tile<m>(c.gv);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     sm = mma_f32_k4(c.kd2[m][p], ua[p], sm);
                     sm = mma_f32_k4(c.kd2[m][4 + p], ub[p], sm);
                 }
                 S[nb][m] = sm;
-            }
+            });
         }
     }
 }
@@ -695,18 +763,49 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
                 for (int e = 0; e < 4; ++e) vd[(4 * c + e) * Cfg::VSTR + r] = vbuf[i][e];
             }
         };
+        // outputs of pair q, left by the chains in its entry's V area (same
+        // word-major layout), to o: 16 bytes per lane-piece; rows past T are
+        // outside the buffer and dropped
+        auto flush = [&](int q) {
+            const uint32_t* vd = reinterpret_cast<const uint32_t*>(ring + (q % NPAIR) * ENT + P::BYTES);
+            const int t0 = (n_first + 2 * q) * kChunk;
+            const int Lr = min(2 * kChunk, T - t0);
+            const size_t rs = (size_t)H * D;
+            const size_t row0 = ((size_t)b * T + t0) * H + h;
+            const Rsrc ro = make_rsrc(o + row0 * D + tile0,
+                                      Lr > 0 ? (uint32_t)(((size_t)(Lr - 1) * rs + NCOL) * ES) : 0u);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int q2 = i * kWave + lane, r = q2 / RP, c = q2 % RP;
+                u32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = vd[(4 * c + e) * Cfg::VSTR + r];
+                buf_store_u32x4(ro, (int)((r * rs + c * EPP) * ES), x);
+            }
+        };
+        auto wait_released = [&](int q) {   // every chain has released pair q
+#pragma unroll
+            for (int c = 0; c < NCW; ++c) spin_until_ge(&done[q % NPAIR][c], q);
+        };
         if (L < NP) issue(L);
         for (int p = L; p < NP; p += NL) {
             const int e = p % NPAIR;
-            if (p >= NPAIR) {   // every chain has released the entry's previous pair
-#pragma unroll
-                for (int c = 0; c < NCW; ++c) spin_until_ge(&done[e][c], p - NPAIR);
+            if (p >= NPAIR) {   // the entry's previous pair: released, outputs out
+                wait_released(p - NPAIR);
+                flush(p - NPAIR);
             }
             write(p);
             // publish: the data stores complete before the flag store
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             __hip_atomic_store(&ready[e], p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (p + NL < NP) issue(p + NL);
+        }
+        // the last pairs' entries are not rewritten: the loader that would
+        // have written pair q + NPAIR writes pair q's outputs out
+        for (int q = NP - NPAIR > 0 ? NP - NPAIR : 0; q < NP; ++q) {
+            if ((q + NPAIR) % NL != L) continue;
+            wait_released(q);
+            flush(q);
         }
         return;
     }
@@ -739,6 +838,28 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
             V[nb] = __builtin_bit_cast(f32x4, x);
         }
     };
+    // outputs of a pair into its entry's V area, over the V words of this
+    // chain's own columns (read before, by this wave: LDS keeps its order),
+    // in the same word-major layout; a loader writes them to o
+    auto o_put = [&](const char* ent, const f32x4 (&Oa)[NB], const f32x4 (&Ob)[NB]) {
+        char* base = const_cast<char*>(ent) + P::BYTES;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int vcol = 16 * (NB * w + nb) + j;   // column within the tile
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int ra = 4 * g + p, rb = kChunk + 4 * g + p;
+                if constexpr (ES == 2) {
+                    char* at = base + (vcol & 1) * 2;
+                    *reinterpret_cast<bf16*>(at + ((vcol >> 1) * Cfg::VSTR + ra) * 4) = from_f32<E>(Oa[nb][p]);
+                    *reinterpret_cast<bf16*>(at + ((vcol >> 1) * Cfg::VSTR + rb) * 4) = from_f32<E>(Ob[nb][p]);
+                } else {
+                    *reinterpret_cast<float*>(base + (vcol * Cfg::VSTR + ra) * 4) = Oa[nb][p];
+                    *reinterpret_cast<float*>(base + (vcol * Cfg::VSTR + rb) * 4) = Ob[nb][p];
+                }
+            }
+        }
+    };
     f32x4 S[NB][D / 16];
     state_load<D, NB>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
     POps<E, D> c;
@@ -759,27 +880,38 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
         }
         f32x4 Va[NB], Vb[NB], Oa[NB], Ob[NB];
         u32x4 ra[NB], rb[NB];
-        // LDS reads in the order of first use (the wait counter is in order)
+        // LDS reads in the order of first use (the wait counter is in order
+        // and counts at most 15: a value is usable only once all but 15 of
+        // the reads issued after it are done, so the reads come in batches)
         v_read(ent, 0, ra);
         v_read(ent, 1, rb);
         pops_load_chain<E, D>(c, ent);
-        pops_load_out<E, D>(c, ent);
-        // all reads are issued here, ahead of the chain (the scheduler would
-        // otherwise sink each to its use and expose its latency); the fp32
-        // operands would not fit the registers at once
-        if constexpr (ES == 2) pin_issued();
-        v_widen2(ra, Va);
-        v_widen2(rb, Vb);
-        pair_step<E, D, NB>(c, S, Va, Vb, Oa, Ob);
-        // release pair s: its reads were all issued above
+        if constexpr (ES == 2) {
+            // batch 1 (chain operands) issued; x_a, x_b need only operands
+            // read a pair ahead; then batch 2 (output operands)
+            pin_issued();
+            bf16x8 sb[NB][P::NSLOT];
+            f32x4 xa[NB], xb[NB];
+            pair_x<E, D, NB>(c, S, sb, xa, xb);
+            pin_issued();
+            pops_load_out<E, D>(c, ent);
+            pin_issued();
+            v_widen2(ra, Va);
+            v_widen2(rb, Vb);
+            pair_rest<E, D, NB>(c, S, sb, xa, xb, Va, Vb, Oa, Ob);
+        } else {
+            pops_load_out<E, D>(c, ent);
+            v_widen2(ra, Va);
+            v_widen2(rb, Vb);
+            pair_step<E, D, NB>(c, S, Va, Vb, Oa, Ob);
+        }
+        o_put(ent, Oa, Ob);
+        // release pair s: its reads and output writes were all issued above
         asm volatile("" ::: "memory");
         __hip_atomic_store(&done[s % NPAIR][w], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         fl = __hip_atomic_load(&ready[(s + 1) % NPAIR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         asm volatile("" ::: "memory");
         pops_load_k<E, D>(c, entry(s + 1));   // (past the last pair: stale, unused)
-        const int n0 = n_first + 2 * s;
-        o_store<E, D, NB>(Oa, o, chunk_pos<D>(b, h, n0, T, H), col0);
-        o_store<E, D, NB>(Ob, o, chunk_pos<D>(b, h, n0 + 1, T, H), col0);
     }
     if (ST) state_store<D, NB>(S, ST + (size_t)u * D * D, col0);
 }
