@@ -10,8 +10,10 @@ resident in HBM before timing; a 1 GiB write between steps evicts them from
 the 256 MB Infinity Cache so each step reads HBM (the write is outside the
 per-step event pair).  Prints ONE JSON line with the prefill tokens/s as
 ``value``, a ``roofline`` object for the prefill pass, the fp64 CPU oracle
-timed on the host (``cpu_baseline``), and a ``decode`` object with the decode
-steps/s of the B=256 workload (1,000 back-to-back in-place steps).
+timed on the host (``cpu_baseline``), a ``decode`` object with the decode
+steps/s of the B=256 workload (1,000 back-to-back in-place steps), and a
+``verify`` object with the multi-token step (T drafted tokens per sequence
+from the B=256 live state into a separate state buffer) per second.
 """
 from __future__ import annotations
 
@@ -46,6 +48,12 @@ def prefill_alg_flops(B, T, H, d):
     return total * B * H
 
 
+def verify_alg_bytes(B, H, d, T, es=2):
+    """S read + S_out written (fp32) once, and per token q, k, v, z, o in the
+    input dtype and beta fp32."""
+    return B * H * (2 * d * d * 4 + T * (5 * d * es + 4))
+
+
 def decode_alg_bytes(B, H, d, es=2):
     """S read + write (fp32) + q, k, v, z, o (es) + beta per (b, h)."""
     return B * H * (2 * d * d * 4 + 5 * d * es + 4)
@@ -73,6 +81,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--verify-tokens", type=int, default=4,
+                    help="drafted tokens per sequence in the verify-step measurement (1..16)")
     ap.add_argument("--workload", choices=["mid", "batched"], default="mid",
                     help="prefill workload: mid = B1 H32 T4096 (the headline), "
                          "batched = B8 H32 T32768 with a carried state")
@@ -91,7 +101,7 @@ def main():
     import linear_attention_recurrence_05_amd as kda
     from linear_attention_recurrence_05_amd.inputs import (DECODE_CONFIG, PREFILL_CONFIGS,
                                                             config_inputs, decode_state,
-                                                            decode_step_inputs)
+                                                            decode_step_inputs, prefill_inputs)
 
     dev = torch.device("cuda:0")
     kda.lib()
@@ -212,6 +222,44 @@ def main():
                          "kernel": "decode_kernel", "alg_bytes_per_step": db},
         }
         del stg, S, S_save
+
+        # multi-token verify step: T drafted tokens per sequence from the live
+        # state, the state after them to a separate buffer (the snapshot stays)
+        T_v = args.verify_tokens
+        gen, A, S = decode_state(c.B, c.H, c.dk, c.dv, seed=c.seed, s0_std=c.s0_std, device=dev)
+        xv = prefill_inputs(c.B, T_v, c.H, c.dk, c.dv, c.dtype, seed=c.seed + 1, device=dev)
+        ov = torch.empty(c.B, T_v, c.H, c.dv, dtype=c.dtype, device=dev)
+        S_out = torch.empty_like(S)
+
+        def run_verify():
+            kda.kda_decode_tokens(xv["q"], xv["k"], xv["v"], xv["z"], xv["beta"], A, -5.0, S,
+                                  S_out, ov, stream)
+
+        run_verify()
+        reps = []
+        for _ in range(5):
+            flush.zero_()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_verify()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1))
+        vms = sorted(reps)[2]
+        vb = verify_alg_bytes(c.B, c.H, c.dk, T_v)
+        vgbs = vb / (vms * 1e-3) / 1e9
+        line["verify"] = {
+            "metric": "KDA multi-token verify steps/s (T drafted tokens per sequence per step)",
+            "value": 1e3 / vms, "unit": "steps/s", "ms_per_step": vms, "tokens_per_step": T_v,
+            "repetitions": 5,
+            "config": {"workload": f"verify_B{c.B}_H{c.H}_T{T_v}_d{c.dk}_bf16_state_fp32",
+                       "B": c.B, "H": c.H, "T": T_v, "d_k": c.dk, "d_v": c.dv},
+            "roofline": {"bound": "hbm", "achieved": vgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": vgbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "tokens_kernel", "alg_bytes_per_step": vb},
+        }
+        del S, S_out, xv
 
     if not args.no_cpu_baseline and args.workload == "mid":
         import oracle

@@ -64,6 +64,9 @@ extern "C" {
 /* Tokens per chunk of the chunkwise prefill (the pages' 16-token tiles). */
 #define KDA_CHUNK 16
 
+/* Largest token count of one kda_decode_tokens call. */
+#define KDA_MAX_DECODE_TOKENS 16
+
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL            */
@@ -129,6 +132,28 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const void *z, const float *beta, const float *A,
                            float g_min, float *S, void *o, int B, int H,
                            int d_k, int d_v, kda_dtype dt, void *stream);
+
+/* T consecutive decode steps (1 <= T <= KDA_MAX_DECODE_TOKENS) of every
+ * sequence from a live state, for checking T drafted tokens at once: the same
+ * recurrence as kda_decode_step applied to tokens t = 0 .. T-1 (dev.to page,
+ * "The Sequence Bottleneck": the gated delta rule; the podcast page,
+ * "Evidence Confidence by Component", names a speculative-decoding use of
+ * KDA without describing it -- this is the plain multi-token step it needs).
+ *   q, k, v, z, o : [B, T, H, d] like kda_chunk_prefill; beta [B, T, H].
+ *   S             : [B, H, d_k, d_v] fp32 state before token 0 (read only).
+ *   S_out         : receives the state after token T-1.  S_out == S commits
+ *                   in place; a separate buffer leaves S as the snapshot to
+ *                   replay the accepted prefix from (call again with the
+ *                   accepted count as T).  Partial overlap of S_out and S,
+ *                   and any overlap of o or S_out with another argument, is
+ *                   KDA_ERR_ALIASING.
+ * S is read and S_out written once per call, whatever T.  Returns
+ * KDA_ERR_INVALID_SHAPE for T outside [1, KDA_MAX_DECODE_TOKENS]. */
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
+                             const void *z, const float *beta, const float *A,
+                             float g_min, const float *S, float *S_out, void *o,
+                             int B, int T, int H, int d_k, int d_v, kda_dtype dt,
+                             void *stream);
 
 /* Diagnostic export of the gate stage: G [B, T, H, d_k] fp32 receives the
  * chunk-local inclusive cumulative log-decay

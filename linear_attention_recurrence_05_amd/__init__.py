@@ -10,21 +10,24 @@ Functions named like the C entry points take torch tensors in the layouts
 
     kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace, stream)
     kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream)
+    kda_decode_tokens(q, k, v, z, beta, A, g_min, S, S_out, o, stream)
     kda_gate_chunk_cumsum(z, A, g_min, G, stream)
     kda_intra_chunk(q, k, z, beta, A, g_min, Tm, Aqk, gamma, stream)
     kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype)
 
-``chunk_prefill`` and ``decode_step`` additionally allocate the outputs (and
+``chunk_prefill``, ``decode_step`` and ``decode_tokens`` additionally allocate the outputs (and
 the workspace) with ``torch.empty`` before calling the same entry points.
 """
 from __future__ import annotations
 
-from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KdaError, KdaLibraryMissing, abi_version,
-                   chunk_prefill, decode_step, kda_chunk_prefill,
-                   kda_chunk_prefill_workspace_bytes, kda_decode_step, kda_gate_chunk_cumsum,
-                   kda_intra_chunk, lib, library_path, status_string)
+from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KDA_MAX_DECODE_TOKENS, KdaError,
+                   KdaLibraryMissing, abi_version, chunk_prefill, decode_step, decode_tokens,
+                   kda_chunk_prefill, kda_chunk_prefill_workspace_bytes, kda_decode_step,
+                   kda_decode_tokens, kda_gate_chunk_cumsum, kda_intra_chunk, lib, library_path,
+                   status_string)
 
-__all__ = ["KDA_BF16", "KDA_CHUNK", "KDA_F32", "KdaError", "KdaLibraryMissing", "abi_version",
-           "chunk_prefill", "decode_step", "kda_chunk_prefill",
-           "kda_chunk_prefill_workspace_bytes", "kda_decode_step", "kda_gate_chunk_cumsum",
-           "kda_intra_chunk", "lib", "library_path", "status_string"]
+__all__ = ["KDA_BF16", "KDA_CHUNK", "KDA_F32", "KDA_MAX_DECODE_TOKENS", "KdaError",
+           "KdaLibraryMissing", "abi_version", "chunk_prefill", "decode_step", "decode_tokens",
+           "kda_chunk_prefill", "kda_chunk_prefill_workspace_bytes", "kda_decode_step",
+           "kda_decode_tokens", "kda_gate_chunk_cumsum", "kda_intra_chunk", "lib",
+           "library_path", "status_string"]

@@ -11,6 +11,7 @@ from .build import library_path
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_CHUNK = 16
+KDA_MAX_DECODE_TOKENS = 16
 
 _STATUS = ["KDA_OK", "KDA_ERR_NULL_POINTER", "KDA_ERR_INVALID_SHAPE", "KDA_ERR_INVALID_VALUE",
            "KDA_ERR_UNSUPPORTED", "KDA_ERR_MISALIGNED", "KDA_ERR_WORKSPACE_TOO_SMALL",
@@ -40,6 +41,8 @@ _SIGNATURES = {
     "kda_chunk_prefill": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6
                           + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "kda_decode_step": ([_vp] * 6 + [ctypes.c_float, _vp, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
+    "kda_decode_tokens": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6 + [_vp],
+                          ctypes.c_int),
     "kda_gate_chunk_cumsum": ([_vp, _vp, ctypes.c_float, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
     "kda_intra_chunk": ([_vp] * 5 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 5 + [_vp],
                         ctypes.c_int),
@@ -128,6 +131,18 @@ def kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream=None):
     _check(st, "kda_decode_step")
 
 
+def kda_decode_tokens(q, k, v, z, beta, A, g_min, S, S_out, o, stream=None):
+    """C entry point kda_decode_tokens on torch tensors: T = q.shape[1] steps from
+    the state S; the state after them goes to S_out (which may be S)."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S=S, S_out=S_out, o=o)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    st = lib().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                 float(g_min), _ptr(S), _ptr(S_out), _ptr(o), B, T, H, dk, dv,
+                                 _dtype_code(q), _stream(stream))
+    _check(st, "kda_decode_tokens")
+
+
 def kda_gate_chunk_cumsum(z, A, g_min, G, stream=None):
     _require_contiguous(z=z, A=A, G=G)
     B, T, H, dk = z.shape
@@ -159,6 +174,17 @@ def chunk_prefill(q, k, v, z, beta, A, g_min=-5.0, S0=None, want_state=True, str
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, ws, stream)
     return o, S_T
+
+
+def decode_tokens(q, k, v, z, beta, A, S, S_out=None, g_min=-5.0, stream=None):
+    """Allocate o (and S_out unless given) and run kda_decode_tokens.
+    Returns (o, S_out)."""
+    B, T, H, dk = q.shape
+    o = torch.empty((B, T, H, v.shape[-1]), dtype=q.dtype, device=q.device)
+    if S_out is None:
+        S_out = torch.empty_like(S)
+    kda_decode_tokens(q, k, v, z, beta, A, g_min, S, S_out, o, stream)
+    return o, S_out
 
 
 def decode_step(q, k, v, z, beta, A, S, g_min=-5.0, stream=None):

@@ -169,6 +169,36 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     return hip_status(kda::launch_decode(a, (hipStream_t)stream), "kda_decode_step launch");
 }
 
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* z,
+                             const float* beta, const float* A, float g_min, const float* S,
+                             float* S_out, void* o, int B, int T, int H, int d_k, int d_v,
+                             kda_dtype dt, void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    if (T < 1 || T > KDA_MAX_DECODE_TOKENS)
+        return fail(KDA_ERR_INVALID_SHAPE, "T=%d outside [1, %d]", T, KDA_MAX_DECODE_TOKENS);
+    size_t nel, ntok;
+    if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t sbytes = (size_t)B * H * d_k * d_v * sizeof(float);
+    const Range r[] = {{"q", q, nel * es, 16},     {"k", k, nel * es, 16},
+                       {"v", v, nel * es, 16},     {"z", z, nel * es, 16},
+                       {"beta", beta, ntok * 4, 4}, {"A", A, (size_t)H * 4, 4},
+                       {"S", S, sbytes, 16},       {"S_out", S_out, sbytes, 16},
+                       {"o", o, nel * es, 16}};
+    const bool req[] = {true, true, true, true, true, true, true, true, true};
+    if ((s = check_ptrs(r, 9, req)) != KDA_OK) return s;
+    // S_out may be S itself (commit in place) but may not overlap it partly;
+    // o and S_out may not overlap anything else
+    for (int out : {7, 8})
+        for (int i = 0; i < 9; ++i) {
+            if (i == out || (out == 7 && i == 6 && S_out == S)) continue;
+            if (overlap(r[out], r[i])) return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
+        }
+    kda::TokensArgs a{q, k, v, z, beta, A, g_min, S, S_out, o, B, T, H, d_k, dt == KDA_BF16};
+    return hip_status(kda::launch_tokens(a, (hipStream_t)stream), "kda_decode_tokens launch");
+}
+
 kda_status kda_gate_chunk_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,
                                  int H, int d_k, kda_dtype dt, void* stream) {
     kda_status s = check_common(d_k, d_k, dt, g_min);

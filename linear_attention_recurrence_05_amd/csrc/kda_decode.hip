@@ -109,6 +109,114 @@ __global__ __launch_bounds__(2 * D) void decode_kernel(
     }
 }
 
+// T consecutive tokens of one sequence per (b, h) from the state S_in; the
+// state after the last token goes to S_out (which may be S_in: commit in
+// place; or another buffer: S_in stays as the snapshot a rejected draft is
+// replayed from).  Same layout and per-token arithmetic as decode_kernel,
+// with S kept in registers across the tokens: S is read and written once
+// for all T tokens.  Three workgroup barriers per token.
+template <typename E, int D>
+__global__ __launch_bounds__(2 * D) void tokens_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
+    float g_min, const float* S_in, float* S_out, E* __restrict__ o, int T, int H) {
+    constexpr int NT = 2 * D;
+    constexpr int CG = D / 4;
+    constexpr int RG = NT / CG;
+    constexpr int RPT = D / RG;
+    constexpr int NWAVE = NT / kWave;
+    static_assert(RG == 8, "layout assumes 8 row groups");
+
+    __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
+    __shared__ float s_red[NWAVE][CG][9];
+
+    const int tid = threadIdx.x;
+    const size_t unit = blockIdx.x;    // b * H + h
+    const size_t b = unit / (size_t)H;
+    const int h = (int)(unit % (size_t)H);
+    const GateConsts gc = make_gate(A[h], g_min);
+    const int cg = tid % CG, rg = tid / CG;
+    const int wave = tid / kWave, lane = tid % kWave;
+
+    const f32x4* Si = reinterpret_cast<const f32x4*>(S_in + unit * (size_t)D * D);
+    f32x4* So = reinterpret_cast<f32x4*>(S_out + unit * (size_t)D * D);
+    f32x4 st[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&Si[(rg + RG * i) * CG + cg]);
+
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = (b * (size_t)T + t) * (size_t)H + h;   // (b, t, h)
+        const size_t vec = tok * (size_t)D;
+        if (t > 0) __syncthreads();   // every thread is done with the previous token's vectors
+        if (tid < D) {
+            s_alpha[tid] = gate_alpha(gc, gate_sigmoid(gc, to_f32(z[vec + tid])));
+            s_k[tid] = to_f32(k[vec + tid]);
+            s_q[tid] = to_f32(q[vec + tid]);
+            s_v[tid] = to_f32(v[vec + tid]);
+        }
+        __syncthreads();
+        float red[9];
+#pragma unroll
+        for (int x = 0; x < 9; ++x) red[x] = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int c = rg + RG * i;
+            const float a = s_alpha[c], kc = s_k[c], qc = s_q[c];
+            st[i] *= a;                                  // S' = Diag(a) S
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                red[x] += kc * st[i][x];                 // p = S'^T k
+                red[4 + x] += qc * st[i][x];             // r = S'^T q
+            }
+            red[8] += qc * kc;                           // q . k
+        }
+#pragma unroll
+        for (int off = CG; off < kWave; off <<= 1)
+#pragma unroll
+            for (int x = 0; x < 9; ++x) red[x] += __shfl_xor(red[x], off);
+        if (lane < CG) {
+#pragma unroll
+            for (int x = 0; x < 9; ++x) s_red[wave][lane][x] = red[x];
+        }
+        __syncthreads();
+        float tot[9];
+#pragma unroll
+        for (int x = 0; x < 9; ++x) {
+            tot[x] = s_red[0][cg][x];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) tot[x] += s_red[w][cg][x];
+        }
+        const float bt = beta[tok];
+        f32x4 e;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) e[x] = bt * (s_v[4 * cg + x] - tot[x]);
+        if (rg == 0) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) o[vec + 4 * cg + x] = from_f32<E>(tot[4 + x] + tot[8] * e[x]);
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) st[i] += s_k[rg + RG * i] * e;   // S = S' + k e^T
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(st[i], &So[(rg + RG * i) * CG + cg]);
+}
+
+template <typename E, int D>
+static hipError_t launch_tokens_t(const TokensArgs& a, hipStream_t stream) {
+    const size_t units = (size_t)a.B * a.H;
+    hipLaunchKernelGGL((tokens_kernel<E, D>), dim3((unsigned)units), dim3(2 * D), 0, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.z, a.beta, a.A,
+                       a.g_min, a.S, a.S_out, (E*)a.o, a.T, a.H);
+    return hipGetLastError();
+}
+
+hipError_t launch_tokens(const TokensArgs& a, hipStream_t stream) {
+    if (a.is_bf16) {
+        return a.d == 128 ? launch_tokens_t<bf16, 128>(a, stream) : launch_tokens_t<bf16, 32>(a, stream);
+    }
+    return a.d == 128 ? launch_tokens_t<float, 128>(a, stream) : launch_tokens_t<float, 32>(a, stream);
+}
+
 template <typename E, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const size_t units = (size_t)a.B * a.H;

@@ -18,6 +18,17 @@ struct DecodeArgs {
     bool is_bf16;
 };
 
+struct TokensArgs {
+    const void *q, *k, *v, *z;
+    const float *beta, *A;
+    float g_min;
+    const float* S;
+    float* S_out;
+    void* o;
+    int B, T, H, d;
+    bool is_bf16;
+};
+
 struct PrefillArgs {
     const void *q, *k, *v, *z;
     const float *beta, *A;
@@ -57,6 +68,7 @@ size_t pair_block_bytes(int d, bool is_bf16);
 bool pair_variant_ok(int d, bool is_bf16, int ncol, int nb);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_tokens(const TokensArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
 // Split plan: pair intra kernel -> workspace -> pair inter kernel, per segment.
 hipError_t launch_split(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);

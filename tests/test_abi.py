@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["kda_abi_version", "kda_status_string", "kda_last_error",
               "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_decode_step",
-              "kda_gate_chunk_cumsum", "kda_intra_chunk"]:
+              "kda_decode_tokens", "kda_gate_chunk_cumsum", "kda_intra_chunk"]:
         assert n in names
 
 
@@ -143,6 +143,38 @@ def test_workspace_query():
 def test_decode_rejects(over, code):
     st, detail = decode(**over)
     assert st == E[code], (st, detail)
+
+
+def tokens(**over):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), z=fake(3), beta=fake(4), A=fake(5),
+                g_min=-5.0, S=fake(6), S_out=fake(7), o=fake(8), B=4, T=4, H=2, d_k=128,
+                d_v=128, dt=kda.KDA_BF16, stream=None)
+    args.update(over)
+    L = kda.lib()
+    st = L.kda_decode_tokens(args["q"], args["k"], args["v"], args["z"], args["beta"], args["A"],
+                             args["g_min"], args["S"], args["S_out"], args["o"], args["B"],
+                             args["T"], args["H"], args["d_k"], args["d_v"], args["dt"],
+                             args["stream"])
+    return st, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(T=0), "KDA_ERR_INVALID_SHAPE"),
+    (dict(T=17), "KDA_ERR_INVALID_SHAPE"),
+    (dict(S=None), "KDA_ERR_NULL_POINTER"),
+    (dict(S_out=None), "KDA_ERR_NULL_POINTER"),
+    (dict(o=None), "KDA_ERR_NULL_POINTER"),
+    (dict(g_min=-6.0), "KDA_ERR_INVALID_VALUE"),
+    (dict(d_k=64, d_v=64), "KDA_ERR_UNSUPPORTED"),
+    (dict(S_out=fake(6, misalign=16)), "KDA_ERR_ALIASING"),   # partial overlap with S
+    (dict(o=fake(6)), "KDA_ERR_ALIASING"),                     # o over S
+    (dict(S_out=fake(1)), "KDA_ERR_ALIASING"),                 # S_out over k
+    (dict(S=fake(6, misalign=8)), "KDA_ERR_MISALIGNED"),
+])
+def test_tokens_rejects(over, code):
+    st, detail = tokens(**over)
+    assert st == E[code], (st, detail)
+    assert detail
 
 
 def test_gate_and_intra_reject():
