@@ -13,7 +13,9 @@ per-step event pair).  Prints ONE JSON line with the prefill tokens/s as
 timed on the host (``cpu_baseline``), a ``decode`` object with the decode
 steps/s of the B=256 workload (1,000 back-to-back in-place steps), and a
 ``verify`` object with the multi-token step (T drafted tokens per sequence
-from the B=256 live state into a separate state buffer) per second.
+from the B=256 live state into a separate state buffer) per second, and a
+``decode_paged`` object with the decode step on states addressed through a
+slot table into a pool.
 """
 from __future__ import annotations
 
@@ -222,6 +224,43 @@ def main():
                          "kernel": "decode_kernel", "alg_bytes_per_step": db},
         }
         del stg, S, S_save
+
+        # the same decode with the states in a pool of 2 B slots, addressed by
+        # a shuffled slot table (the serving layout)
+        n_slots = 2 * c.B
+        gen, A, _ = decode_state(1, c.H, c.dk, c.dv, seed=c.seed, s0_std=c.s0_std, device=dev)
+        pool = torch.randn(n_slots, c.H, c.dk, c.dv, device=dev) * float(c.s0_std)
+        slots = torch.randperm(n_slots, device=dev)[:c.B].to(torch.int32)
+        n_p = 200
+        stg = decode_step_inputs(gen, c.B, c.H, c.dk, c.dv, c.dtype, dev, steps=n_p)
+
+        def run_paged():
+            for i in range(n_p):
+                kda.kda_decode_step_paged(stg["q"][i], stg["k"][i], stg["v"][i], stg["z"][i],
+                                          stg["beta"][i], A, -5.0, pool, slots, od, stream)
+
+        run_paged()
+        reps = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_paged()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1))
+        pms = sorted(reps)[1] / n_p
+        pgbs = db / (pms * 1e-3) / 1e9
+        line["decode_paged"] = {
+            "metric": "KDA decode steps/s, states in a slot-addressed pool", "value": 1e3 / pms,
+            "unit": "steps/s", "ms_per_step": pms, "steps": n_p, "repetitions": 3,
+            "config": {"workload": f"decode_paged_B{c.B}_H{c.H}_d{c.dk}_bf16_pool{n_slots}",
+                       "B": c.B, "H": c.H, "d_k": c.dk, "d_v": c.dv, "n_slots": n_slots},
+            "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": pgbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "decode_kernel (paged)", "alg_bytes_per_step": db},
+        }
+        del stg, pool
 
         # multi-token verify step: T drafted tokens per sequence from the live
         # state, the state after them to a separate buffer (the snapshot stays)

@@ -155,6 +155,48 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
                              int B, int T, int H, int d_k, int d_v, kda_dtype dt,
                              void *stream);
 
+/* Paged states (a serving engine's layout: dev.to page, "Infrastructure and
+ * Training/Inference Mechanics", fixed-size KDA states held apart from the
+ * attention cache).  The states live in a pool [n_slots, H, d_k, d_v] fp32,
+ * and sequence b uses the pool row named by an int32 slot table [B] in
+ * device memory; the calls below are the dense calls with S0 / S_T / S
+ * replaced by pool rows.  Slot values are read by the kernels only: a
+ * sequence whose slot lies outside [0, n_slots) is skipped (none of its
+ * outputs and no pool row are written).  Two sequences writing one slot in
+ * the same call race; a sequence may read and write the same slot.  The pool
+ * may not overlap any other argument, nor o; the slot tables may coincide.
+ * Returns KDA_ERR_INVALID_SHAPE for n_slots < 1. */
+
+/* kda_chunk_prefill from pool row slots_in[b] (NULL: zero initial states)
+ * into pool row slots_out[b] (NULL: no state written).  Workspace as for
+ * kda_chunk_prefill (the same size query). */
+kda_status kda_chunk_prefill_paged(const void *q, const void *k, const void *v,
+                                   const void *z, const float *beta,
+                                   const float *A, float g_min, float *pool,
+                                   int n_slots, const int *slots_in,
+                                   const int *slots_out, void *o, int B,
+                                   int T, int H, int d_k, int d_v,
+                                   kda_dtype dt, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* kda_decode_step on pool row slots[b], in place. */
+kda_status kda_decode_step_paged(const void *q, const void *k, const void *v,
+                                 const void *z, const float *beta,
+                                 const float *A, float g_min, float *pool,
+                                 int n_slots, const int *slots, void *o, int B,
+                                 int H, int d_k, int d_v, kda_dtype dt,
+                                 void *stream);
+
+/* kda_decode_tokens from pool row slots_in[b] into pool row slots_out[b]
+ * (the same row commits in place; another keeps the snapshot). */
+kda_status kda_decode_tokens_paged(const void *q, const void *k, const void *v,
+                                   const void *z, const float *beta,
+                                   const float *A, float g_min, float *pool,
+                                   int n_slots, const int *slots_in,
+                                   const int *slots_out, void *o, int B,
+                                   int T, int H, int d_k, int d_v,
+                                   kda_dtype dt, void *stream);
+
 /* Diagnostic export of the gate stage: G [B, T, H, d_k] fp32 receives the
  * chunk-local inclusive cumulative log-decay
  *   G_t = sum of g_s over s from the start of t's KDA_CHUNK-token chunk to t,

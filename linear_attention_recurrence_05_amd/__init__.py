@@ -11,6 +11,10 @@ Functions named like the C entry points take torch tensors in the layouts
     kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace, stream)
     kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream)
     kda_decode_tokens(q, k, v, z, beta, A, g_min, S, S_out, o, stream)
+    kda_chunk_prefill_paged(q, k, v, z, beta, A, g_min, pool, slots_in, slots_out, o,
+                            workspace, stream)
+    kda_decode_step_paged(q, k, v, z, beta, A, g_min, pool, slots, o, stream)
+    kda_decode_tokens_paged(q, k, v, z, beta, A, g_min, pool, slots_in, slots_out, o, stream)
     kda_gate_chunk_cumsum(z, A, g_min, G, stream)
     kda_intra_chunk(q, k, z, beta, A, g_min, Tm, Aqk, gamma, stream)
     kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype)
@@ -22,12 +26,14 @@ from __future__ import annotations
 
 from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KDA_MAX_DECODE_TOKENS, KdaError,
                    KdaLibraryMissing, abi_version, chunk_prefill, decode_step, decode_tokens,
-                   kda_chunk_prefill, kda_chunk_prefill_workspace_bytes, kda_decode_step,
-                   kda_decode_tokens, kda_gate_chunk_cumsum, kda_intra_chunk, lib, library_path,
-                   status_string)
+                   kda_chunk_prefill, kda_chunk_prefill_paged, kda_chunk_prefill_workspace_bytes,
+                   kda_decode_step, kda_decode_step_paged, kda_decode_tokens,
+                   kda_decode_tokens_paged, kda_gate_chunk_cumsum, kda_intra_chunk, lib,
+                   library_path, status_string)
 
 __all__ = ["KDA_BF16", "KDA_CHUNK", "KDA_F32", "KDA_MAX_DECODE_TOKENS", "KdaError",
            "KdaLibraryMissing", "abi_version", "chunk_prefill", "decode_step", "decode_tokens",
-           "kda_chunk_prefill", "kda_chunk_prefill_workspace_bytes", "kda_decode_step",
-           "kda_decode_tokens", "kda_gate_chunk_cumsum", "kda_intra_chunk", "lib",
+           "kda_chunk_prefill", "kda_chunk_prefill_paged", "kda_chunk_prefill_workspace_bytes",
+           "kda_decode_step", "kda_decode_step_paged", "kda_decode_tokens",
+           "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk", "lib",
            "library_path", "status_string"]

@@ -43,6 +43,12 @@ _SIGNATURES = {
     "kda_decode_step": ([_vp] * 6 + [ctypes.c_float, _vp, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
     "kda_decode_tokens": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6 + [_vp],
                           ctypes.c_int),
+    "kda_chunk_prefill_paged": ([_vp] * 6 + [ctypes.c_float, _vp, _i, _vp, _vp, _vp] + [_i] * 6
+                                + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "kda_decode_step_paged": ([_vp] * 6 + [ctypes.c_float, _vp, _i, _vp, _vp] + [_i] * 5 + [_vp],
+                              ctypes.c_int),
+    "kda_decode_tokens_paged": ([_vp] * 6 + [ctypes.c_float, _vp, _i, _vp, _vp, _vp] + [_i] * 6
+                                + [_vp], ctypes.c_int),
     "kda_gate_chunk_cumsum": ([_vp, _vp, ctypes.c_float, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
     "kda_intra_chunk": ([_vp] * 5 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 5 + [_vp],
                         ctypes.c_int),
@@ -141,6 +147,58 @@ def kda_decode_tokens(q, k, v, z, beta, A, g_min, S, S_out, o, stream=None):
                                  float(g_min), _ptr(S), _ptr(S_out), _ptr(o), B, T, H, dk, dv,
                                  _dtype_code(q), _stream(stream))
     _check(st, "kda_decode_tokens")
+
+
+def _slots(t, B):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.numel() != B:
+        raise ValueError("a slot table is an int32 tensor of B entries")
+    return t
+
+
+def kda_chunk_prefill_paged(q, k, v, z, beta, A, g_min, pool, slots_in, slots_out, o,
+                            workspace=None, stream=None):
+    """C entry point kda_chunk_prefill_paged: states from pool[slots_in[b]] into
+    pool[slots_out[b]] (either table may be None)."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, pool=pool, slots_in=slots_in,
+                        slots_out=slots_out, o=o)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kda_chunk_prefill_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                       float(g_min), _ptr(pool), pool.shape[0],
+                                       _ptr(_slots(slots_in, B)), _ptr(_slots(slots_out, B)),
+                                       _ptr(o), B, T, H, dk, dv, _dtype_code(q), _ptr(workspace),
+                                       ws_bytes, _stream(stream))
+    _check(st, "kda_chunk_prefill_paged")
+
+
+def kda_decode_step_paged(q, k, v, z, beta, A, g_min, pool, slots, o, stream=None):
+    """C entry point kda_decode_step_paged: pool[slots[b]] updated in place."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, pool=pool, slots=slots, o=o)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    st = lib().kda_decode_step_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                     float(g_min), _ptr(pool), pool.shape[0],
+                                     _ptr(_slots(slots, B)), _ptr(o), B, H, dk, dv,
+                                     _dtype_code(q), _stream(stream))
+    _check(st, "kda_decode_step_paged")
+
+
+def kda_decode_tokens_paged(q, k, v, z, beta, A, g_min, pool, slots_in, slots_out, o,
+                            stream=None):
+    """C entry point kda_decode_tokens_paged: T steps from pool[slots_in[b]] into
+    pool[slots_out[b]]."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, pool=pool, slots_in=slots_in,
+                        slots_out=slots_out, o=o)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    st = lib().kda_decode_tokens_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                       float(g_min), _ptr(pool), pool.shape[0],
+                                       _ptr(_slots(slots_in, B)), _ptr(_slots(slots_out, B)),
+                                       _ptr(o), B, T, H, dk, dv, _dtype_code(q), _stream(stream))
+    _check(st, "kda_decode_tokens_paged")
 
 
 def kda_gate_chunk_cumsum(z, A, g_min, G, stream=None):

@@ -84,6 +84,44 @@ kda_status check_shape(int B, int T, int H, int d, size_t& n_tok_el, size_t& n_t
     return KDA_OK;
 }
 
+// Checks shared by the paged entry points: the pool, the slot tables and the
+// tensors of a [B, T, H, d] call; o and the pool may overlap nothing else.
+// Slot values live on the device and are not read here: a sequence whose
+// slot lies outside [0, n_slots) is skipped by the kernels.
+kda_status check_paged(const void* q, const void* k, const void* v, const void* z,
+                       const float* beta, const float* A, const float* pool, int n_slots,
+                       const int* slots_in, bool in_required, const int* slots_out,
+                       bool out_required, const void* o, int B, int T, int H, int d,
+                       kda_dtype dt, const void* ws, size_t ws_need) {
+    size_t nel, ntok;
+    kda_status s = check_shape(B, T, H, d, nel, ntok);
+    if (s != KDA_OK) return s;
+    if (n_slots < 1) return fail(KDA_ERR_INVALID_SHAPE, "n_slots=%d must be >= 1", n_slots);
+    if ((long long)n_slots * H > (1LL << 26))
+        return fail(KDA_ERR_INVALID_SHAPE, "n_slots*H = %lld is too large", (long long)n_slots * H);
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const Range r[] = {{"q", q, nel * es, 16},      {"k", k, nel * es, 16},
+                       {"v", v, nel * es, 16},      {"z", z, nel * es, 16},
+                       {"beta", beta, ntok * 4, 4}, {"A", A, (size_t)H * 4, 4},
+                       {"slots_in", slots_in, (size_t)B * 4, 4},
+                       {"slots_out", slots_out, (size_t)B * 4, 4},
+                       {"pool", pool, (size_t)n_slots * H * d * d * sizeof(float), 16},
+                       {"o", o, nel * es, 16},      {"workspace", ws, ws_need, 16}};
+    const bool req[] = {true, true, true, true, true, true, in_required, out_required, true, true,
+                        ws_need > 0};
+    if ((s = check_ptrs(r, 11, req)) != KDA_OK) return s;
+    for (int out : {8, 9, 10})
+        for (int i = 0; i < 11; ++i)
+            if (i != out && overlap(r[out], r[i]))
+                return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
+    return KDA_OK;
+}
+
+kda::StateIO paged_state(float* pool, int n_slots, const int* slots_in, const int* slots_out) {
+    return kda::StateIO{slots_in ? pool : nullptr, slots_in, slots_out ? pool : nullptr, slots_out,
+                        slots_in, slots_out, n_slots};
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,7 +181,8 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                 return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
         }
     }
-    kda::PrefillArgs a{q, k, v, z, beta, A, g_min, S0, o, S_T, B, T, H, d_k, dt == KDA_BF16};
+    kda::PrefillArgs a{q, k, v, z, beta, A, g_min, kda::dense_state(S0, S_T), o, B, T, H, d_k,
+                       dt == KDA_BF16};
     return hip_status(kda::launch_prefill(a, plan, workspace, (hipStream_t)stream), "kda_chunk_prefill launch");
 }
 
@@ -165,7 +204,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
         for (int i = 0; i < 8; ++i)
             if (i != out && overlap(r[out], r[i]))
                 return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
-    kda::DecodeArgs a{q, k, v, z, beta, A, g_min, S, o, B, H, d_k, dt == KDA_BF16};
+    kda::DecodeArgs a{q, k, v, z, beta, A, g_min, kda::dense_state(S, S), o, B, H, d_k, dt == KDA_BF16};
     return hip_status(kda::launch_decode(a, (hipStream_t)stream), "kda_decode_step launch");
 }
 
@@ -195,8 +234,62 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const 
             if (i == out || (out == 7 && i == 6 && S_out == S)) continue;
             if (overlap(r[out], r[i])) return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
         }
-    kda::TokensArgs a{q, k, v, z, beta, A, g_min, S, S_out, o, B, T, H, d_k, dt == KDA_BF16};
+    kda::TokensArgs a{q, k, v, z, beta, A, g_min, kda::dense_state(S, S_out), o, B, T, H, d_k,
+                      dt == KDA_BF16};
     return hip_status(kda::launch_tokens(a, (hipStream_t)stream), "kda_decode_tokens launch");
+}
+
+kda_status kda_chunk_prefill_paged(const void* q, const void* k, const void* v, const void* z,
+                                   const float* beta, const float* A, float g_min, float* pool,
+                                   int n_slots, const int* slots_in, const int* slots_out, void* o,
+                                   int B, int T, int H, int d_k, int d_v, kda_dtype dt,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    size_t nel, ntok;
+    if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
+    const kda::PlanInfo plan = kda::choose_plan(B, T, H, d_k, dt == KDA_BF16);
+    if ((s = check_paged(q, k, v, z, beta, A, pool, n_slots, slots_in, false, slots_out, false, o, B,
+                         T, H, d_k, dt, workspace, plan.ws_bytes)) != KDA_OK)
+        return s;
+    if (workspace_bytes < plan.ws_bytes)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    plan.ws_bytes);
+    kda::PrefillArgs a{q, k, v, z, beta, A, g_min, paged_state(pool, n_slots, slots_in, slots_out), o,
+                       B, T, H, d_k, dt == KDA_BF16};
+    return hip_status(kda::launch_prefill(a, plan, workspace, (hipStream_t)stream),
+                      "kda_chunk_prefill_paged launch");
+}
+
+kda_status kda_decode_step_paged(const void* q, const void* k, const void* v, const void* z,
+                                 const float* beta, const float* A, float g_min, float* pool,
+                                 int n_slots, const int* slots, void* o, int B, int H, int d_k,
+                                 int d_v, kda_dtype dt, void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    if ((s = check_paged(q, k, v, z, beta, A, pool, n_slots, slots, true, slots, true, o, B, 1, H, d_k,
+                         dt, nullptr, 0)) != KDA_OK)
+        return s;
+    kda::DecodeArgs a{q, k, v, z, beta, A, g_min, paged_state(pool, n_slots, slots, slots), o, B, H,
+                      d_k, dt == KDA_BF16};
+    return hip_status(kda::launch_decode(a, (hipStream_t)stream), "kda_decode_step_paged launch");
+}
+
+kda_status kda_decode_tokens_paged(const void* q, const void* k, const void* v, const void* z,
+                                   const float* beta, const float* A, float g_min, float* pool,
+                                   int n_slots, const int* slots_in, const int* slots_out, void* o,
+                                   int B, int T, int H, int d_k, int d_v, kda_dtype dt,
+                                   void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    if (T < 1 || T > KDA_MAX_DECODE_TOKENS)
+        return fail(KDA_ERR_INVALID_SHAPE, "T=%d outside [1, %d]", T, KDA_MAX_DECODE_TOKENS);
+    if ((s = check_paged(q, k, v, z, beta, A, pool, n_slots, slots_in, true, slots_out, true, o, B, T,
+                         H, d_k, dt, nullptr, 0)) != KDA_OK)
+        return s;
+    kda::TokensArgs a{q, k, v, z, beta, A, g_min, paged_state(pool, n_slots, slots_in, slots_out), o,
+                      B, T, H, d_k, dt == KDA_BF16};
+    return hip_status(kda::launch_tokens(a, (hipStream_t)stream), "kda_decode_tokens_paged launch");
 }
 
 kda_status kda_gate_chunk_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,

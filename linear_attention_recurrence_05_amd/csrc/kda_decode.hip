@@ -26,7 +26,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(2 * D) void decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
-    float g_min, float* __restrict__ S, E* __restrict__ o, int H) {
+    float g_min, StateIO io, E* __restrict__ o, int H) {
     constexpr int NT = 2 * D;          // threads
     constexpr int CG = D / 4;          // column groups of 4 (float4)
     constexpr int RG = NT / CG;        // row groups (= 8)
@@ -39,8 +39,9 @@ __global__ __launch_bounds__(2 * D) void decode_kernel(
 
     const int tid = threadIdx.x;
     const size_t unit = blockIdx.x;    // b * H + h
-    const int h = (int)(unit % (size_t)H);
+    const int bi = (int)(unit / (size_t)H), h = (int)(unit % (size_t)H);
     const size_t vec = unit * (size_t)D;
+    if (io.skip(bi)) return;           // uniform over the workgroup
 
     if (tid < D) {
         GateConsts gc = make_gate(A[h], g_min);
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(2 * D) void decode_kernel(
     __syncthreads();
 
     const int cg = tid % CG, rg = tid / CG;
-    f32x4* Sv = reinterpret_cast<f32x4*>(S + unit * (size_t)D * D);
+    f32x4* Sv = reinterpret_cast<f32x4*>(io.out_at(bi, h, H, D));   // in place: in == out
     f32x4 st[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&Sv[(rg + RG * i) * CG + cg]);
@@ -109,17 +110,17 @@ __global__ __launch_bounds__(2 * D) void decode_kernel(
     }
 }
 
-// T consecutive tokens of one sequence per (b, h) from the state S_in; the
-// state after the last token goes to S_out (which may be S_in: commit in
-// place; or another buffer: S_in stays as the snapshot a rejected draft is
-// replayed from).  Same layout and per-token arithmetic as decode_kernel,
+// T consecutive tokens of one sequence per (b, h) from the state io.in; the
+// state after the last token goes to io.out (which may be the same state:
+// commit in place; or another one: the input stays as the snapshot a
+// rejected draft is replayed from).  Same layout and per-token arithmetic as decode_kernel,
 // with S kept in registers across the tokens: S is read and written once
 // for all T tokens.  Three workgroup barriers per token.
 template <typename E, int D>
 __global__ __launch_bounds__(2 * D) void tokens_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
-    float g_min, const float* S_in, float* S_out, E* __restrict__ o, int T, int H) {
+    float g_min, StateIO io, E* __restrict__ o, int T, int H) {
     constexpr int NT = 2 * D;
     constexpr int CG = D / 4;
     constexpr int RG = NT / CG;
@@ -134,12 +135,13 @@ __global__ __launch_bounds__(2 * D) void tokens_kernel(
     const size_t unit = blockIdx.x;    // b * H + h
     const size_t b = unit / (size_t)H;
     const int h = (int)(unit % (size_t)H);
+    if (io.skip((int)b)) return;       // uniform over the workgroup
     const GateConsts gc = make_gate(A[h], g_min);
     const int cg = tid % CG, rg = tid / CG;
     const int wave = tid / kWave, lane = tid % kWave;
 
-    const f32x4* Si = reinterpret_cast<const f32x4*>(S_in + unit * (size_t)D * D);
-    f32x4* So = reinterpret_cast<f32x4*>(S_out + unit * (size_t)D * D);
+    const f32x4* Si = reinterpret_cast<const f32x4*>(io.in_at((int)b, h, H, D));
+    f32x4* So = reinterpret_cast<f32x4*>(io.out_at((int)b, h, H, D));
     f32x4 st[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&Si[(rg + RG * i) * CG + cg]);
@@ -206,7 +208,7 @@ static hipError_t launch_tokens_t(const TokensArgs& a, hipStream_t stream) {
     const size_t units = (size_t)a.B * a.H;
     hipLaunchKernelGGL((tokens_kernel<E, D>), dim3((unsigned)units), dim3(2 * D), 0, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.z, a.beta, a.A,
-                       a.g_min, a.S, a.S_out, (E*)a.o, a.T, a.H);
+                       a.g_min, a.S, (E*)a.o, a.T, a.H);
     return hipGetLastError();
 }
 

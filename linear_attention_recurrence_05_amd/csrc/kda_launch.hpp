@@ -8,11 +8,46 @@
 
 namespace kda {
 
+// The states a launch reads and writes, for unit (b, h) of d x d fp32:
+//   in  + (row_in(b) * H + h) * d * d,   out + (row_out(b) * H + h) * d * d,
+// with row(b) = b when the slot table is null (dense [B, H, d, d]) and
+// slot[b] otherwise (a pool of n_slots states).  A null in means zeros, a
+// null out means no state written.  The caller's own slot tables (ck_in,
+// ck_out) decide which sequences run: one whose slot lies outside
+// [0, n_slots) is skipped -- no output row and no state is written for it.
+// (A launch in the middle of a segmented prefill reads and writes a carry
+// whose table differs from the caller's, hence the separate check tables.)
+struct StateIO {
+    const float* in;
+    const int* in_slot;
+    float* out;
+    const int* out_slot;
+    const int* ck_in;
+    const int* ck_out;
+    int n_slots;
+
+    __device__ bool skip(int b) const {
+        return (ck_in && (unsigned)ck_in[b] >= (unsigned)n_slots) ||
+               (ck_out && (unsigned)ck_out[b] >= (unsigned)n_slots);
+    }
+    __device__ const float* in_at(int b, int h, int H, int d) const {
+        return in ? in + ((size_t)(in_slot ? in_slot[b] : b) * H + h) * (size_t)d * d : nullptr;
+    }
+    __device__ float* out_at(int b, int h, int H, int d) const {
+        return out ? out + ((size_t)(out_slot ? out_slot[b] : b) * H + h) * (size_t)d * d : nullptr;
+    }
+};
+
+// Dense states (no slot tables).
+inline StateIO dense_state(const float* in, float* out) {
+    return StateIO{in, nullptr, out, nullptr, nullptr, nullptr, 0};
+}
+
 struct DecodeArgs {
     const void *q, *k, *v, *z;
     const float *beta, *A;
     float g_min;
-    float* S;
+    StateIO S;          // read and written in place (in == out)
     void* o;
     int B, H, d;
     bool is_bf16;
@@ -22,8 +57,7 @@ struct TokensArgs {
     const void *q, *k, *v, *z;
     const float *beta, *A;
     float g_min;
-    const float* S;
-    float* S_out;
+    StateIO S;          // the state before the tokens (in), after them (out)
     void* o;
     int B, T, H, d;
     bool is_bf16;
@@ -33,9 +67,8 @@ struct PrefillArgs {
     const void *q, *k, *v, *z;
     const float *beta, *A;
     float g_min;
-    const float* S0;
+    StateIO S;          // S0 (in, may be null) and S_T (out, may be null)
     void* o;
-    float* S_T;
     int B, T, H, d;
     bool is_bf16;
 };

@@ -693,8 +693,8 @@ struct PairCfg {
 
 template <typename E, int D, int NCW, int NB>
 __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_kernel(
-    const char* __restrict__ ws, const E* __restrict__ v, const float* S0, E* __restrict__ o,
-    float* ST, int B, int T, int H, int n_first, int n_count, int nct) {
+    const char* __restrict__ ws, const E* __restrict__ v, StateIO io, E* __restrict__ o,
+    int B, int T, int H, int n_first, int n_count, int nct) {
     using P = PBlk<E, D>;
     using Cfg = PairCfg<E, D, NCW, NB>;
     constexpr int NPAIR = Cfg::NPAIR, NL = Cfg::NL, ENT = Cfg::ENT, ES = Cfg::ES;
@@ -709,6 +709,7 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
     int u, ct;
     if (!map_unit(nct, B * H, u, ct)) return;   // uniform over the workgroup
     const int b = u / H, h = u % H;
+    if (io.skip(b)) return;                      // uniform over the workgroup
     const int w = wave_id();
     const int lane = lane_id();
     const int tile0 = ct * NCOL;
@@ -861,7 +862,7 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
         }
     };
     f32x4 S[NB][D / 16];
-    state_load<D, NB>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
+    state_load<D, NB>(S, io.in_at(b, h, H, D), col0);
     POps<E, D> c;
     // The loop body is one basic block (a branch inside it keeps the
     // scheduler from overlapping a step's tail with what follows): the next
@@ -913,7 +914,7 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
         asm volatile("" ::: "memory");
         pops_load_k<E, D>(c, entry(s + 1));   // (past the last pair: stale, unused)
     }
-    if (ST) state_store<D, NB>(S, ST + (size_t)u * D * D, col0);
+    if (io.out) state_store<D, NB>(S, io.out_at(b, h, H, D), col0);
 }
 
 // ------------------------------------------------------------ launch
@@ -936,14 +937,14 @@ bool pair_variant_ok(int d, bool is_bf16, int ncol, int nb) {
 static unsigned pair_grid(int units, int nct) { return (unsigned)(((units + 7) / 8) * 8 * nct); }
 
 template <typename E, int D, int NCW, int NB>
-static hipError_t launch_pair_inter_v(const char* ws, const E* v, const float* s_in, E* o,
-                                      float* s_out, const PrefillArgs& a, int n_first,
-                                      int n_count, hipStream_t stream) {
+static hipError_t launch_pair_inter_v(const char* ws, const E* v, const StateIO& io, E* o,
+                                      const PrefillArgs& a, int n_first, int n_count,
+                                      hipStream_t stream) {
     using Cfg = PairCfg<E, D, NCW, NB>;
     const int nct = D / Cfg::NCOL;
     hipLaunchKernelGGL((pair_inter_kernel<E, D, NCW, NB>), dim3(pair_grid(a.B * a.H, nct)),
-                       dim3(Cfg::THREADS), 0, stream, ws, v, s_in, o, s_out, a.B, a.T, a.H,
-                       n_first, n_count, nct);
+                       dim3(Cfg::THREADS), 0, stream, ws, v, io, o, a.B, a.T, a.H, n_first,
+                       n_count, nct);
     return hipGetLastError();
 }
 
@@ -956,7 +957,10 @@ static hipError_t launch_split_t(const PrefillArgs& a, const PlanInfo& p, void* 
     const int seg = NC < kSegChunks ? NC : kSegChunks;
     const int NPmax = (seg + 1) / 2;
     char* fws = (char*)ws;
-    float* carry = a.S_T;
+    // the state between segments: the caller's output state (its rows or
+    // slots), else a dense buffer after the pair blocks in the workspace
+    float* carry = a.S.out;
+    const int* carry_slot = a.S.out_slot;
     if (NC > seg && !carry) carry = (float*)(fws + (size_t)units * NPmax * P::BYTES);
     const E* v = (const E*)a.v;
     E* o = (E*)a.o;
@@ -968,11 +972,18 @@ static hipError_t launch_split_t(const PrefillArgs& a, const PlanInfo& p, void* 
                            a.g_min, fws, a.B, a.T, a.H, n_first, NP);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const float* s_in = n_first == 0 ? a.S0 : carry;
-        const bool last = n_first + n_count >= NC;
-        float* s_out = last ? a.S_T : carry;
+        const bool first = n_first == 0, last = n_first + n_count >= NC;
+        StateIO io = a.S;
+        if (!first) {
+            io.in = carry;
+            io.in_slot = carry_slot;
+        }
+        if (!last) {
+            io.out = carry;
+            io.out_slot = carry_slot;
+        }
 #define KDA_PAIR_INTER(NCW, NB) \
-    e = launch_pair_inter_v<E, D, NCW, NB>(fws, v, s_in, o, s_out, a, n_first, n_count, stream)
+    e = launch_pair_inter_v<E, D, NCW, NB>(fws, v, io, o, a, n_first, n_count, stream)
         if constexpr (D == 128 && sizeof(E) == 2) {
             if (p.nb == 2 && p.ncol == 64) KDA_PAIR_INTER(2, 2);
             else if (p.nb == 2) KDA_PAIR_INTER(1, 2);

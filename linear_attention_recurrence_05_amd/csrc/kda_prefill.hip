@@ -118,7 +118,7 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
                                                     const E* __restrict__ v, const E* __restrict__ z,
                                                     const float* __restrict__ beta,
                                                     const float* __restrict__ A, float g_min,
-                                                    const float* S0, E* __restrict__ o, float* ST,
+                                                    StateIO io, E* __restrict__ o,
                                                     int B, int T, int H, int nct) {
     using Bk = Blk<E, D>;
     using Cfg = FusedCfg<E, D>;
@@ -127,6 +127,7 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
     int u, ct;
     if (!map_unit(nct, B * H, u, ct)) return;   // uniform over the workgroup
     const int b = u / H, h = u % H;
+    if (io.skip(b)) return;                      // uniform over the workgroup
     const int w = wave_id();
     const int NC = (T + kChunk - 1) / kChunk;
     const int NM = (NC + NPROD - 1) / NPROD;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
     f32x4 S[NB][D / 16];
     constexpr int ES = (int)sizeof(E);
     u32x4 Vc[NPROD][NB], Vn[NPROD][NB];
-    state_load<D, NB>(S, S0 ? S0 + (size_t)u * D * D : nullptr, col0);
+    state_load<D, NB>(S, io.in_at(b, h, H, D), col0);
 #pragma unroll
     for (int cc = 0; cc < NPROD; ++cc)
         if (cc < NC) v_load<D, NB>(Vc[cc], v, ES, chunk_pos<D>(b, h, cc, T, H), col0);
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
             for (int nb = 0; nb < NB; ++nb) Vc[cc][nb] = Vn[cc][nb];
         wg_barrier();
     }
-    if (ST) state_store<D, NB>(S, ST + (size_t)u * D * D, col0);
+    if (io.out) state_store<D, NB>(S, io.out_at(b, h, H, D), col0);
 }
 
 // --------------------------------------------------------------- plans / launchers
@@ -285,16 +286,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PlanInfo& p, void
         const dim3 grid(grid_units(units, nct)), block(512);
         if (p.ncol == 128 && D == 128)
             hipLaunchKernelGGL((fused_kernel<E, D, 2, 4>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S0, o, a.S_T, a.B, a.T, a.H, nct);
+                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
         else if (p.ncol == 64 && D == 128)
             hipLaunchKernelGGL((fused_kernel<E, D, 1, 4>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S0, o, a.S_T, a.B, a.T, a.H, nct);
+                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
         else if (p.ncol == 32)
             hipLaunchKernelGGL((fused_kernel<E, D, 1, 2>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S0, o, a.S_T, a.B, a.T, a.H, nct);
+                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
         else
             hipLaunchKernelGGL((fused_kernel<E, D, 1, 1>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S0, o, a.S_T, a.B, a.T, a.H, nct);
+                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
         return hipGetLastError();
     }
     (void)ws;

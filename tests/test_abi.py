@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["kda_abi_version", "kda_status_string", "kda_last_error",
               "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_decode_step",
-              "kda_decode_tokens", "kda_gate_chunk_cumsum", "kda_intra_chunk"]:
+              "kda_decode_tokens", "kda_chunk_prefill_paged", "kda_decode_step_paged",
+              "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk"]:
         assert n in names
 
 
@@ -175,6 +176,61 @@ def test_tokens_rejects(over, code):
     st, detail = tokens(**over)
     assert st == E[code], (st, detail)
     assert detail
+
+
+def paged_decode(**over):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), z=fake(3), beta=fake(4), A=fake(5), g_min=-5.0,
+                pool=fake(6), n_slots=8, slots=fake(7), o=fake(8), B=4, H=2, d_k=128, d_v=128,
+                dt=kda.KDA_BF16, stream=None)
+    args.update(over)
+    L = kda.lib()
+    st = L.kda_decode_step_paged(args["q"], args["k"], args["v"], args["z"], args["beta"], args["A"],
+                                 args["g_min"], args["pool"], args["n_slots"], args["slots"],
+                                 args["o"], args["B"], args["H"], args["d_k"], args["d_v"],
+                                 args["dt"], args["stream"])
+    return st, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_slots=0), "KDA_ERR_INVALID_SHAPE"),
+    (dict(pool=None), "KDA_ERR_NULL_POINTER"),
+    (dict(slots=None), "KDA_ERR_NULL_POINTER"),
+    (dict(slots=fake(7, misalign=2)), "KDA_ERR_MISALIGNED"),
+    (dict(o=fake(6)), "KDA_ERR_ALIASING"),          # o over the pool
+    (dict(slots=fake(6)), "KDA_ERR_ALIASING"),      # slot table inside the pool
+    (dict(d_k=32, d_v=128), "KDA_ERR_UNSUPPORTED"),
+])
+def test_paged_decode_rejects(over, code):
+    st, detail = paged_decode(**over)
+    assert st == E[code], (st, detail)
+    assert detail
+
+
+def test_paged_prefill_and_tokens_reject():
+    L = kda.lib()
+    # prefill: the split plan's workspace is checked like the dense call's
+    os.environ["KDA_PREFILL_PLAN"] = "split"
+    try:
+        st = L.kda_chunk_prefill_paged(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), -5.0,
+                                       fake(6), 4, fake(7), fake(7), fake(8), 1, 64, 2, 32, 32,
+                                       kda.KDA_F32, None, 0, None)
+        assert st == E["KDA_ERR_NULL_POINTER"]
+        need = kda.kda_chunk_prefill_workspace_bytes(1, 64, 2, 32, 32, kda.KDA_F32)
+        st = L.kda_chunk_prefill_paged(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), -5.0,
+                                       fake(6), 4, None, None, fake(8), 1, 64, 2, 32, 32,
+                                       kda.KDA_F32, fake(9), need - 1, None)
+        assert st == E["KDA_ERR_WORKSPACE_TOO_SMALL"]
+    finally:
+        del os.environ["KDA_PREFILL_PLAN"]
+    # tokens: both tables required, T bounded
+    st = L.kda_decode_tokens_paged(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), -5.0,
+                                   fake(6), 4, fake(7), None, fake(8), 2, 3, 2, 32, 32,
+                                   kda.KDA_F32, None)
+    assert st == E["KDA_ERR_NULL_POINTER"]
+    st = L.kda_decode_tokens_paged(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), -5.0,
+                                   fake(6), 4, fake(7), fake(7), fake(8), 2, 17, 2, 32, 32,
+                                   kda.KDA_F32, None)
+    assert st == E["KDA_ERR_INVALID_SHAPE"]
 
 
 def test_gate_and_intra_reject():
