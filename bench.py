@@ -231,7 +231,7 @@ def main():
         gen, A, _ = decode_state(1, c.H, c.dk, c.dv, seed=c.seed, s0_std=c.s0_std, device=dev)
         pool = torch.randn(n_slots, c.H, c.dk, c.dv, device=dev) * float(c.s0_std)
         slots = torch.randperm(n_slots, device=dev)[:c.B].to(torch.int32)
-        n_p = 200
+        n_p = min(200, n)
         stg = decode_step_inputs(gen, c.B, c.H, c.dk, c.dv, c.dtype, dev, steps=n_p)
 
         def run_paged():
@@ -257,7 +257,9 @@ def main():
             "config": {"workload": f"decode_paged_B{c.B}_H{c.H}_d{c.dk}_bf16_pool{n_slots}",
                        "B": c.B, "H": c.H, "d_k": c.dk, "d_v": c.dv, "n_slots": n_slots},
             "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": pgbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": pgbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_B256_H32_d128_bf16_step_bytes"),
+                         "traffic_unit": "bytes per step (the same kernel as dense decode)",
                          "kernel": "decode_kernel (paged)", "alg_bytes_per_step": db},
         }
         del stg, pool
@@ -295,7 +297,10 @@ def main():
             "config": {"workload": f"verify_B{c.B}_H{c.H}_T{T_v}_d{c.dk}_bf16_state_fp32",
                        "B": c.B, "H": c.H, "T": T_v, "d_k": c.dk, "d_v": c.dv},
             "roofline": {"bound": "hbm", "achieved": vgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": vgbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": vgbs / HBM_PEAK_GBS,
+                         "traffic": (measured_traffic(f"verify_B{c.B}_H{c.H}_T{T_v}_d{c.dk}_bf16_step_bytes")
+                                     if T_v == 4 else None),
+                         "traffic_unit": "bytes per step",
                          "kernel": "tokens_kernel", "alg_bytes_per_step": vb},
         }
         del S, S_out, xv
