@@ -96,6 +96,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
+// lds + 16 l (lds wave-uniform), without VGPRs.  Completion is counted like a
+// load's (in order with the wave's other loads); past the buffer's end the
+// bytes are zero.
+__device__ __forceinline__ void buf_load_lds16(Rsrc r, int off, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+// Wait until every buffer load this wave issued has completed (vmcnt = 0;
+// expcnt and lgkmcnt left at their maximum, i.e. not waited for).
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 template <typename T> __device__ __forceinline__ T buf_load(Rsrc r, int off);
 template <> __device__ __forceinline__ uint32_t buf_load<uint32_t>(Rsrc r, int off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
@@ -114,6 +125,9 @@ __device__ __forceinline__ void buf_store_u16(Rsrc r, int off, unsigned short x)
 }
 __device__ __forceinline__ void buf_store_u32x4(Rsrc r, int off, u32x4 x) {
     __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u32x2(Rsrc r, int off, u32x2 x) {
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
 }
 __device__ __forceinline__ void buf_store_u32(Rsrc r, int off, uint32_t x) {
     __builtin_amdgcn_raw_buffer_store_b32(x, r, off, 0, 0);
@@ -194,6 +208,35 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
     r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
     r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
     return r;
+}
+
+// 32-bit word of lane (this lane xor X) of the quad, X = 1 or 2.
+template <int X>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t x) {
+    static_assert(X == 1 || X == 2, "quad xor");
+    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, ctrl, 0xF, 0xF, false);
+}
+
+// Rows of an accumulator tile as bf16, in registers.  Lane (j, g) holds
+// column j, rows 4g .. 4g+3 of a 16x16 fp32 tile; on return lane
+// (4a + q, g) holds row 4g + q, columns 4a .. 4a+3, as four bf16 (8 bytes,
+// column order).  A 4x4 transpose inside each quad of lanes: 16-bit halves
+// across lane pairs (xor 1), then 32-bit words across pair pairs (xor 2).
+__device__ __forceinline__ u32x2 acc_rows_bf16(f32x4 x) {
+    const int q = (int)(threadIdx.x & 3);
+    const uint32_t w0 = __builtin_bit_cast(uint32_t, pack2(x[0], x[1]));   // rows 0, 1 of this column
+    const uint32_t w1 = __builtin_bit_cast(uint32_t, pack2(x[2], x[3]));   // rows 2, 3
+    // lanes (2c, 2c+1): the even lane keeps the low halves (rows 0 and 2) of
+    // both columns, the odd lane the high halves (rows 1 and 3)
+    const uint32_t sel = (q & 1) ? 0x03020706u : 0x05040100u;
+    const uint32_t a0 = __builtin_amdgcn_perm(quad_xor<1>(w0), w0, sel);
+    const uint32_t a1 = __builtin_amdgcn_perm(quad_xor<1>(w1), w1, sel);
+    // now lane q holds row (q & 1) in a0 and row (q & 1) + 2 in a1, for
+    // columns 2 (q >> 1) and 2 (q >> 1) + 1; lanes q and q ^ 2 swap one word
+    const bool hi = (q & 2) != 0;
+    const uint32_t r = quad_xor<2>(hi ? a0 : a1);
+    return hi ? u32x2{r, a1} : u32x2{a0, r};
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }

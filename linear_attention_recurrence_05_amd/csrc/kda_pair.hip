@@ -473,14 +473,21 @@ __device__ __forceinline__ void pops_load_k(POps<E, D>& c, const char* blk) {
     }
 }
 
-// Operands of the state chain, in the order it uses them.
+// Operands of U_a, U_b.
 template <typename E, int D>
-__device__ __forceinline__ void pops_load_chain(POps<E, D>& c, const char* blk) {
+__device__ __forceinline__ void pops_load_u(POps<E, D>& c, const char* blk) {
     using P = PBlk<E, D>;
-    const int lane = lane_id(), g = lane >> 4, r = lane & 15;
+    const int lane = lane_id();
     c.tma = *reinterpret_cast<const V4<E>*>(blk + P::TMA + lane * P::OPB);
     c.mkb = *reinterpret_cast<const V4<E>*>(blk + P::MKB + lane * P::OPB);
     c.tmb = *reinterpret_cast<const V4<E>*>(blk + P::TMB + lane * P::OPB);
+}
+
+// Operands of the state update.
+template <typename E, int D>
+__device__ __forceinline__ void pops_load_supd(POps<E, D>& c, const char* blk) {
+    using P = PBlk<E, D>;
+    const int lane = lane_id(), g = lane >> 4, r = lane & 15;
     {
         const int mm = min(r >> 1, P::MT - 1);   // lanes past the last tile read a valid word
         c.gv = *reinterpret_cast<const f32x2*>(blk + P::GAB + (16 * mm + 4 * g + 2 * (r & 1)) * 4);
@@ -489,6 +496,13 @@ __device__ __forceinline__ void pops_load_chain(POps<E, D>& c, const char* blk) 
     for (int m = 0; m < P::MT; ++m) {
         c.kd2[m] = *reinterpret_cast<const V8<E>*>(blk + P::kd2_offset(m, g, r));
     }
+}
+
+// Operands of the state chain (U and the state update), in the order it uses them.
+template <typename E, int D>
+__device__ __forceinline__ void pops_load_chain(POps<E, D>& c, const char* blk) {
+    pops_load_u<E, D>(c, blk);
+    pops_load_supd<E, D>(c, blk);
 }
 
 // Operands of the outputs only (used after the state update).
@@ -531,6 +545,44 @@ __device__ __forceinline__ void pair_x(const POps<E, D>& c, const f32x4 (&S)[NB]
     }
 }
 
+// [U_a; U_b] of a pair (bf16) from x_a, x_b and V (accumulator layout), as
+// the B operand of the K = 32 products.  Every 16x16x16 product starts from a
+// zero accumulator: an MFMA of one shape must not take as srcC the in-flight
+// result of an MFMA of another shape (16x16x32 -> 16x16x16 chains read stale
+// srcC on gfx950).
+template <typename E, int D>
+__device__ __forceinline__ bf16x8 pair_u(const POps<E, D>& c, const f32x4& xa, const f32x4& xb,
+                                         const f32x4& Va, const f32x4& Vb) {
+    const bf16x4 ua = pack4(mma_bf16_k16(c.tma, pack4(Va - xa), zero4()));
+    const f32x4 xbc = mma_bf16_k16(c.mkb, ua, zero4());
+    const bf16x4 ub = pack4(mma_bf16_k16(c.tmb, pack4(Vb - xb - xbc), zero4()));
+    return cat8(ua, ub);
+}
+
+// S <- Diag(gam_a gam_b) S + [Kd_a Diag(gam_b); Kd_b]^T [U_a; U_b] (bf16).
+template <typename E, int D>
+__device__ __forceinline__ void pair_supdate(const POps<E, D>& c, f32x4 (&S)[D / 16], const bf16x8& u2) {
+    static_for<0, PBlk<E, D>::MT>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        S[m] = mma_bf16_k32(c.kd2[m], u2, S[m] * gab_tile<m>(c.gv));
+    });
+}
+
+// Outputs of a pair (bf16) from the packed state at its start and [U_a; U_b].
+template <typename E, int D>
+__device__ __forceinline__ void pair_out(const POps<E, D>& c, const bf16x8 (&sb)[PBlk<E, D>::NSLOT],
+                                         const bf16x8& u2, f32x4& Oa, f32x4& Ob) {
+    f32x4 oa = zero4(), ob = zero4();
+#pragma unroll
+    for (int s = 0; s < PBlk<E, D>::NSLOT; ++s) {
+        oa = mma_bf16_k32(c.qa[s], sb[s], oa);
+        ob = mma_bf16_k32(c.qb[s], sb[s], ob);
+    }
+    const bf16x4 ua = bf16x4{u2[0], u2[1], u2[2], u2[3]};
+    Oa = oa + mma_bf16_k16(c.aqa, ua, zero4());
+    Ob = ob + mma_bf16_k32(c.ob2, u2, zero4());
+}
+
 // The rest of a pair (bf16) after pair_x: U_a, U_b, the state update, then
 // the outputs from the packed old state.
 template <typename E, int D, int NB>
@@ -539,29 +591,11 @@ __device__ __forceinline__ void pair_rest(const POps<E, D>& c, f32x4 (&S)[NB][D 
                                           const f32x4 (&xa)[NB], const f32x4 (&xb)[NB],
                                           const f32x4 (&Va)[NB], const f32x4 (&Vb)[NB],
                                           f32x4 (&Oa)[NB], f32x4 (&Ob)[NB]) {
-    using P = PBlk<E, D>;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        // every 16x16x16 product below starts from a zero accumulator: an
-        // MFMA of one shape must not take as srcC the in-flight result of
-        // an MFMA of another shape (16x16x32 -> 16x16x16 chains read stale
-        // srcC on gfx950)
-        const bf16x4 ua = pack4(mma_bf16_k16(c.tma, pack4(Va[nb] - xa[nb]), zero4()));
-        const f32x4 xbc = mma_bf16_k16(c.mkb, ua, zero4());
-        const bf16x4 ub = pack4(mma_bf16_k16(c.tmb, pack4(Vb[nb] - xb[nb] - xbc), zero4()));
-        const bf16x8 u2 = cat8(ua, ub);
-        static_for<0, P::MT>([&](auto mc) {
-            constexpr int m = decltype(mc)::value;
-            S[nb][m] = mma_bf16_k32(c.kd2[m], u2, S[nb][m] * gab_tile<m>(c.gv));
-        });
-        f32x4 oa = zero4(), ob = zero4();
-#pragma unroll
-        for (int s = 0; s < P::NSLOT; ++s) {
-            oa = mma_bf16_k32(c.qa[s], sb[nb][s], oa);
-            ob = mma_bf16_k32(c.qb[s], sb[nb][s], ob);
-        }
-        Oa[nb] = oa + mma_bf16_k16(c.aqa, ua, zero4());
-        Ob[nb] = ob + mma_bf16_k32(c.ob2, u2, zero4());
+        const bf16x8 u2 = pair_u<E, D>(c, xa[nb], xb[nb], Va[nb], Vb[nb]);
+        pair_supdate<E, D>(c, S[nb], u2);
+        pair_out<E, D>(c, sb[nb], u2, Oa[nb], Ob[nb]);
     }
 }
 
@@ -917,6 +951,225 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
     if (io.out) state_store<D, NB>(S, io.out_at(b, h, H, D), col0);
 }
 
+// ------------------------------------------------------------ pair roles kernel
+//
+// bf16 chains of one 16-column block, with each step split over two waves.
+// One wave issues its LDS reads, MFMAs and VALU one after the other, so a
+// single chain wave pays for all of a pair's operand reads and products in
+// sequence; here the chain wave computes x, U and the state update and leaves
+// [U_a; U_b] in the ring entry, and the output wave keeps a replica of the
+// state (the same update from the same operands and U, hence bit-identical),
+// forms the pair's outputs and stores them.  Loader waves move each pair
+// block from the workspace straight into its ring entry (LDS DMA, no VGPRs),
+// one pair in flight per loader, and V through VGPRs.
+//
+// Flags, as in pair_inter_kernel, plus:
+//   uready[c]   last pair whose [U_a; U_b] chain c has left in its entry;
+//   done[e][r]  readers r = chain waves 0 .. NCW-1, then output waves.
+// The output wave of chain c waits only for uready[c]; a chain never waits
+// for its output wave except through the ring (a loader refills an entry
+// once every reader released it), so no wait closes a cycle.
+template <typename E, int D, int NCW_>
+struct RoleCfg {
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int NCW = NCW_;
+    static constexpr int NCOL = 16 * NCW;                        // value columns per workgroup
+    static constexpr int LDS_MAX = 160 * 1024 - 512;             // room for the flags
+    static constexpr int VSTR = 2 * kChunk + 2;                  // as in PairCfg
+    static constexpr int VBYTES = NCOL * ES / 4 * VSTR * 4;
+    static constexpr int UBYTES = NCW * kWave * 16;              // one bf16x8 per lane and chain
+    static constexpr int ENT = PBlk<E, D>::BYTES + VBYTES + UBYTES;
+    static constexpr int NPAIR = LDS_MAX / ENT < 5 ? LDS_MAX / ENT : 5;
+    static constexpr int NREAD = 2 * NCW;                        // chain and output waves
+    static constexpr int NL = 8 - NREAD;                         // loader waves: two waves per SIMD
+    static constexpr int THREADS = (NREAD + NL) * kWave;
+    static_assert(ES == 2, "bf16 operands");
+    static_assert(NCOL <= D, "column tile wider than the head");
+    static_assert(NPAIR >= 2, "the ring needs two pair entries");
+    static_assert((2 * kChunk * NCOL * ES / 16) % kWave == 0, "V pieces per loader lane");
+    static_assert(VBYTES % 16 == 0 && ENT % 16 == 0, "ring entries stay 16-byte aligned");
+};
+
+template <typename E, int D, int NCW>
+__global__ __launch_bounds__((RoleCfg<E, D, NCW>::THREADS)) void pair_roles_kernel(
+    const char* __restrict__ ws, const E* __restrict__ v, StateIO io, E* __restrict__ o, int B,
+    int T, int H, int n_first, int n_count, int nct) {
+    using P = PBlk<E, D>;
+    using Cfg = RoleCfg<E, D, NCW>;
+    constexpr int NPAIR = Cfg::NPAIR, NL = Cfg::NL, ENT = Cfg::ENT, ES = Cfg::ES;
+    constexpr int NCOL = Cfg::NCOL, NREAD = Cfg::NREAD;
+    constexpr int BLK16 = P::BYTES / 16;              // 16-byte pieces of one pair block
+    constexpr int PER_LANE = (BLK16 + kWave - 1) / kWave;
+    constexpr int RP = NCOL * ES / 16;                // 16-byte pieces per V row of the tile
+    constexpr int VPL = 2 * kChunk * RP / kWave;
+    constexpr int EPP = 16 / ES;                      // elements per piece
+    constexpr int UOFF = P::BYTES + Cfg::VBYTES;      // [U_a; U_b] of the entry's pair
+    __shared__ __attribute__((aligned(16))) char ring[NPAIR * ENT];
+    __shared__ int ready[NPAIR], done[NPAIR][NREAD], uready[NCW];
+    int u, ct;
+    if (!map_unit(nct, B * H, u, ct)) return;   // uniform over the workgroup
+    const int b = u / H, h = u % H;
+    if (io.skip(b)) return;                      // uniform over the workgroup
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int tile0 = ct * NCOL;
+    const int NP = (n_count + 1) / 2;
+    const char* blk0 = ws + (size_t)u * NP * P::BYTES;
+    const Rsrc rws = make_rsrc(blk0, (uint32_t)((size_t)NP * P::BYTES));
+    if (w == 0) {
+        if (lane < NPAIR) {
+            ready[lane] = -1;
+#pragma unroll
+            for (int c = 0; c < NREAD; ++c) done[lane][c] = -1;
+        }
+        if (lane < NCW) uready[lane] = -1;
+    }
+    wg_barrier();   // the only barrier: flags initialised
+    auto entry = [&](int p) { return ring + (p % NPAIR) * ENT; };
+
+    if (w >= NREAD) {
+        // ------------------------------------------------ loader waves
+        const int L = w - NREAD;
+        for (int p = L; p < NP; p += NL) {
+            if (p >= NPAIR) {   // every reader has released the entry's previous pair
+#pragma unroll
+                for (int c = 0; c < NREAD; ++c) spin_until_ge(&done[p % NPAIR][c], p - NPAIR);
+            }
+            char* dst = entry(p);
+            // V (rows t0 .. t0+31 of the tile's columns; rows past T read 0)
+            // into VGPRs, then the pair block into the entry: V comes from
+            // memory the producer did not just write, so it is issued first
+            // and its latency overlaps the block's
+            const int t0 = (n_first + 2 * p) * kChunk;
+            const int Lr = min(2 * kChunk, T - t0);
+            const size_t rs = (size_t)H * D;
+            const size_t row0 = ((size_t)b * T + t0) * H + h;
+            const Rsrc rv = make_rsrc(v + row0 * D + tile0,
+                                      Lr > 0 ? (uint32_t)(((size_t)(Lr - 1) * rs + NCOL) * ES) : 0u);
+            u32x4 vbuf[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int q = i * kWave + lane, r = q / RP, c = q % RP;
+                vbuf[i] = buf_load<u32x4>(rv, (int)((r * rs + c * EPP) * ES));
+            }
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int piece = i * kWave + lane;
+                if (i + 1 < PER_LANE || piece < BLK16)
+                    buf_load_lds16(rws, (p * BLK16 + piece) * 16, dst + i * kWave * 16);
+            }
+            vm_wait_all();   // V and every piece of the block have landed
+            // V area: word-major (word w of row r at w * VSTR + r)
+            uint32_t* vd = reinterpret_cast<uint32_t*>(dst + P::BYTES);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int q = i * kWave + lane, r = q / RP, c = q % RP;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vd[(4 * c + e) * Cfg::VSTR + r] = vbuf[i][e];
+            }
+            // publish: the V stores complete before the flag store
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __hip_atomic_store(&ready[p % NPAIR], p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        return;
+    }
+
+    const int j = lane & 15, g = lane >> 4;
+    if (w < NCW) {
+        // ------------------------------------------------ chain waves
+        const int col0 = tile0 + 16 * w;
+        const int vcol = 16 * w + j;   // column within the tile
+        // V of chunk half (0 = a, 1 = b): raw words, widened when needed
+        auto v_read = [&](const char* ent, int half) {
+            const uint32_t* at = reinterpret_cast<const uint32_t*>(ent + P::BYTES) + half * kChunk +
+                                 4 * g + (vcol >> 1) * Cfg::VSTR;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(at);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(at + 2);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        auto v_widen = [&](u32x4 x) {
+            x <<= 16 * (1 - (vcol & 1));   // bf16 of this column to the high half
+            x &= 0xFFFF0000u;
+            return __builtin_bit_cast(f32x4, x);
+        };
+        f32x4 S[1][D / 16];
+        state_load<D, 1>(S, io.in_at(b, h, H, D), col0);
+        POps<E, D> c;
+        // one basic block per step but for the rare re-read of a pair whose
+        // first operands were read ahead of its publication
+        spin_until_ge(&ready[0], 0);
+        pops_load_k<E, D>(c, entry(0));
+        int fl = 0;
+        for (int s = 0; s < NP; ++s) {
+            char* ent = entry(s);
+            if (fl < s) {
+                spin_until_ge(&ready[s % NPAIR], s);
+                pops_load_k<E, D>(c, ent);
+            }
+            const u32x4 ra = v_read(ent, 0), rb = v_read(ent, 1);
+            pops_load_chain<E, D>(c, ent);
+            pin_issued();
+            bf16x8 sb[1][P::NSLOT];
+            f32x4 xa[1], xb[1];
+            pair_x<E, D, 1>(c, S, sb, xa, xb);
+            const bf16x8 u2 = pair_u<E, D>(c, xa[0], xb[0], v_widen(ra), v_widen(rb));
+            *reinterpret_cast<bf16x8*>(ent + UOFF + (w * kWave + lane) * 16) = u2;
+            asm volatile("" ::: "memory");
+            __hip_atomic_store(&uready[w], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            pair_supdate<E, D>(c, S[0], u2);
+            // release pair s: its reads were all issued above
+            asm volatile("" ::: "memory");
+            __hip_atomic_store(&done[s % NPAIR][w], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            fl = __hip_atomic_load(&ready[(s + 1) % NPAIR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            asm volatile("" ::: "memory");
+            pops_load_k<E, D>(c, entry(s + 1));   // (past the last pair: stale, unused)
+        }
+        if (io.out) state_store<D, 1>(S, io.out_at(b, h, H, D), col0);
+        return;
+    }
+
+    // ---------------------------------------------------- output waves
+    const int wc = w - NCW;                 // the chain this wave follows
+    const int col0 = tile0 + 16 * wc;
+    f32x4 S[D / 16];
+    {
+        f32x4 S1[1][D / 16];
+        state_load<D, 1>(S1, io.in_at(b, h, H, D), col0);
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m) S[m] = S1[0][m];
+    }
+    POps<E, D> c;
+    for (int s = 0; s < NP; ++s) {
+        char* ent = entry(s);
+        spin_until_ge(&uready[wc], s);
+        const bf16x8 u2 = *reinterpret_cast<const bf16x8*>(ent + UOFF + (wc * kWave + lane) * 16);
+        pops_load_out<E, D>(c, ent);
+        pops_load_supd<E, D>(c, ent);
+        pin_issued();
+        bf16x8 sb[P::NSLOT];
+#pragma unroll
+        for (int k = 0; k < P::NSLOT; ++k) sb[k] = pack8(S[2 * k], S[2 * k + 1]);
+        f32x4 Oa, Ob;
+        pair_out<E, D>(c, sb, u2, Oa, Ob);
+        pair_supdate<E, D>(c, S, u2);
+        // outputs: rows 4g + (j & 3) of each chunk, columns 4 (j >> 2) .. +3
+        // of this block, 8 bytes per lane and chunk; rows past T are dropped
+        {
+            const int t0 = (n_first + 2 * s) * kChunk;
+            const int Lr = min(2 * kChunk, T - t0);
+            const size_t rs = (size_t)H * D;
+            const size_t row0 = ((size_t)b * T + t0) * H + h;
+            const Rsrc ro = make_rsrc(o + row0 * D + col0,
+                                      Lr > 0 ? (uint32_t)(((size_t)(Lr - 1) * rs + 16) * ES) : 0u);
+            const int r = 4 * g + (j & 3), off = (int)((r * rs + 4 * (j >> 2)) * ES);
+            buf_store_u32x2(ro, off, acc_rows_bf16(Oa));
+            buf_store_u32x2(ro, off + (int)(kChunk * rs * ES), acc_rows_bf16(Ob));
+        }
+        asm volatile("" ::: "memory");
+        __hip_atomic_store(&done[s % NPAIR][NCW + wc], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
 // ------------------------------------------------------------ launch
 
 size_t pair_block_bytes(int d, bool is_bf16) {
@@ -943,6 +1196,18 @@ static hipError_t launch_pair_inter_v(const char* ws, const E* v, const StateIO&
     using Cfg = PairCfg<E, D, NCW, NB>;
     const int nct = D / Cfg::NCOL;
     hipLaunchKernelGGL((pair_inter_kernel<E, D, NCW, NB>), dim3(pair_grid(a.B * a.H, nct)),
+                       dim3(Cfg::THREADS), 0, stream, ws, v, io, o, a.B, a.T, a.H, n_first,
+                       n_count, nct);
+    return hipGetLastError();
+}
+
+template <typename E, int D, int NCW>
+static hipError_t launch_pair_roles_v(const char* ws, const E* v, const StateIO& io, E* o,
+                                      const PrefillArgs& a, int n_first, int n_count,
+                                      hipStream_t stream) {
+    using Cfg = RoleCfg<E, D, NCW>;
+    const int nct = D / Cfg::NCOL;
+    hipLaunchKernelGGL((pair_roles_kernel<E, D, NCW>), dim3(pair_grid(a.B * a.H, nct)),
                        dim3(Cfg::THREADS), 0, stream, ws, v, io, o, a.B, a.T, a.H, n_first,
                        n_count, nct);
     return hipGetLastError();
@@ -989,7 +1254,7 @@ static hipError_t launch_split_t(const PrefillArgs& a, const PlanInfo& p, void* 
             else if (p.nb == 2) KDA_PAIR_INTER(1, 2);
             else if (p.ncol == 64) KDA_PAIR_INTER(4, 1);
             else if (p.ncol == 32) KDA_PAIR_INTER(2, 1);
-            else KDA_PAIR_INTER(1, 1);
+            else e = launch_pair_roles_v<E, D, 1>(fws, v, io, o, a, n_first, n_count, stream);
         } else {
             if (p.ncol == 32) KDA_PAIR_INTER(2, 1);
             else KDA_PAIR_INTER(1, 1);
