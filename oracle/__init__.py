@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 benchmark's CPU-baseline leg may import this package.  It shares no code with
 the GPU library and the GPU library never calls it.
 
-* ``kda_oracle.c``  -- token-by-token recurrence in C, fp64 (``liboracle.so``)
+* ``kda_oracle.c``  -- token-by-token recurrence in C, fp64 (``liboracle.so``),
+  and its exact gradients by a reverse sweep over the stored states
 * ``chunkwise.py``  -- an independent chunkwise form in numpy, fp64
 
 The C library is built with gcc by :func:`build` (``oracle/build.py``).
@@ -19,7 +20,7 @@ import numpy as np
 from .build import build, library_path
 
 __all__ = ["Oracle", "build", "library_path", "default", "gate",
-           "gate_chunk_cumsum", "prefill", "decode", "max_threads"]
+           "gate_chunk_cumsum", "prefill", "decode", "backward", "max_threads"]
 
 _dbl_p = ctypes.POINTER(ctypes.c_double)
 _flt_p = ctypes.POINTER(ctypes.c_float)
@@ -66,6 +67,9 @@ class Oracle:
         lib.kda_oracle_decode.argtypes = ([_flt_p] * 6 + [ctypes.c_double, _dbl_p, _dbl_p,
                                                           L, L, L, L, ctypes.c_int])
         lib.kda_oracle_decode.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = ([_flt_p] * 6 + [ctypes.c_double] + [_flt_p] * 3
+                                            + [_dbl_p] * 7 + [L, L, L, L, L, ctypes.c_int])
+        lib.kda_oracle_backward.restype = ctypes.c_int
         lib.kda_oracle_max_threads.argtypes = []
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -128,6 +132,29 @@ class Oracle:
             raise MemoryError("oracle decode: allocation failed")
         return o
 
+    def backward(self, q, k, v, z, beta, A, g_min, S0, dO, dST=None, nthreads=0):
+        """fp64 gradients of L = sum(dO * o) + sum(dST * S_T) through the
+        token-by-token prefill.  Shapes as in :meth:`prefill`; dO [B,T,H,dv],
+        dST [B,H,dk,dv] or None.  Returns a dict of fp64 arrays dq, dk, dv,
+        dz, dbeta, dA, dS0."""
+        q, k, v, z, beta, A, dO = (_f32(x) for x in (q, k, v, z, beta, A, dO))
+        B, T, H, dk = k.shape
+        dv = v.shape[-1]
+        s0 = None if S0 is None else _f32(S0)
+        dst = None if dST is None else _f32(dST)
+        out = dict(dq=np.empty((B, T, H, dk)), dk=np.empty((B, T, H, dk)),
+                   dv=np.empty((B, T, H, dv)), dz=np.empty((B, T, H, dk)),
+                   dbeta=np.empty((B, T, H)), dA=np.empty((H,)),
+                   dS0=np.empty((B, H, dk, dv)))
+        rc = self.lib.kda_oracle_backward(
+            _fp(q), _fp(k), _fp(v), _fp(z), _fp(beta), _fp(A), float(g_min),
+            None if s0 is None else _fp(s0), _fp(dO), None if dst is None else _fp(dst),
+            *(_dp(out[n]) for n in ("dq", "dk", "dv", "dz", "dbeta", "dA", "dS0")),
+            B, T, H, dk, dv, int(nthreads))
+        if rc != 0:
+            raise MemoryError("oracle backward: allocation failed")
+        return out
+
 
 _default: Oracle | None = None
 
@@ -158,3 +185,7 @@ def prefill(q, k, v, z, beta, A, g_min, S0=None, nthreads=0, want_state=True):
 
 def decode(q, k, v, z, beta, A, g_min, S, nthreads=0):
     return default().decode(q, k, v, z, beta, A, g_min, S, nthreads)
+
+
+def backward(q, k, v, z, beta, A, g_min, S0, dO, dST=None, nthreads=0):
+    return default().backward(q, k, v, z, beta, A, g_min, S0, dO, dST, nthreads)

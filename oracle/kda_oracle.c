@@ -201,6 +201,153 @@ int kda_oracle_decode(const float *q, const float *k, const float *v,
     return failed ? 1 : 0;
 }
 
+/* Gradients of the token-by-token prefill (reverse-mode differentiation of
+ * the recurrence above, written out step by step; the pages describe no
+ * backward pass, so this is the exact gradient of the forward definition).
+ *
+ * Scalar loss: L = sum(dO * o) + sum(dST * S_T), i.e. dO and dST are the
+ * incoming gradients of o and S_T (dST may be NULL: zeros).  Outputs (double):
+ *   dq, dk, dz [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H], dA [H],
+ *   dS0 [B,H,dk,dv] (the gradient of the initial state, whether or not S0 is
+ *   NULL).
+ * Every per-token state S_0 .. S_T of a head is kept (T+1 copies of dk x dv
+ * doubles), so this is for small and medium T.
+ *
+ * Per token (forward, for reference):
+ *   x = e^{A} z, s = Sigmoid(x), a = e^{g_min s}, S' = Diag(a) S_{t-1},
+ *   u = v - S'^T k, e = beta u, S_t = S' + k e^T, o = S_t^T q.
+ * Reverse, with dS the gradient of S_t (dST at t = T-1):
+ *   dS += q do^T;         dq = S_t do
+ *   de = dS^T k;          dk = dS e;       dbeta = de . u;   dv = beta de
+ *   dp = -beta de;        dS' = dS + k dp^T;   dk += S' dp
+ *   da = rowsum(dS' o S_{t-1});   dg = da a;   dx = dg g_min s (1 - s)
+ *   dz = dx e^{A};        dA += dx x;      dS_{t-1} = Diag(a) dS'
+ */
+int kda_oracle_backward(const float *q, const float *k, const float *v,
+                        const float *z, const float *beta, const float *A,
+                        double g_min, const float *S0, const float *dO,
+                        const float *dST, double *dq, double *dk, double *dv,
+                        double *dz, double *dbeta, double *dA, double *dS0,
+                        long B, long T, long H, long dk_, long dv_, int nthreads)
+{
+    const long DK = dk_, DV = dv_, units = B * H;
+    const size_t SS = (size_t)DK * DV;
+    double *dA_unit = (double *)calloc((size_t)units, sizeof(double));
+    if (!dA_unit)
+        return 1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(|| : failed)
+#endif
+    for (long u = 0; u < units; ++u) {
+        const long b = u / H, h = u % H;
+        /* states S_0 .. S_T, per token: a, s, x (dk each), u (dv) */
+        double *St = (double *)malloc(sizeof(double) * (SS * (size_t)(T + 1)));
+        double *tok = (double *)malloc(sizeof(double) * ((size_t)T * (3 * DK + DV) + 2 * SS + DK + DV));
+        if (!St || !tok) {
+            free(St);
+            free(tok);
+            failed = 1;
+            continue;
+        }
+        double *dS = tok + (size_t)T * (3 * DK + DV);
+        double *dSp = dS + SS;
+        double *de = dSp + SS; /* dv */
+        double *da = de + DV;  /* dk */
+        const double eA = exp((double)A[h]);
+        const size_t sbase = ((size_t)b * H + h) * SS;
+        for (size_t e = 0; e < SS; ++e)
+            St[e] = S0 ? (double)S0[sbase + e] : 0.0;
+        /* forward, keeping what the reverse sweep needs */
+        for (long t = 0; t < T; ++t) {
+            const size_t row = ((size_t)b * T + t) * H + h;
+            const float *kv = k + row * DK, *zv = z + row * DK, *vv = v + row * DV;
+            double *a = tok + (size_t)t * (3 * DK + DV), *sg = a + DK, *xs = sg + DK, *uu = xs + DK;
+            const double *Sp = St + (size_t)t * SS;
+            double *Sn = St + (size_t)(t + 1) * SS;
+            for (long c = 0; c < DK; ++c) {
+                xs[c] = eA * (double)zv[c];
+                sg[c] = logistic(xs[c]);
+                a[c] = exp(g_min * sg[c]);
+                for (long j = 0; j < DV; ++j)
+                    Sn[c * DV + j] = a[c] * Sp[c * DV + j];
+            }
+            for (long j = 0; j < DV; ++j) {
+                double p = 0.0;
+                for (long c = 0; c < DK; ++c)
+                    p += (double)kv[c] * Sn[c * DV + j];
+                uu[j] = (double)vv[j] - p;
+            }
+            for (long c = 0; c < DK; ++c)
+                for (long j = 0; j < DV; ++j)
+                    Sn[c * DV + j] += (double)kv[c] * (double)beta[row] * uu[j];
+        }
+        /* reverse sweep */
+        for (size_t e = 0; e < SS; ++e)
+            dS[e] = dST ? (double)dST[sbase + e] : 0.0;
+        for (long t = T - 1; t >= 0; --t) {
+            const size_t row = ((size_t)b * T + t) * H + h;
+            const float *qv = q + row * DK, *kv = k + row * DK, *dov = dO + row * DV;
+            const double bt = beta[row];
+            const double *a = tok + (size_t)t * (3 * DK + DV), *sg = a + DK, *xs = sg + DK, *uu = xs + DK;
+            const double *Sprev = St + (size_t)t * SS, *Scur = St + (size_t)(t + 1) * SS;
+            /* o = S_t^T q */
+            for (long c = 0; c < DK; ++c) {
+                double acc = 0.0;
+                for (long j = 0; j < DV; ++j) {
+                    dS[c * DV + j] += (double)qv[c] * (double)dov[j];
+                    acc += Scur[c * DV + j] * (double)dov[j];
+                }
+                dq[row * DK + c] = acc;
+            }
+            /* S_t = S' + k e^T, e = beta (v - S'^T k) */
+            double db = 0.0;
+            for (long j = 0; j < DV; ++j) {
+                double acc = 0.0;
+                for (long c = 0; c < DK; ++c)
+                    acc += (double)kv[c] * dS[c * DV + j];
+                de[j] = acc;
+                db += acc * uu[j];
+                dv[row * DV + j] = bt * acc;
+            }
+            dbeta[row] = db;
+            for (long c = 0; c < DK; ++c) {
+                double dkc = 0.0, dac = 0.0;
+                for (long j = 0; j < DV; ++j) {
+                    const double sprime = a[c] * Sprev[c * DV + j];
+                    const double dp = -bt * de[j];
+                    dkc += dS[c * DV + j] * bt * uu[j] + sprime * dp;
+                    dSp[c * DV + j] = dS[c * DV + j] + (double)kv[c] * dp;
+                    dac += dSp[c * DV + j] * Sprev[c * DV + j];
+                }
+                dk[row * DK + c] = dkc;
+                da[c] = dac;
+            }
+            /* S' = Diag(a) S_{t-1}, a = exp(g_min Sigmoid(e^A z)) */
+            for (long c = 0; c < DK; ++c) {
+                const double dg = da[c] * a[c];
+                const double dx = dg * g_min * sg[c] * (1.0 - sg[c]);
+                dz[row * DK + c] = dx * eA;
+                dA_unit[u] += dx * xs[c];
+                for (long j = 0; j < DV; ++j)
+                    dS[c * DV + j] = a[c] * dSp[c * DV + j];
+            }
+        }
+        for (size_t e = 0; e < SS; ++e)
+            dS0[sbase + e] = dS[e];
+        free(St);
+        free(tok);
+    }
+    for (long h = 0; h < H; ++h)
+        dA[h] = 0.0;
+    for (long u = 0; u < units; ++u)
+        dA[u % H] += dA_unit[u];
+    free(dA_unit);
+    return failed ? 1 : 0;
+}
+
 int kda_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -300,10 +300,77 @@ def pin_decode_matches_prefill(orc):
     np.testing.assert_array_equal(S, ST)
 
 
+# --------------------------------------------------------------------------- gradients
+
+def _loss_fd(x, dO, dST, g_min, C):
+    """L = sum(dO o) + sum(dST S_T) through the fp64 chunkwise form."""
+    o, ST = chunk_prefill(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], g_min,
+                          x["S0"], C)
+    return float(np.sum(dO * o) + np.sum(dST * ST))
+
+
+def pin_backward_finite_difference(orc):
+    """Gradients of L = sum(dO o) + sum(dST S_T) against Richardson-extrapolated
+    central differences of L through the independent fp64 chunkwise form, along
+    random directions, for every input (q, k, v, z, beta, A, S0)."""
+    rng = np.random.default_rng(31)
+    B, T, H, dk, dv = 2, 11, 2, 4, 3
+    for g_min in (-5.0, -1.3):
+        q, k, v, z, beta, A, S0 = _inputs(rng, B, T, H, dk, dv)
+        dO = rng.standard_normal((B, T, H, dv))
+        dST = rng.standard_normal((B, H, dk, dv))
+        gr = orc.backward(q, k, v, z, beta, A, g_min, S0, dO.astype(np.float32),
+                          dST.astype(np.float32))
+        dO = dO.astype(np.float32).astype(np.float64)
+        dST = dST.astype(np.float32).astype(np.float64)
+        x0 = {n: a.astype(np.float64) for n, a in
+              dict(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0).items()}
+        names = dict(q="dq", k="dk", v="dv", z="dz", beta="dbeta", A="dA", S0="dS0")
+        for n, gname in names.items():
+            for _ in range(2):
+                d = rng.standard_normal(x0[n].shape)
+
+                def D(h):
+                    xp = dict(x0)
+                    xm = dict(x0)
+                    xp[n] = x0[n] + h * d
+                    xm[n] = x0[n] - h * d
+                    return (_loss_fd(xp, dO, dST, g_min, 4) - _loss_fd(xm, dO, dST, g_min, 4)) / (2 * h)
+
+                h = 1e-3
+                fd = (4.0 * D(h / 2) - D(h)) / 3.0
+                an = float(np.sum(gr[gname] * d))
+                scale = max(abs(fd), float(np.linalg.norm(gr[gname]) * np.linalg.norm(d)), 1e-3)
+                assert abs(an - fd) <= 1e-8 * scale, (n, g_min, an, fd)
+
+
+def pin_backward_beta_zero(orc):
+    """beta = 0 closed form: o_t = S0^T (e^{cumsum g} q_t), S_T = Diag(e^{sum g}) S0,
+    so dq_t = e^{cumsum g} (S0 dO_t), dk = dv = 0 and
+    dS0 = sum_t (e^{cumsum g} q_t) dO_t^T + Diag(e^{sum g}) dST."""
+    rng = np.random.default_rng(32)
+    B, T, H, dk, dv = 2, 9, 3, 5, 4
+    q, k, v, z, beta, A, S0 = _inputs(rng, B, T, H, dk, dv)
+    beta = np.zeros_like(beta)
+    dO = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    dST = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gr = orc.backward(q, k, v, z, beta, A, -5.0, S0, dO, dST)
+    g = -5.0 * expit(np.exp(A.astype(np.float64))[None, None, :, None] * z.astype(np.float64))
+    Gam = np.exp(np.cumsum(g, axis=1))                                   # [B,T,H,dk]
+    S0d = S0.astype(np.float64)
+    dq_ref = Gam * np.einsum("bhcj,bthj->bthc", S0d, dO.astype(np.float64))
+    dS0_ref = (np.einsum("bthc,bthj->bhcj", Gam * q, dO.astype(np.float64))
+               + Gam[:, -1][..., None] * dST)
+    np.testing.assert_allclose(gr["dq"], dq_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gr["dS0"], dS0_ref, rtol=1e-12, atol=1e-13)
+    assert np.all(gr["dk"] == 0.0) and np.all(gr["dv"] == 0.0)
+
+
 PINS = [pin_gate_at_zero, pin_gate_library, pin_gate_bounds_printed, pin_chunk_cumsum,
         pin_scalar_ema, pin_beta_zero, pin_exact_retrieval, pin_linear_attention,
         pin_alpha_one_beta_zero, pin_chunkwise_equivalence, pin_continuation,
-        pin_linearity, pin_structure, pin_decode_matches_prefill]
+        pin_linearity, pin_structure, pin_decode_matches_prefill,
+        pin_backward_finite_difference, pin_backward_beta_zero]
 
 
 def failing_pins(orc):

@@ -33,6 +33,21 @@ MUTANTS = [
     ("state_not_carried", "S[e] = S0 ? (double)S0[sbase + e] : 0.0;", "S[e] = 0.0;"),
     ("decode_wrong_beta", "beta[u], A[h]", "beta[h], A[h]"),
     ("write_uses_query", "double kc = kv[c];", "double kc = qv[c];"),
+    # the reverse sweep
+    ("bwd_dq_from_previous_state", "acc += Scur[c * DV + j] * (double)dov[j];",
+     "acc += Sprev[c * DV + j] * (double)dov[j];"),
+    ("bwd_dp_sign", "const double dp = -bt * de[j];", "const double dp = bt * de[j];"),
+    ("bwd_state_grad_not_decayed", "dS[c * DV + j] = a[c] * dSp[c * DV + j];",
+     "dS[c * DV + j] = dSp[c * DV + j];"),
+    ("bwd_dA_without_x", "dA_unit[u] += dx * xs[c];", "dA_unit[u] += dx;"),
+    ("bwd_dz_without_expA", "dz[row * DK + c] = dx * eA;", "dz[row * DK + c] = dx;"),
+    ("bwd_dbeta_uses_e", "db += acc * uu[j];", "db += acc * bt * uu[j];"),
+    ("bwd_sigmoid_derivative", "g_min * sg[c] * (1.0 - sg[c])", "g_min * sg[c]"),
+    ("bwd_da_uses_decayed_state", "dac += dSp[c * DV + j] * Sprev[c * DV + j];",
+     "dac += dSp[c * DV + j] * a[c] * Sprev[c * DV + j];"),
+    ("bwd_dST_ignored", "dS[e] = dST ? (double)dST[sbase + e] : 0.0;", "dS[e] = 0.0;"),
+    ("bwd_dk_write_term_dropped", "dkc += dS[c * DV + j] * bt * uu[j] + sprime * dp;",
+     "dkc += sprime * dp;"),
 ]
 
 
