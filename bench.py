@@ -4,7 +4,7 @@
 
 One step = one chunkwise prefill pass (gate + intra-chunk + inter-chunk, all
 in libkda's HIP kernels: for this workload a pair-producer launch and a
-state-chain launch) over the mid-size synthetic workload: B=1, H=32,
+state-chain launch, pair_roles_kernel) over the mid-size synthetic workload: B=1, H=32,
 T=4096, d_k=d_v=128, bf16 q/k/v/z, fp32 beta/A/state, g_min=-5.  Inputs are
 resident in HBM before timing, and cold: the steps cycle through copies of
 the inputs, so a step's inputs were last touched more than 1 GiB of traffic
@@ -202,7 +202,7 @@ def main():
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"prefill_{args.workload}_pass_bytes_{'split' if nb else 'fused'}"),
                      "traffic_unit": "bytes per pass",
-                     "kernel": ("prefill pass (pair_intra_kernel + pair_inter_kernel)" if nb
+                     "kernel": ("prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
                                 else "prefill pass (fused_kernel)"),
                      "alg_bytes_per_step": alg_b,
                      "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
