@@ -17,7 +17,8 @@ steps/s of the B=256 workload (1,000 back-to-back in-place steps), and a
 ``verify`` object with the multi-token step (T drafted tokens per sequence
 from the B=256 live state into a separate state buffer) per second, and a
 ``decode_paged`` object with the decode step on states addressed through a
-slot table into a pool.
+slot table into a pool, and a ``backward`` object with the gradients of the
+same prefill (kda_chunk_backward) per second.
 """
 from __future__ import annotations
 
@@ -58,6 +59,13 @@ def verify_alg_bytes(B, H, d, T, es=2):
     return B * H * (2 * d * d * 4 + T * (5 * d * es + 4))
 
 
+def backward_alg_bytes(B, T, H, d, es=2):
+    """Per token-head: q, k, v, z, dO read and dq, dk, dv, dz written (es
+    bytes each), beta read and dbeta written (fp32); per (b, h): dS_T read and
+    dS0 written (fp32)."""
+    return B * T * H * (9 * d * es + 8) + B * H * d * d * 4 * 2
+
+
 def decode_alg_bytes(B, H, d, es=2):
     """S read + write (fp32) + q, k, v, z, o (es) + beta per (b, h)."""
     return B * H * (2 * d * d * 4 + 5 * d * es + 4)
@@ -90,6 +98,8 @@ def main():
     ap.add_argument("--workload", choices=["mid", "batched"], default="mid",
                     help="prefill workload: mid = B1 H32 T4096 (the headline), "
                          "batched = B8 H32 T32768 with a carried state")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--plan", default=None,
                     help="force the prefill plan (sets KDA_PREFILL_PLAN: split | fused:<ncol>)")
     args = ap.parse_args()
@@ -327,6 +337,48 @@ def main():
                          "kernel": "tokens_kernel", "alg_bytes_per_step": vb},
         }
         del S, S_out, xv
+
+    if not args.no_backward and args.workload == "mid":
+        # gradients of the same prefill (dO ~ N(0, 1), dS_T ~ N(0, 1))
+        from linear_attention_recurrence_05_amd.inputs import backward_grads
+        gr = backward_grads(B, T, H, d, d, cfg.dtype, seed=cfg_index, device=dev)
+        gq = [torch.empty_like(x[n]) for n in ("q", "k", "v", "z")]
+        gb = torch.empty(B, T, H, dtype=torch.float32, device=dev)
+        gA = torch.empty(H, dtype=torch.float32, device=dev)
+        gS0 = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+        nbw = kda.kda_chunk_backward_workspace_bytes(B, T, H, d, d, cfg.dtype)
+        wsb = torch.empty(nbw, dtype=torch.uint8, device=dev)
+
+        def run_bwd():
+            kda.kda_chunk_backward(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
+                                   x["S0"], gr["dO"], gr["dST"], *gq, gb, gA, gS0, wsb, stream)
+
+        run_bwd()
+        reps = []
+        for _ in range(args.backward_steps):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_bwd()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1))
+        bms = sorted(reps)[len(reps) // 2]
+        bb = backward_alg_bytes(B, T, H, d)
+        bgbs = bb / (bms * 1e-3) / 1e9
+        line["backward"] = {
+            "metric": "KDA prefill-backward tokens/s",
+            "value": tokens / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms,
+            "repetitions": args.backward_steps,
+            "config": {"workload": f"backward_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T, "H": H,
+                       "d_k": d, "d_v": d, "workspace_bytes": nbw},
+            "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bgbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "backward pass (bwd_ckpt_kernel + bwd_seg_kernel + "
+                                   "bwd_finalize_kernel + bwd_dA_kernel)",
+                         "alg_bytes_per_step": bb},
+        }
+        del wsb, gq, gS0
 
     if not args.no_cpu_baseline and args.workload == "mid":
         import oracle

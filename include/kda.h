@@ -125,6 +125,41 @@ kda_status kda_chunk_prefill(const void *q, const void *k, const void *v,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Bytes of device workspace kda_chunk_backward needs for these sizes (0 for
+ * arguments it would reject).  It holds the state at the start of every
+ * 16-token chunk (B * H * ceil(T / 16) * d_k * d_v * 4 bytes), one state per
+ * (b, h) carried between launches, and partial sums of one segment of the
+ * sequence (at most about 256 MiB, or one 64-token block). */
+size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
+                                          kda_dtype dt);
+
+/* Gradients of kda_chunk_prefill (the pages give no backward pass; this is
+ * the exact gradient of the recurrence above, for training).  With dO the
+ * gradient of o [B, T, H, d_v] (element type dt) and dS_T that of the final
+ * state [B, H, d_k, d_v] fp32 (NULL: zero), it writes the gradients of
+ * L = sum(dO * o) + sum(dS_T * S_T):
+ *   dq, dk, dz [B, T, H, d_k] and dv [B, T, H, d_v]   element type dt
+ *   dbeta [B, T, H], dA [H]                            fp32
+ *   dS0 [B, H, d_k, d_v]  fp32, the gradient of the initial state (NULL: not
+ *                         written; it is the same whether or not S0 is NULL)
+ * q, k, v, z, beta, A, g_min and S0 (NULL: zero) are the forward call's
+ * inputs; the forward states are recomputed from them, o is not needed.
+ *   S0, dS_T and dS0 must be 16-byte aligned.  No output may overlap an input,
+ *   another output or the workspace.
+ *   workspace       : device memory of at least
+ *                     kda_chunk_backward_workspace_bytes(...) bytes, scratch
+ *                     for this call only.
+ * The sweep runs in fp32 whatever dt is.  dA and dbeta are summed over
+ * value-column blocks and tokens in a fixed order (deterministic). */
+kda_status kda_chunk_backward(const void *q, const void *k, const void *v,
+                              const void *z, const float *beta, const float *A,
+                              float g_min, const float *S0, const void *dO,
+                              const float *dS_T, void *dq, void *dk, void *dv,
+                              void *dz, float *dbeta, float *dA, float *dS0,
+                              int B, int T, int H, int d_k, int d_v,
+                              kda_dtype dt, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* One recurrent decode step: for every (b, h) the state S [B, H, d_k, d_v]
  * (fp32) is read once and overwritten in place with S_t; o receives
  * S_t^T q_t.  o must not overlap S or the inputs. */

@@ -49,6 +49,9 @@ _SIGNATURES = {
                               ctypes.c_int),
     "kda_decode_tokens_paged": ([_vp] * 6 + [ctypes.c_float, _vp, _i, _vp, _vp, _vp] + [_i] * 6
                                 + [_vp], ctypes.c_int),
+    "kda_chunk_backward_workspace_bytes": ([_i, _i, _i, _i, _i, _i], ctypes.c_size_t),
+    "kda_chunk_backward": ([_vp] * 6 + [ctypes.c_float] + [_vp] * 10 + [_i] * 6
+                           + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "kda_gate_chunk_cumsum": ([_vp, _vp, ctypes.c_float, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
     "kda_intra_chunk": ([_vp] * 5 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 5 + [_vp],
                         ctypes.c_int),
@@ -232,6 +235,46 @@ def chunk_prefill(q, k, v, z, beta, A, g_min=-5.0, S0=None, want_state=True, str
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, ws, stream)
     return o, S_T
+
+
+def kda_chunk_backward_workspace_bytes(B, T, H, d_k, d_v, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+    return int(lib().kda_chunk_backward_workspace_bytes(B, T, H, d_k, d_v, code))
+
+
+def kda_chunk_backward(q, k, v, z, beta, A, g_min, S0, dO, dS_T, dq, dk, dv, dz, dbeta, dA, dS0,
+                       workspace, stream=None):
+    """C entry point kda_chunk_backward on torch tensors (layouts of kda.h)."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0, dO=dO, dS_T=dS_T, dq=dq,
+                        dk=dk, dv=dv, dz=dz, dbeta=dbeta, dA=dA, dS0=dS0)
+    B, T, H, dkk = q.shape
+    dvv = v.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kda_chunk_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                  float(g_min), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _ptr(dz), _ptr(dbeta), _ptr(dA), _ptr(dS0),
+                                  B, T, H, dkk, dvv, _dtype_code(q), _ptr(workspace), ws_bytes,
+                                  _stream(stream))
+    _check(st, "kda_chunk_backward")
+
+
+def chunk_backward(q, k, v, z, beta, A, dO, g_min=-5.0, S0=None, dS_T=None, want_dS0=True,
+                   stream=None):
+    """Allocate the gradients (and the workspace) with torch.empty and run
+    kda_chunk_backward.  Returns a dict with dq, dk, dv, dz, dbeta, dA, dS0."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    g = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+             dz=torch.empty_like(z),
+             dbeta=torch.empty((B, T, H), dtype=torch.float32, device=q.device),
+             dA=torch.empty((H,), dtype=torch.float32, device=q.device),
+             dS0=(torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+                  if want_dS0 else None))
+    nbytes = kda_chunk_backward_workspace_bytes(B, T, H, dk, dv, q.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    kda_chunk_backward(q, k, v, z, beta, A, g_min, S0, dO, dS_T, g["dq"], g["dk"], g["dv"],
+                       g["dz"], g["dbeta"], g["dA"], g["dS0"], ws, stream)
+    return g
 
 
 def decode_tokens(q, k, v, z, beta, A, S, S_out=None, g_min=-5.0, stream=None):

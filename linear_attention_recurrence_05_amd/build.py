@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_pair.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_pair.hip", "kda_backward.hip"]
 ARCH = "gfx950"
 
 

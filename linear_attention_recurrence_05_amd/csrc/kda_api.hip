@@ -292,6 +292,54 @@ kda_status kda_decode_tokens_paged(const void* q, const void* k, const void* v, 
     return hip_status(kda::launch_tokens(a, (hipStream_t)stream), "kda_decode_tokens_paged launch");
 }
 
+size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v, kda_dtype dt) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return 0;
+    if (!(d_k == d_v && (d_k == 32 || d_k == 128))) return 0;
+    if (B < 1 || T < 1 || H < 1 || (long long)B * H > (1LL << 26) ||
+        (unsigned long long)B * T * H > (1ULL << 40) || (long long)H * d_k > (1LL << 24))
+        return 0;
+    return kda::bwd_layout(B, T, H, d_k).total;
+}
+
+kda_status kda_chunk_backward(const void* q, const void* k, const void* v, const void* z,
+                              const float* beta, const float* A, float g_min, const float* S0,
+                              const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                              void* dz, float* dbeta, float* dA, float* dS0, int B, int T, int H,
+                              int d_k, int d_v, kda_dtype dt, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    size_t nel, ntok;
+    if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
+    const size_t need = kda::bwd_layout(B, T, H, d_k).total;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t sbytes = (size_t)B * H * d_k * d_v * sizeof(float);
+    const Range r[] = {{"q", q, nel * es, 16},       {"k", k, nel * es, 16},
+                       {"v", v, nel * es, 16},       {"z", z, nel * es, 16},
+                       {"beta", beta, ntok * 4, 4},  {"A", A, (size_t)H * 4, 4},
+                       {"S0", S0, sbytes, 16},       {"dO", dO, nel * es, 16},
+                       {"dS_T", dS_T, sbytes, 16},   {"dq", dq, nel * es, 16},
+                       {"dk", dk, nel * es, 16},     {"dv", dv, nel * es, 16},
+                       {"dz", dz, nel * es, 16},     {"dbeta", dbeta, ntok * 4, 4},
+                       {"dA", dA, (size_t)H * 4, 4}, {"dS0", dS0, sbytes, 16},
+                       {"workspace", workspace, need, 16}};
+    constexpr int n = 17;
+    const bool req[n] = {true, true, true, true, true, true, false, true, false,
+                         true, true, true, true, true, true, false, true};
+    if ((s = check_ptrs(r, n, req)) != KDA_OK) return s;
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    // outputs (dq .. dS0) and the workspace may overlap nothing else
+    for (int out = 9; out < n; ++out)
+        for (int i = 0; i < n; ++i)
+            if (i != out && overlap(r[out], r[i]))
+                return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
+    kda::BackwardArgs a{q,  k,  v,  z,     beta, A,  g_min, S0, dO, dS_T, dq, dk,
+                        dv, dz, dbeta, dA, dS0,  B,  T,     H,  d_k, dt == KDA_BF16};
+    return hip_status(kda::launch_backward(a, workspace, (hipStream_t)stream),
+                      "kda_chunk_backward launch");
+}
+
 kda_status kda_gate_chunk_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,
                                  int H, int d_k, kda_dtype dt, void* stream) {
     kda_status s = check_common(d_k, d_k, dt, g_min);

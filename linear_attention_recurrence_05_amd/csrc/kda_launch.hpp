@@ -73,6 +73,37 @@ struct PrefillArgs {
     bool is_bf16;
 };
 
+// Gradients of a prefill: inputs of the forward call plus dO (and dST, may be
+// null: zeros); outputs dq, dk, dv, dz (element type of the inputs), dbeta,
+// dA (fp32) and dS0 (fp32, may be null: not written).
+struct BackwardArgs {
+    const void *q, *k, *v, *z;
+    const float *beta, *A;
+    float g_min;
+    const float* S0;
+    const void* dO;
+    const float* dST;
+    void *dq, *dk, *dv, *dz;
+    float *dbeta, *dA, *dS0;
+    int B, T, H, d;
+    bool is_bf16;
+};
+
+// Backward geometry: value columns per workgroup, tokens per finalize block,
+// and the bound on the per-segment partial sums in the workspace.
+constexpr int kBwdCols = 8;
+constexpr int kBwdTokBlock = 64;
+constexpr size_t kBwdPartialBudget = (size_t)256 << 20;
+
+// Byte offsets of the backward workspace regions (each 256-byte aligned).
+struct BwdLayout {
+    size_t ckpt, carry, pq, pk, pg, pb, dA_part, total;
+    int seg;     // tokens per reverse-sweep launch (multiple of kBwdTokBlock)
+    int NC;      // chunks (checkpoints) per sequence
+    int ntb;     // finalize token blocks per sequence
+};
+BwdLayout bwd_layout(int B, int T, int H, int d);
+
 // How a prefill is executed.
 enum class Plan {
     kFused,   // gate + intra + inter in one launch; one workgroup per (b, h, column tile)
@@ -105,6 +136,7 @@ hipError_t launch_tokens(const TokensArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
 // Split plan: pair intra kernel -> workspace -> pair inter kernel, per segment.
 hipError_t launch_split(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, void* ws, hipStream_t stream);
 hipError_t launch_gate_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,
                               int H, int d, bool is_bf16, hipStream_t stream);
 hipError_t launch_intra_diag(const void* q, const void* k, const void* z, const float* beta,

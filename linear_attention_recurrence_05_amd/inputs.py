@@ -135,3 +135,14 @@ def decode_step_inputs(gen, B, H, dk, dv, dtype=torch.bfloat16, device="cpu", st
         return dict(q=q, k=k, v=v, z=z, beta=beta)
     parts = [decode_step_inputs(gen, B, H, dk, dv, dtype, device) for _ in range(steps)]
     return {key: torch.stack([p[key] for p in parts]) for key in parts[0]}
+
+
+def backward_grads(B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, with_dST=True,
+                   device="cpu"):
+    """Incoming gradients for a backward call: dO ~ N(0, 1) [B,T,H,dv] in the
+    input dtype and, if asked, dS_T ~ N(0, 1) [B,H,dk,dv] fp32, drawn in that
+    order from their own generator (seed + 1000)."""
+    gen = _gen(seed + 1000, device)
+    dO = _randn(gen, (B, T, H, dv), device).to(dtype)
+    dST = _randn(gen, (B, H, dk, dv), device) if with_dST else None
+    return dict(dO=dO, dST=dST)

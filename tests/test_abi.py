@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for n in ["kda_abi_version", "kda_status_string", "kda_last_error",
               "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_decode_step",
               "kda_decode_tokens", "kda_chunk_prefill_paged", "kda_decode_step_paged",
-              "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk"]:
+              "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk",
+              "kda_chunk_backward_workspace_bytes", "kda_chunk_backward"]:
         assert n in names
 
 
@@ -249,3 +250,52 @@ def test_binding_raises_named_errors():
     x = torch.zeros(1, 16, 1, 48)   # d = 48 unsupported, caught on the host
     with pytest.raises(kda.KdaError, match="KDA_ERR_UNSUPPORTED"):
         kda.kda_gate_chunk_cumsum(x, torch.zeros(1), -5.0, torch.zeros_like(x), stream=0)
+
+
+def backward(**over):
+    """Call kda_chunk_backward with fake pointers; every use below fails
+    host-side validation, so nothing is launched."""
+    args = dict(q=fake(0), k=fake(1), v=fake(2), z=fake(3), beta=fake(4), A=fake(5), g_min=-5.0,
+                S0=fake(6), dO=fake(7), dST=fake(8), dq=fake(9), dk=fake(10), dv=fake(11),
+                dz=fake(12), dbeta=fake(13), dA=fake(14), dS0=fake(15), B=1, T=64, H=2, d_k=32,
+                d_v=32, dt=kda.KDA_F32, ws=fake(16), ws_bytes=0, stream=None)
+    args.update(over)
+    L = kda.lib()
+    st = L.kda_chunk_backward(*(args[n] for n in ("q", "k", "v", "z", "beta", "A", "g_min", "S0",
+                                                  "dO", "dST", "dq", "dk", "dv", "dz", "dbeta",
+                                                  "dA", "dS0", "B", "T", "H", "d_k", "d_v", "dt",
+                                                  "ws", "ws_bytes", "stream")))
+    return st, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dO=None), "KDA_ERR_NULL_POINTER"),
+    (dict(dz=None), "KDA_ERR_NULL_POINTER"),
+    (dict(dA=None), "KDA_ERR_NULL_POINTER"),
+    (dict(ws=None), "KDA_ERR_NULL_POINTER"),
+    (dict(T=0), "KDA_ERR_INVALID_SHAPE"),
+    (dict(g_min=-6.0), "KDA_ERR_INVALID_VALUE"),
+    (dict(d_k=64, d_v=64), "KDA_ERR_UNSUPPORTED"),
+    (dict(dS0=fake(15, misalign=4)), "KDA_ERR_MISALIGNED"),
+    (dict(dST=fake(8, misalign=8)), "KDA_ERR_MISALIGNED"),
+    (dict(), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(ws_bytes=1 << 33, dq=fake(0)), "KDA_ERR_ALIASING"),          # dq == q
+    (dict(ws_bytes=1 << 33, dS0=fake(14)), "KDA_ERR_ALIASING"),        # dS0 == dA
+    (dict(ws_bytes=1 << 33, ws=fake(12, misalign=16)), "KDA_ERR_ALIASING"),   # inside dz
+])
+def test_backward_rejects(over, code):
+    st, detail = backward(**over)
+    assert st == E[code], (st, detail)
+    assert detail
+
+
+def test_backward_workspace_query():
+    n = kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_BF16)
+    # at least the chunk-start states: 32 heads x 256 chunks x 128 x 128 fp32
+    assert n >= 32 * 256 * 128 * 128 * 4
+    # the partial sums stay bounded as T grows (segments), the checkpoints do not
+    n2 = kda.kda_chunk_backward_workspace_bytes(1, 8192, 32, 128, 128, kda.KDA_BF16)
+    extra = 32 * 256 * 128 * 128 * 4
+    assert extra <= n2 - n <= extra + (1 << 20)
+    assert kda.kda_chunk_backward_workspace_bytes(0, 64, 2, 32, 32, kda.KDA_F32) == 0
+    assert kda.kda_chunk_backward_workspace_bytes(1, 64, 2, 64, 64, kda.KDA_F32) == 0
