@@ -127,9 +127,10 @@ kda_status kda_chunk_prefill(const void *q, const void *k, const void *v,
 
 /* Bytes of device workspace kda_chunk_backward needs for these sizes (0 for
  * arguments it would reject).  It holds the state at the start of every
- * 16-token chunk (B * H * ceil(T / 16) * d_k * d_v * 4 bytes), one state per
- * (b, h) carried between launches, and partial sums of one segment of the
- * sequence (at most about 256 MiB, or one 64-token block). */
+ * 16-token chunk (B * H * ceil(T / 16) * d_k * d_v * 4 bytes), the delta-rule
+ * correction v - S'^T k of every token (B * T * H * d_v * 4 bytes), one state
+ * per (b, h) carried between launches, and partial sums of one segment of
+ * the sequence (at most about 256 MiB, or one 16-token block). */
 size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
                                           kda_dtype dt);
 

@@ -19,15 +19,19 @@
 // j of S sees only v_j), so the work splits over (b, h, block of 8 value
 // columns) workgroups with no exchange between them; only the row sums over
 // columns (dq, dk, dg) and dbeta need the blocks together, and they are
-// summed afterwards in a fixed order.  A workgroup has d_k threads, thread c
-// owning key row c of the 8 columns in registers, so every reduction over
-// value columns stays in the thread and the one over key rows (S'^T k in the
-// forward, dS^T k in the reverse) is a wave reduce-scatter plus an exchange of
-// the per-wave sums through LDS: one workgroup barrier per token.
+// summed afterwards in a fixed order.  A workgroup is one wave (64 lanes; 32
+// for d_k = 32), lane l owning key rows RPT l .. RPT l + RPT - 1 of the 8
+// columns in registers (RPT = d_k / 64, or 1), so every reduction over value
+// columns stays in the lane and the one over key rows (dS^T k in the
+// reverse, S'^T k in the forward) is a wave reduce-scatter by DPP row and
+// half-row mirrors and quad permutes, two cross-row swaps and eight
+// readlanes: no workgroup barrier and no LDS round trip per token.
 //   bwd_ckpt_kernel   forward over the sequence, storing the state slice at
-//                     the start of each 16-token chunk (HBM checkpoints).
+//                     the start of each 16-token chunk and the delta-rule
+//                     correction u = v - S'^T k of every token (HBM).
 //   bwd_seg_kernel    per chunk, last to first: recompute the chunk's states
-//                     from its checkpoint into LDS, then sweep it in reverse;
+//                     from its checkpoint and the stored u (no reduction),
+//                     keeping them in LDS, then sweep the chunk in reverse;
 //                     writes dv and per-block partials of dq, dk, dg, dbeta.
 //                     Runs over segments of the sequence (last first), the
 //                     state gradient carried between launches, so that the
@@ -35,10 +39,11 @@
 //   bwd_finalize_kernel  sums the partials over column blocks, applies the
 //                     gate derivative (dz) and forms per-token-block dA terms.
 //   bwd_dA_kernel     sums the dA terms of each head in a fixed order.
-// The sweep is a serial chain of VALU work and workgroup barriers per token
-// (no contraction wide enough for MFMA: per token each thread does O(8) FMAs
-// per product); it is bounded by latency, with HBM traffic for inputs, the
-// checkpoints and the partials.
+// Inputs of a chunk are loaded into registers one chunk ahead and parked in
+// LDS, so the per-token chain never waits on HBM.  The sweep is a serial
+// chain of VALU work per token (no contraction wide enough for MFMA: per
+// token a lane does O(16) FMAs per product); it is bounded by latency, with
+// HBM traffic for inputs, checkpoints, u and the partials.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -46,13 +51,12 @@ namespace kda {
 
 template <int D>
 struct BwdGeom {
-    static constexpr int N = kBwdCols;         // value columns per workgroup
-    static constexpr int NT = D;               // threads: one per key row
-    static constexpr int NCB = D / N;          // column blocks per head
-    static constexpr int W = NT < kWave ? NT : kWave;   // lanes of a wave in use
-    static constexpr int NW = NT / W;          // waves
-    static_assert(N == 8, "row pieces of 8 values");
-    static_assert(N <= W, "one reduced column per group of W / N lanes");
+    static constexpr int N = kBwdCols;                  // value columns per workgroup
+    static constexpr int W = D < kWave ? D : kWave;     // threads: one wave
+    static constexpr int RPT = D / W;                   // key rows per thread
+    static constexpr int NCB = D / N;                   // column blocks per head
+    static_assert(N == 8, "the reduction hands out 8 columns over lanes 0, 2, .., 14");
+    static_assert(W >= 16, "the reduction works on whole DPP rows of 16 lanes");
 };
 
 // ------------------------------------------------------------------ helpers
@@ -92,95 +96,208 @@ __device__ __forceinline__ void store8f(float* p, const float (&x)[8]) {
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
-// Reduce-scatter of N values over the W lanes of a wave: at each step a lane
-// keeps half of its values and adds the partner's copy of that half (the
-// partner keeps the other half); once one value is left the remaining lane
-// masks complete the sum.  Afterwards lane l holds the wave's sum of value
-// (l mod W) / (W / N).
-template <int W, int N, int M>
-__device__ __forceinline__ void wave_rs(float* w, int lane) {
-    if constexpr (N > 1) {
-        const bool up = (lane & M) != 0;
+// R consecutive elements of a row-major vector, moved as one access.
+template <typename E, int R>
+struct alignas(sizeof(E) * R) Rows {
+    E x[R];
+};
+
+// Value of the lane given by a DPP control inside each row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowMirror = 0x140;       // lane i <- lane 15 - i of its row (i ^ 15)
+constexpr int kDppRowHalfMirror = 0x141;   // lane i <- lane 7 - i of its half-row (i ^ 7)
+constexpr int kDppQuadXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+
+// Sum over the W lanes of a wave of 8 per-lane values; every lane receives all
+// 8 sums (wave-uniform).  Reduce-scatter: each step pairs a lane with one
+// holding the same columns, the lane keeps half of them and adds the
+// partner's copy of that half.  Partners i ^ 15, i ^ 7, i ^ 2 (bits 3, 2, 1
+// select the kept half) cover 8 distinct lanes; i ^ 1 completes the row of
+// 16, the cross-row swaps the wave.  Lane 2j then holds the sum of column j
+// (j = 4 bit3 + 2 bit2 + bit1), which readlane broadcasts.
+template <int W>
+__device__ __forceinline__ void wave_sum8(const float (&part)[8], float (&out)[8]) {
+    const int lane = (int)threadIdx.x & (W - 1);
+    float a[4], b[2];
+    const bool u3 = (lane & 8) != 0, u2 = (lane & 4) != 0, u1 = (lane & 2) != 0;
 #pragma unroll
-        for (int i = 0; i < N / 2; ++i) {
-            const float send = up ? w[i] : w[i + N / 2];
-            const float keep = up ? w[i + N / 2] : w[i];
-            w[i] = keep + __shfl_xor(send, M, W);
+    for (int i = 0; i < 4; ++i)
+        a[i] = (u3 ? part[i + 4] : part[i]) + dpp<kDppRowMirror>(u3 ? part[i] : part[i + 4]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        b[i] = (u2 ? a[i + 2] : a[i]) + dpp<kDppRowHalfMirror>(u2 ? a[i] : a[i + 2]);
+    float c = (u1 ? b[1] : b[0]) + dpp<kDppQuadXor2>(u1 ? b[0] : b[1]);
+    c += dpp<kDppQuadXor1>(c);
+    if constexpr (W > 16) c += __shfl_xor(c, 16, W);
+    if constexpr (W > 32) c += __shfl_xor(c, 32, W);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        out[j] = __builtin_bit_cast(float,
+                                    __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 2 * j));
+}
+
+// ------------------------------------------------------------------ staging
+
+// One chunk's inputs for one workgroup, loaded into registers a chunk ahead of
+// use and parked in LDS at the chunk's start.  Lane l holds its key rows' z,
+// k (and q) for the chunk's tokens; lane r < 16 holds token r's 8-column
+// slices of the shared vectors (v in the forward; u and dO in the reverse)
+// and its beta.  Tokens past T read as zero.
+template <typename E, int R, bool REV>
+struct Stage {
+    Rows<E, R> z[kChunk], k[kChunk], q[REV ? kChunk : 1];
+    float x[8], dO[8], beta;
+};
+
+// The LDS side: z, k, q are private to their lane (lane l reads back only
+// entry l); the shared vectors and beta are double-buffered by chunk parity.
+template <typename E, int R, int W, bool REV>
+struct StageLds {
+    Rows<E, R> z[kChunk][W], k[kChunk][W], q[REV ? kChunk : 1][W];
+    float x[2][kChunk][8], dO[2][REV ? kChunk : 1][8], beta[2][kChunk];
+};
+
+// x8 points at the shared vector of the chunk's first token for this
+// column block (v, or u), with a stride of xstride elements per token.
+template <typename E, typename X, int D, bool REV>
+__device__ __forceinline__ void stage_load(Stage<E, BwdGeom<D>::RPT, REV>& s,
+                                           const E* __restrict__ q, const E* __restrict__ k,
+                                           const E* __restrict__ z,
+                                           const float* __restrict__ beta,
+                                           const E* __restrict__ dO, const X* __restrict__ x8,
+                                           size_t xstride, int b, int h, int T, int H, int cb,
+                                           int cs) {
+    using G = BwdGeom<D>;
+    constexpr int R = G::RPT;
+    const int l = (int)threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < kChunk; ++r) {
+        const int t = cs + r;
+        const size_t i = (((size_t)b * T + t) * H + h) * D + R * l;
+        if (t < T) {
+            s.z[r] = *reinterpret_cast<const Rows<E, R>*>(z + i);
+            s.k[r] = *reinterpret_cast<const Rows<E, R>*>(k + i);
+            if constexpr (REV) s.q[r] = *reinterpret_cast<const Rows<E, R>*>(q + i);
+        } else {
+#pragma unroll
+            for (int e = 0; e < R; ++e) {
+                s.z[r].x[e] = from_f32<E>(0.f);
+                s.k[r].x[e] = from_f32<E>(0.f);
+                if constexpr (REV) s.q[r].x[e] = from_f32<E>(0.f);
+            }
         }
-        wave_rs<W, N / 2, M / 2>(w, lane);
-    } else if constexpr (M >= 1) {
-        w[0] += __shfl_xor(w[0], M, W);
-        wave_rs<W, 1, M / 2>(w, lane);
+    }
+    if (l < kChunk) {
+        const int t = cs + l;
+        if (t < T) {
+            const size_t row = ((size_t)b * T + t) * H + h;
+            load8(x8 + (size_t)l * xstride, s.x);
+            if constexpr (REV) load8(dO + row * D + cb * kBwdCols, s.dO);
+            s.beta = beta[row];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s.x[j] = s.dO[j] = 0.f;
+            s.beta = 0.f;
+        }
     }
 }
 
-// Sum over the workgroup's key rows (threads) of N per-thread values, result
-// in every thread.  wsum is a double buffer of per-wave sums; par alternates
-// so that one barrier per call suffices (a buffer is rewritten only after the
-// next call's barrier, which every reader of its previous contents has passed).
-template <int D>
-__device__ __forceinline__ void rows_sum(const float (&part)[kBwdCols], float (&out)[kBwdCols],
-                                         float (*wsum)[BwdGeom<D>::NW][kBwdCols], int& par) {
-    using G = BwdGeom<D>;
-    constexpr int N = G::N, W = G::W, NW = G::NW, GL = W / N;
-    float w[N];
+template <typename E, int R, int W, bool REV>
+__device__ __forceinline__ void stage_store(const Stage<E, R, REV>& s, StageLds<E, R, W, REV>& L,
+                                            int buf) {
+    const int l = (int)threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < N; ++i) w[i] = part[i];
-    const int lane = (int)threadIdx.x & (W - 1), wave = (int)threadIdx.x / W;
-    wave_rs<W, N, W / 2>(w, lane);
-    if (lane % GL == 0) wsum[par][wave][lane / GL] = w[0];
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-        float s = wsum[par][0][j];
-#pragma unroll
-        for (int x = 1; x < NW; ++x) s += wsum[par][x][j];
-        out[j] = s;
+    for (int r = 0; r < kChunk; ++r) {
+        L.z[r][l] = s.z[r];
+        L.k[r][l] = s.k[r];
+        if constexpr (REV) L.q[r][l] = s.q[r];
     }
-    par ^= 1;
+    if (l < kChunk) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            L.x[buf][l][j] = s.x[j];
+            if constexpr (REV) L.dO[buf][l][j] = s.dO[j];
+        }
+        L.beta[buf][l] = s.beta;
+    }
 }
 
 // ------------------------------------------------------------------ kernels
 
-// Forward over the whole sequence; the state slice of each chunk's start goes
-// to ckpt[(u * NCB + cb) * NC + n] (D x 8 floats, row-major).
+// Forward over the whole sequence.  The state slice of each chunk's start
+// goes to ckpt[(u * NCB + cb) * NC + n] (D x 8 floats, row-major), the
+// correction u of token t to ucor[((u * NCB + cb) * T + t) * 8].
 template <typename E, int D>
-__global__ __launch_bounds__(D) void bwd_ckpt_kernel(
+__global__ __launch_bounds__(BwdGeom<D>::W) void bwd_ckpt_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ z,
     const float* __restrict__ beta, const float* __restrict__ A, float g_min,
-    const float* __restrict__ S0, float* __restrict__ ckpt, int B, int T, int H) {
+    const float* __restrict__ S0, float* __restrict__ ckpt, float* __restrict__ ucor, int B,
+    int T, int H) {
     using G = BwdGeom<D>;
-    constexpr int N = G::N;
-    __shared__ float wsum[2][G::NW][N];
-    const int c = (int)threadIdx.x;
+    constexpr int N = G::N, R = G::RPT, W = G::W;
+    __shared__ StageLds<E, R, W, false> sl;
+    const int l = (int)threadIdx.x;
     const int cb = (int)(blockIdx.x % G::NCB);
     const size_t u = blockIdx.x / G::NCB;
     const int b = (int)(u / (size_t)H), h = (int)(u % (size_t)H);
     const int NC = (T + kChunk - 1) / kChunk;
     const GateConsts gc = make_gate(A[h], g_min);
-    float S[N];
-    if (S0) load8f(S0 + (u * D + c) * D + cb * N, S);
-    else
+    float S[R][N];
 #pragma unroll
-        for (int j = 0; j < N; ++j) S[j] = 0.f;
-    float* ck = ckpt + (u * G::NCB + cb) * (size_t)NC * (D * N) + c * N;
-    int par = 0;
-    for (int t = 0; t < T; ++t) {
-        if (t % kChunk == 0) store8f(ck + (size_t)(t / kChunk) * (D * N), S);
-        const size_t row = ((size_t)b * T + t) * H + h;
-        const float a = gate_alpha(gc, gate_sigmoid(gc, to_f32(z[row * D + c])));
-        const float kc = to_f32(k[row * D + c]);
-        float Sp[N], part[N], p[N], vv[N];
+    for (int i = 0; i < R; ++i) {
+        if (S0) load8f(S0 + (u * D + R * l + i) * D + cb * N, S[i]);
+        else
 #pragma unroll
-        for (int j = 0; j < N; ++j) {
-            Sp[j] = a * S[j];
-            part[j] = kc * Sp[j];
+            for (int j = 0; j < N; ++j) S[i][j] = 0.f;
+    }
+    float* ck = ckpt + (u * G::NCB + cb) * (size_t)NC * (D * N) + (R * l) * N;
+    float* uc = ucor + (u * G::NCB + cb) * (size_t)T * N;
+    const size_t vstride = (size_t)H * D;     // elements between tokens of a head
+    const E* vb = v + ((size_t)b * T * H + h) * D + cb * N;
+    Stage<E, R, false> st;
+    stage_load<E, E, D, false>(st, nullptr, k, z, beta, nullptr, vb, vstride, b, h, T, H, cb, 0);
+    for (int n = 0; n < NC; ++n) {
+        const int buf = n & 1;
+        stage_store(st, sl, buf);
+        if (n + 1 < NC)
+            stage_load<E, E, D, false>(st, nullptr, k, z, beta, nullptr,
+                                       vb + (size_t)(n + 1) * kChunk * vstride, vstride, b, h, T,
+                                       H, cb, (n + 1) * kChunk);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < R; ++i) store8f(ck + (size_t)n * (D * N) + i * N, S[i]);
+        const int L = min(kChunk, T - n * kChunk);
+        for (int r = 0; r < L; ++r) {
+            const Rows<E, R> zr = sl.z[r][l], kr = sl.k[r][l];
+            float kc[R], part[N], p[N];
+#pragma unroll
+            for (int j = 0; j < N; ++j) part[j] = 0.f;
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float a = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
+                kc[i] = to_f32(kr.x[i]);
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    S[i][j] *= a;
+                    part[j] += kc[i] * S[i][j];
+                }
+            }
+            wave_sum8<W>(part, p);
+            const float bt = sl.beta[buf][r];
+            float uu[N];
+#pragma unroll
+            for (int j = 0; j < N; ++j) uu[j] = sl.x[buf][r][j] - p[j];
+            if (l == 0) store8f(uc + (size_t)(n * kChunk + r) * N, uu);
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int j = 0; j < N; ++j) S[i][j] += kc[i] * bt * uu[j];
         }
-        rows_sum<D>(part, p, wsum, par);
-        load8(v + row * D + cb * N, vv);
-        const float kb = kc * beta[row];
-#pragma unroll
-        for (int j = 0; j < N; ++j) S[j] = Sp[j] + kb * (vv[j] - p[j]);
     }
 }
 
@@ -189,124 +306,150 @@ __global__ __launch_bounds__(D) void bwd_ckpt_kernel(
 // (t1 == T) or the carry of the previous launch, and ends in dS0 (t0 == 0)
 // or the carry.  Partials are indexed by the token's place in the segment.
 template <typename E, int D>
-__global__ __launch_bounds__(D) void bwd_seg_kernel(
-    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
-    float g_min, const E* __restrict__ dO, const float* __restrict__ dST,
-    const float* __restrict__ ckpt, float* __restrict__ carry, float* __restrict__ dS0,
+__global__ __launch_bounds__(BwdGeom<D>::W) void bwd_seg_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ z,
+    const float* __restrict__ beta, const float* __restrict__ A, float g_min,
+    const E* __restrict__ dO, const float* __restrict__ dST, const float* __restrict__ ckpt,
+    const float* __restrict__ ucor, float* __restrict__ carry, float* __restrict__ dS0,
     E* __restrict__ dv, float* __restrict__ pq, float* __restrict__ pk, float* __restrict__ pg,
     float* __restrict__ pb, int B, int T, int H, int t0, int t1, int seg) {
     using G = BwdGeom<D>;
-    constexpr int N = G::N;
-    // hist[r][i][c]: the state slice before token r of the chunk, thread c's
-    // row, values 4i..4i+3 (each thread reads back only its own row)
-    __shared__ f32x4 hist[kChunk][N / 4][D];
-    __shared__ float ubuf[kChunk][N];           // u = v - S'^T k per token
-    __shared__ float wsum[2][G::NW][N];
-    const int c = (int)threadIdx.x;
+    constexpr int N = G::N, R = G::RPT, W = G::W;
+    // hist[r][m][l]: the state slice before token r of the chunk, lane l's
+    // rows, values 4m .. 4m+3 of row R l + m / 2 (lane l reads back only its own)
+    __shared__ f32x4 hist[kChunk][R * N / 4][W];
+    __shared__ StageLds<E, R, W, true> sl;
+    const int l = (int)threadIdx.x;
     const int cb = (int)(blockIdx.x % G::NCB);
     const size_t u = blockIdx.x / G::NCB;
     const int b = (int)(u / (size_t)H), h = (int)(u % (size_t)H);
     const int NC = (T + kChunk - 1) / kChunk;
     const GateConsts gc = make_gate(A[h], g_min);
-    const size_t slice = (u * D + c) * D + cb * N;           // [b, h, c, cb * N]
-    float dS[N];
-    if (t1 == T) {
-        if (dST) load8f(dST + slice, dS);
-        else
+    float dS[R][N];
 #pragma unroll
-            for (int j = 0; j < N; ++j) dS[j] = 0.f;
-    } else {
-        load8f(carry + slice, dS);
+    for (int i = 0; i < R; ++i) {
+        const size_t slice = (u * D + R * l + i) * D + cb * N;   // [b, h, row, cb * N]
+        if (t1 == T) {
+            if (dST) load8f(dST + slice, dS[i]);
+            else
+#pragma unroll
+                for (int j = 0; j < N; ++j) dS[i][j] = 0.f;
+        } else {
+            load8f(carry + slice, dS[i]);
+        }
     }
-    const float* ck = ckpt + (u * G::NCB + cb) * (size_t)NC * (D * N) + c * N;
-    int par = 0;
-    for (int n = (t1 - 1) / kChunk; n >= t0 / kChunk; --n) {
+    const float* ck = ckpt + (u * G::NCB + cb) * (size_t)NC * (D * N) + (R * l) * N;
+    const float* uc = ucor + (u * G::NCB + cb) * (size_t)T * N;
+    const int n_hi = (t1 - 1) / kChunk, n_lo = t0 / kChunk;
+    Stage<E, R, true> st;
+    stage_load<E, float, D, true>(st, q, k, z, beta, dO, uc + (size_t)n_hi * kChunk * N, N, b, h,
+                                  T, H, cb, n_hi * kChunk);
+    for (int n = n_hi; n >= n_lo; --n) {
         const int cs = n * kChunk;
         const int L = min(kChunk, T - cs);
-        float S[N];
-        load8f(ck + (size_t)n * (D * N), S);
-        // recompute the chunk's states
+        const int buf = n & 1;
+        stage_store(st, sl, buf);
+        if (n > n_lo)
+            stage_load<E, float, D, true>(st, q, k, z, beta, dO, uc + (size_t)(cs - kChunk) * N,
+                                          N, b, h, T, H, cb, cs - kChunk);
+        __syncthreads();
+        float S[R][N];
+#pragma unroll
+        for (int i = 0; i < R; ++i) load8f(ck + (size_t)n * (D * N) + i * N, S[i]);
+        // recompute the chunk's states from the stored corrections
         for (int r = 0; r < L; ++r) {
 #pragma unroll
-            for (int i = 0; i < N / 4; ++i)
-                hist[r][i][c] = f32x4{S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]};
-            const size_t row = ((size_t)b * T + cs + r) * H + h;
-            const float a = gate_alpha(gc, gate_sigmoid(gc, to_f32(z[row * D + c])));
-            const float kc = to_f32(k[row * D + c]);
-            float Sp[N], part[N], p[N], vv[N];
+            for (int i = 0; i < R; ++i)
 #pragma unroll
-            for (int j = 0; j < N; ++j) {
-                Sp[j] = a * S[j];
-                part[j] = kc * Sp[j];
-            }
-            rows_sum<D>(part, p, wsum, par);
-            load8(v + row * D + cb * N, vv);
-            const float kb = kc * beta[row];
+                for (int m = 0; m < N / 4; ++m)
+                    hist[r][i * (N / 4) + m][l] =
+                        f32x4{S[i][4 * m], S[i][4 * m + 1], S[i][4 * m + 2], S[i][4 * m + 3]};
+            const Rows<E, R> zr = sl.z[r][l], kr = sl.k[r][l];
+            const float bt = sl.beta[buf][r];
 #pragma unroll
-            for (int j = 0; j < N; ++j) {
-                const float uj = vv[j] - p[j];
-                if (c == 0) ubuf[r][j] = uj;
-                S[j] = Sp[j] + kb * uj;
+            for (int i = 0; i < R; ++i) {
+                const float a = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
+                const float kb = to_f32(kr.x[i]) * bt;
+#pragma unroll
+                for (int j = 0; j < N; ++j) S[i][j] = a * S[i][j] + kb * sl.x[buf][r][j];
             }
         }
-        __syncthreads();   // ubuf of the last token
         // reverse sweep
         for (int r = L - 1; r >= 0; --r) {
             const int t = cs + r;
-            const size_t row = ((size_t)b * T + t) * H + h;
-            const float a = gate_alpha(gc, gate_sigmoid(gc, to_f32(z[row * D + c])));
-            const float kc = to_f32(k[row * D + c]);
-            const float qc = to_f32(q[row * D + c]);
-            const float bt = beta[row];
-            float Sprev[N], uu[N], dov[N], Sp[N], part[N], de[N];
-#pragma unroll
-            for (int i = 0; i < N / 4; ++i) {
-                const f32x4 x = hist[r][i][c];
-                Sprev[4 * i] = x[0];
-                Sprev[4 * i + 1] = x[1];
-                Sprev[4 * i + 2] = x[2];
-                Sprev[4 * i + 3] = x[3];
-            }
-#pragma unroll
-            for (int j = 0; j < N; ++j) uu[j] = ubuf[r][j];
-            load8(dO + row * D + cb * N, dov);
-            float dqc = 0.f;
+            const Rows<E, R> zr = sl.z[r][l], kr = sl.k[r][l], qr = sl.q[r][l];
+            const float bt = sl.beta[buf][r];
+            float uu[N], dov[N], part[N], de[N];
 #pragma unroll
             for (int j = 0; j < N; ++j) {
-                Sp[j] = a * Sprev[j];
-                const float Scur = Sp[j] + kc * bt * uu[j];
-                dS[j] += qc * dov[j];
-                dqc += Scur * dov[j];
-                part[j] = kc * dS[j];
+                uu[j] = sl.x[buf][r][j];
+                dov[j] = sl.dO[buf][r][j];
+                part[j] = 0.f;
             }
-            rows_sum<D>(part, de, wsum, par);
-            float dkc = 0.f, dac = 0.f, db = 0.f;
+            float a[R], kc[R], Sprev[R][N], Sp[R][N], dqc[R];
 #pragma unroll
-            for (int j = 0; j < N; ++j) {
-                dkc += bt * (dS[j] * uu[j] - Sp[j] * de[j]);
-                const float dSp = dS[j] - kc * bt * de[j];
-                dac += dSp * Sprev[j];
-                dS[j] = a * dSp;
-                db += de[j] * uu[j];
+            for (int i = 0; i < R; ++i) {
+                a[i] = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
+                kc[i] = to_f32(kr.x[i]);
+                const float qc = to_f32(qr.x[i]);
+#pragma unroll
+                for (int m = 0; m < N / 4; ++m) {
+                    const f32x4 x = hist[r][i * (N / 4) + m][l];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Sprev[i][4 * m + e] = x[e];
+                }
+                dqc[i] = 0.f;
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    Sp[i][j] = a[i] * Sprev[i][j];
+                    const float Scur = Sp[i][j] + kc[i] * bt * uu[j];
+                    dS[i][j] += qc * dov[j];
+                    dqc[i] += Scur * dov[j];
+                    part[j] += kc[i] * dS[i][j];
+                }
+            }
+            wave_sum8<W>(part, de);
+            float dkc[R], dgc[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                float dk_ = 0.f, da_ = 0.f;
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    dk_ += bt * (dS[i][j] * uu[j] - Sp[i][j] * de[j]);
+                    const float dSp = dS[i][j] - kc[i] * bt * de[j];
+                    da_ += dSp * Sprev[i][j];
+                    dS[i][j] = a[i] * dSp;
+                }
+                dkc[i] = dk_;
+                dgc[i] = da_ * a[i];
             }
             const size_t prow = (((size_t)cb * B + b) * seg + (t - t0)) * H + h;
-            pq[prow * D + c] = dqc;
-            pk[prow * D + c] = dkc;
-            pg[prow * D + c] = dac * a;
-            if (c == 0) {
-                pb[prow] = db;
-                float dvv[N];
+            *reinterpret_cast<Rows<float, R>*>(pq + prow * D + R * l) =
+                *reinterpret_cast<const Rows<float, R>*>(dqc);
+            *reinterpret_cast<Rows<float, R>*>(pk + prow * D + R * l) =
+                *reinterpret_cast<const Rows<float, R>*>(dkc);
+            *reinterpret_cast<Rows<float, R>*>(pg + prow * D + R * l) =
+                *reinterpret_cast<const Rows<float, R>*>(dgc);
+            if (l == 0) {
+                float db = 0.f, dvv[N];
 #pragma unroll
-                for (int j = 0; j < N; ++j) dvv[j] = bt * de[j];
-                store8(dv + row * D + cb * N, dvv);
+                for (int j = 0; j < N; ++j) {
+                    db += de[j] * uu[j];
+                    dvv[j] = bt * de[j];
+                }
+                pb[prow] = db;
+                store8(dv + (((size_t)b * T + t) * H + h) * D + cb * N, dvv);
             }
         }
     }
-    if (t0 == 0) {
-        if (dS0) store8f(dS0 + slice, dS);
-    } else {
-        store8f(carry + slice, dS);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const size_t slice = (u * D + R * l + i) * D + cb * N;
+        if (t0 == 0) {
+            if (dS0) store8f(dS0 + slice, dS[i]);
+        } else {
+            store8f(carry + slice, dS[i]);
+        }
     }
 }
 
@@ -411,6 +554,7 @@ BwdLayout bwd_layout(int B, int T, int H, int d) {
     };
     L.ckpt = take(units * L.NC * (size_t)d * d * sizeof(float));
     L.carry = take(units * (size_t)d * d * sizeof(float));
+    L.ucor = take(units * (size_t)T * d * sizeof(float));
     const size_t pel = (size_t)NCB * units * seg;   // partial rows
     L.pq = take(pel * d * sizeof(float));
     L.pk = take(pel * d * sizeof(float));
@@ -428,6 +572,7 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
     const size_t units = (size_t)a.B * a.H;
     float* ckpt = (float*)(ws + L.ckpt);
     float* carry = (float*)(ws + L.carry);
+    float* ucor = (float*)(ws + L.ucor);
     float* pq = (float*)(ws + L.pq);
     float* pk = (float*)(ws + L.pk);
     float* pg = (float*)(ws + L.pg);
@@ -437,15 +582,15 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
     const E* k = (const E*)a.k;
     const E* v = (const E*)a.v;
     const E* z = (const E*)a.z;
-    const dim3 grid((unsigned)(units * G::NCB)), block(D);
+    const dim3 grid((unsigned)(units * G::NCB)), block(G::W);
     hipLaunchKernelGGL((bwd_ckpt_kernel<E, D>), grid, block, 0, stream, k, v, z, a.beta, a.A,
-                       a.g_min, a.S0, ckpt, a.B, a.T, a.H);
+                       a.g_min, a.S0, ckpt, ucor, a.B, a.T, a.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int t1 = a.T; t1 > 0;) {
         const int t0 = ((t1 - 1) / L.seg) * L.seg;
-        hipLaunchKernelGGL((bwd_seg_kernel<E, D>), grid, block, 0, stream, q, k, v, z, a.beta,
-                           a.A, a.g_min, (const E*)a.dO, a.dST, ckpt, carry, a.dS0, (E*)a.dv, pq,
+        hipLaunchKernelGGL((bwd_seg_kernel<E, D>), grid, block, 0, stream, q, k, z, a.beta, a.A,
+                           a.g_min, (const E*)a.dO, a.dST, ckpt, ucor, carry, a.dS0, (E*)a.dv, pq,
                            pk, pg, pb, a.B, a.T, a.H, t0, t1, L.seg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int n_tok = t1 - t0;

@@ -92,12 +92,12 @@ struct BackwardArgs {
 // Backward geometry: value columns per workgroup, tokens per finalize block,
 // and the bound on the per-segment partial sums in the workspace.
 constexpr int kBwdCols = 8;
-constexpr int kBwdTokBlock = 64;
+constexpr int kBwdTokBlock = 16;
 constexpr size_t kBwdPartialBudget = (size_t)256 << 20;
 
 // Byte offsets of the backward workspace regions (each 256-byte aligned).
 struct BwdLayout {
-    size_t ckpt, carry, pq, pk, pg, pb, dA_part, total;
+    size_t ckpt, carry, ucor, pq, pk, pg, pb, dA_part, total;
     int seg;     // tokens per reverse-sweep launch (multiple of kBwdTokBlock)
     int NC;      // chunks (checkpoints) per sequence
     int ntb;     // finalize token blocks per sequence
