@@ -373,7 +373,9 @@ def main():
             "config": {"workload": f"backward_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T, "H": H,
                        "d_k": d, "d_v": d, "workspace_bytes": nbw},
             "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bgbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": bgbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("backward_mid_pass_bytes"),
+                         "traffic_unit": "bytes per pass",
                          "kernel": "backward pass (bwd_ckpt_kernel + bwd_seg_kernel + "
                                    "bwd_finalize_kernel + bwd_dA_kernel)",
                          "alg_bytes_per_step": bb},
