@@ -95,9 +95,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--verify-tokens", type=int, default=4,
                     help="drafted tokens per sequence in the verify-step measurement (1..16)")
-    ap.add_argument("--workload", choices=["mid", "batched"], default="mid",
+    ap.add_argument("--workload", choices=["mid", "batched", "long"], default="mid",
                     help="prefill workload: mid = B1 H32 T4096 (the headline), "
-                         "batched = B8 H32 T32768 with a carried state")
+                         "batched = B8 H32 T32768 with a carried state, "
+                         "long = B1 H32 T1048576 (one million-token sequence)")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--plan", default=None,
@@ -119,7 +120,7 @@ def main():
 
     dev = torch.device("cuda:0")
     kda.lib()
-    cfg_index = 1 if args.workload == "mid" else 2
+    cfg_index = {"mid": 1, "batched": 2, "long": 3}[args.workload]
     cfg = PREFILL_CONFIGS[cfg_index]
     B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.dk
     x = config_inputs(cfg_index, dev)
