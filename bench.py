@@ -99,6 +99,9 @@ def main():
                     help="prefill workload: mid = B1 H32 T4096 (the headline), "
                          "batched = B8 H32 T32768 with a carried state, "
                          "long = B1 H32 T1048576 (one million-token sequence)")
+    ap.add_argument("--segments", type=int, default=1,
+                    help="prefill by a scan over this many segments of each sequence "
+                         "(kda_chunk_prefill_segmented); 1 = the direct chunkwise prefill")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--plan", default=None,
@@ -126,7 +129,11 @@ def main():
     x = config_inputs(cfg_index, dev)
     o = torch.empty(B, T, H, d, dtype=cfg.dtype, device=dev)
     ST = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
-    nb = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, cfg.dtype)
+    if args.segments > 1:
+        nb = kda.kda_chunk_prefill_segmented_workspace_bytes(B, T, H, d, d, args.segments,
+                                                             cfg.dtype)
+    else:
+        nb = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, cfg.dtype)
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
     stream = torch.cuda.current_stream()
     # Cold inputs without a flush kernel: the steps cycle through n_rot copies
@@ -141,8 +148,13 @@ def main():
 
     def step(i):
         xi = xs[i % n_rot]
-        kda.kda_chunk_prefill(xi["q"], xi["k"], xi["v"], xi["z"], xi["beta"], xi["A"], xi["g_min"],
-                              xi["S0"], o, ST, ws, stream)
+        if args.segments > 1:
+            kda.kda_chunk_prefill_segmented(xi["q"], xi["k"], xi["v"], xi["z"], xi["beta"],
+                                            xi["A"], xi["g_min"], xi["S0"], o, ST, args.segments,
+                                            ws, stream)
+        else:
+            kda.kda_chunk_prefill(xi["q"], xi["k"], xi["v"], xi["z"], xi["beta"], xi["A"],
+                                  xi["g_min"], xi["S0"], o, ST, ws, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -207,13 +219,18 @@ def main():
         "config": {"workload": f"{args.workload}_prefill_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T,
                    "H": H, "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": -5.0,
                    "S0": "zeros" if x["S0"] is None else "N(0, 0.01)",
-                   "parallelism": "single GPU", "plan": "split" if nb else "fused",
+                   "parallelism": "single GPU",
+                   "plan": (f"segment scan over {args.segments} segments" if args.segments > 1
+                            else ("split" if nb else "fused")),
                    "workspace_bytes": nb},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(f"prefill_{args.workload}_pass_bytes_{'split' if nb else 'fused'}"),
+                     "traffic": (None if args.segments > 1 else measured_traffic(
+                         f"prefill_{args.workload}_pass_bytes_{'split' if nb else 'fused'}")),
                      "traffic_unit": "bytes per pass",
-                     "kernel": ("prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
+                     "kernel": ("segment-scan prefill (three prefill passes + segscan_kernel)"
+                                if args.segments > 1 else
+                                "prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
                                 else "prefill pass (fused_kernel)"),
                      "alg_bytes_per_step": alg_b,
                      "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,

@@ -125,6 +125,37 @@ kda_status kda_chunk_prefill(const void *q, const void *k, const void *v,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Bytes of device workspace kda_chunk_prefill_segmented needs (0 for
+ * arguments it would reject): the inner prefill's workspace for B * n_seg
+ * rows of T / n_seg tokens, a zero value tensor of the size of v, and four
+ * state tensors [B * n_seg, H, d_k, d_v] fp32. */
+size_t kda_chunk_prefill_segmented_workspace_bytes(int B, int T, int H, int d_k,
+                                                   int d_v, int n_seg,
+                                                   kda_dtype dt);
+
+/* kda_chunk_prefill computed by a scan over n_seg segments of T / n_seg
+ * tokens each (n_seg must divide T): the single-GPU form of the pages' KDA
+ * context parallelism (dev.to "Kimi K3 Architecture ...", section
+ * "Infrastructure and Training/Inference Mechanics": local state updates
+ * merged by a prefix scan of fixed-size states).  Each segment's state map
+ * S_end = M S_in + N comes from two prefills of all segments side by side (v
+ * = 0 from S0 = I; v from S0 = 0); a scan gives every segment's start state
+ * and S_T; a last prefill from those start states writes o.  Same arguments,
+ * layouts, aliasing rules and results (up to rounding) as kda_chunk_prefill;
+ * the chunk grid restarts at every segment start.  It costs three prefill
+ * passes plus the scan, and is the building block of a prefill split across
+ * devices by sequence position.
+ *   workspace : at least kda_chunk_prefill_segmented_workspace_bytes(...)
+ *               bytes (never NULL). */
+kda_status kda_chunk_prefill_segmented(const void *q, const void *k,
+                                       const void *v, const void *z,
+                                       const float *beta, const float *A,
+                                       float g_min, const float *S0, void *o,
+                                       float *S_T, int B, int T, int H,
+                                       int d_k, int d_v, int n_seg,
+                                       kda_dtype dt, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace kda_chunk_backward needs for these sizes (0 for
  * arguments it would reject).  It holds the state at the start of every
  * 16-token chunk (B * H * ceil(T / 16) * d_k * d_v * 4 bytes), the delta-rule

@@ -21,15 +21,20 @@ Functions named like the C entry points take torch tensors in the layouts
     kda_chunk_backward(q, k, v, z, beta, A, g_min, S0, dO, dS_T, dq, dk, dv, dz, dbeta, dA,
                        dS0, workspace, stream)
     kda_chunk_backward_workspace_bytes(B, T, H, d_k, d_v, dtype)
+    kda_chunk_prefill_segmented(q, k, v, z, beta, A, g_min, S0, o, S_T, n_seg, workspace, stream)
+    kda_chunk_prefill_segmented_workspace_bytes(B, T, H, d_k, d_v, n_seg, dtype)
 
-``chunk_prefill``, ``chunk_backward``, ``decode_step`` and ``decode_tokens`` additionally allocate the outputs (and
+``chunk_prefill``, ``chunk_prefill_segmented``, ``chunk_backward``, ``decode_step`` and
+``decode_tokens`` additionally allocate the outputs (and
 the workspace) with ``torch.empty`` before calling the same entry points.
 """
 from __future__ import annotations
 
 from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KDA_MAX_DECODE_TOKENS, KdaError,
-                   KdaLibraryMissing, abi_version, chunk_backward, chunk_prefill, decode_step,
-                   decode_tokens, kda_chunk_backward, kda_chunk_backward_workspace_bytes,
+                   KdaLibraryMissing, abi_version, chunk_backward, chunk_prefill,
+                   chunk_prefill_segmented, decode_step, decode_tokens, kda_chunk_backward,
+                   kda_chunk_backward_workspace_bytes, kda_chunk_prefill_segmented,
+                   kda_chunk_prefill_segmented_workspace_bytes,
                    kda_chunk_prefill, kda_chunk_prefill_paged, kda_chunk_prefill_workspace_bytes,
                    kda_decode_step, kda_decode_step_paged, kda_decode_tokens,
                    kda_decode_tokens_paged, kda_gate_chunk_cumsum, kda_intra_chunk, lib,
@@ -37,7 +42,8 @@ from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KDA_MAX_DECODE_TOKENS, KdaError
 
 __all__ = ["KDA_BF16", "KDA_CHUNK", "KDA_F32", "KDA_MAX_DECODE_TOKENS", "KdaError",
            "KdaLibraryMissing", "abi_version", "chunk_backward", "chunk_prefill",
-           "kda_chunk_backward", "kda_chunk_backward_workspace_bytes", "decode_step", "decode_tokens",
+           "chunk_prefill_segmented", "kda_chunk_backward", "kda_chunk_backward_workspace_bytes",
+           "kda_chunk_prefill_segmented", "kda_chunk_prefill_segmented_workspace_bytes", "decode_step", "decode_tokens",
            "kda_chunk_prefill", "kda_chunk_prefill_paged", "kda_chunk_prefill_workspace_bytes",
            "kda_decode_step", "kda_decode_step_paged", "kda_decode_tokens",
            "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk", "lib",

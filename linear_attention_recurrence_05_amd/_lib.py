@@ -49,6 +49,9 @@ _SIGNATURES = {
                               ctypes.c_int),
     "kda_decode_tokens_paged": ([_vp] * 6 + [ctypes.c_float, _vp, _i, _vp, _vp, _vp] + [_i] * 6
                                 + [_vp], ctypes.c_int),
+    "kda_chunk_prefill_segmented_workspace_bytes": ([_i] * 7, ctypes.c_size_t),
+    "kda_chunk_prefill_segmented": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 7
+                                    + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "kda_chunk_backward_workspace_bytes": ([_i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "kda_chunk_backward": ([_vp] * 6 + [ctypes.c_float] + [_vp] * 10 + [_i] * 6
                            + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
@@ -234,6 +237,39 @@ def chunk_prefill(q, k, v, z, beta, A, g_min=-5.0, S0=None, want_state=True, str
     nbytes = kda_chunk_prefill_workspace_bytes(B, T, H, dk, dv, q.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, ws, stream)
+    return o, S_T
+
+
+def kda_chunk_prefill_segmented_workspace_bytes(B, T, H, d_k, d_v, n_seg, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+    return int(lib().kda_chunk_prefill_segmented_workspace_bytes(B, T, H, d_k, d_v, n_seg, code))
+
+
+def kda_chunk_prefill_segmented(q, k, v, z, beta, A, g_min, S0, o, S_T, n_seg, workspace,
+                                stream=None):
+    """C entry point kda_chunk_prefill_segmented on torch tensors (layouts of kda.h)."""
+    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0, o=o, S_T=S_T)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kda_chunk_prefill_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta),
+                                           _ptr(A), float(g_min), _ptr(S0), _ptr(o), _ptr(S_T),
+                                           B, T, H, dk, dv, int(n_seg), _dtype_code(q),
+                                           _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "kda_chunk_prefill_segmented")
+
+
+def chunk_prefill_segmented(q, k, v, z, beta, A, n_seg, g_min=-5.0, S0=None, want_state=True,
+                            stream=None):
+    """Allocate o (and S_T, workspace) with torch.empty and run
+    kda_chunk_prefill_segmented.  Returns (o, S_T or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
+    nbytes = kda_chunk_prefill_segmented_workspace_bytes(B, T, H, dk, dv, n_seg, q.dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    kda_chunk_prefill_segmented(q, k, v, z, beta, A, g_min, S0, o, S_T, n_seg, ws, stream)
     return o, S_T
 
 

@@ -292,6 +292,56 @@ kda_status kda_decode_tokens_paged(const void* q, const void* k, const void* v, 
     return hip_status(kda::launch_tokens(a, (hipStream_t)stream), "kda_decode_tokens_paged launch");
 }
 
+size_t kda_chunk_prefill_segmented_workspace_bytes(int B, int T, int H, int d_k, int d_v,
+                                                   int n_seg, kda_dtype dt) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return 0;
+    if (!(d_k == d_v && (d_k == 32 || d_k == 128))) return 0;
+    if (B < 1 || T < 1 || H < 1 || n_seg < 1 || T % n_seg != 0 ||
+        (long long)B * n_seg * H > (1LL << 26) || (unsigned long long)B * T * H > (1ULL << 40) ||
+        (long long)H * d_k > (1LL << 24))
+        return 0;
+    return kda::seg_layout(B, T, H, d_k, dt == KDA_BF16, n_seg).total;
+}
+
+kda_status kda_chunk_prefill_segmented(const void* q, const void* k, const void* v, const void* z,
+                                       const float* beta, const float* A, float g_min,
+                                       const float* S0, void* o, float* S_T, int B, int T, int H,
+                                       int d_k, int d_v, int n_seg, kda_dtype dt, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    kda_status s = check_common(d_k, d_v, dt, g_min);
+    if (s != KDA_OK) return s;
+    size_t nel, ntok;
+    if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
+    if (n_seg < 1 || T % n_seg != 0)
+        return fail(KDA_ERR_INVALID_SHAPE, "n_seg=%d must be >= 1 and divide T=%d", n_seg, T);
+    if ((long long)B * n_seg * H > (1LL << 26))
+        return fail(KDA_ERR_INVALID_SHAPE, "B*n_seg*H = %lld is too large", (long long)B * n_seg * H);
+    const size_t need = kda::seg_layout(B, T, H, d_k, dt == KDA_BF16, n_seg).total;
+    const size_t es = dt == KDA_BF16 ? 2 : 4;
+    const size_t st_bytes = (size_t)B * H * d_k * d_v * sizeof(float);
+    const Range r[] = {{"q", q, nel * es, 16},          {"k", k, nel * es, 16},
+                       {"v", v, nel * es, 16},          {"z", z, nel * es, 16},
+                       {"beta", beta, ntok * 4, 4},     {"A", A, (size_t)H * 4, 4},
+                       {"S0", S0, st_bytes, 4},         {"o", o, nel * es, 16},
+                       {"S_T", S_T, st_bytes, 4},       {"workspace", workspace, need, 16}};
+    const bool req[] = {true, true, true, true, true, true, false, true, false, true};
+    if ((s = check_ptrs(r, 10, req)) != KDA_OK) return s;
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    for (int out : {7, 8, 9}) {
+        for (int i = 0; i < 10; ++i) {
+            if (i == out) continue;
+            if (out == 8 && i == 6 && S_T == S0) continue;
+            if (overlap(r[out], r[i]))
+                return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
+        }
+    }
+    kda::PrefillArgs a{q, k, v, z, beta, A, g_min, kda::dense_state(S0, S_T), o, B, T, H, d_k,
+                       dt == KDA_BF16};
+    return hip_status(kda::launch_segmented(a, n_seg, workspace, (hipStream_t)stream),
+                      "kda_chunk_prefill_segmented launch");
+}
+
 size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v, kda_dtype dt) {
     if (dt != KDA_F32 && dt != KDA_BF16) return 0;
     if (!(d_k == d_v && (d_k == 32 || d_k == 128))) return 0;

@@ -137,6 +137,17 @@ hipError_t launch_prefill(const PrefillArgs& a, const PlanInfo& p, void* ws, hip
 // Split plan: pair intra kernel -> workspace -> pair inter kernel, per segment.
 hipError_t launch_split(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, void* ws, hipStream_t stream);
+
+// Segment-scan prefill: the T tokens of each sequence as R segments of T / R
+// (laid side by side as B * R batch rows), the state map of each segment,
+// a scan over segments, and a last pass from the scanned start states.
+struct SegLayout {
+    PlanInfo inner;        // plan of the inner prefill calls (B * R rows of T / R)
+    size_t inner_ws, vzero, ident, M, N, Sin, total;   // byte offsets, 256-aligned
+};
+SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R);
+// a.S: dense S0 (in, may be null) and S_T (out, may be null).
+hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t stream);
 hipError_t launch_gate_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,
                               int H, int d, bool is_bf16, hipStream_t stream);
 hipError_t launch_intra_diag(const void* q, const void* k, const void* z, const float* beta,

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
               "kda_chunk_prefill_workspace_bytes", "kda_chunk_prefill", "kda_decode_step",
               "kda_decode_tokens", "kda_chunk_prefill_paged", "kda_decode_step_paged",
               "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk",
-              "kda_chunk_backward_workspace_bytes", "kda_chunk_backward"]:
+              "kda_chunk_backward_workspace_bytes", "kda_chunk_backward",
+              "kda_chunk_prefill_segmented_workspace_bytes", "kda_chunk_prefill_segmented"]:
         assert n in names
 
 
@@ -300,3 +301,40 @@ def test_backward_workspace_query():
     assert extra <= n2 - n <= extra + (1 << 20)
     assert kda.kda_chunk_backward_workspace_bytes(0, 64, 2, 32, 32, kda.KDA_F32) == 0
     assert kda.kda_chunk_backward_workspace_bytes(1, 64, 2, 64, 64, kda.KDA_F32) == 0
+
+
+def segmented(**over):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), z=fake(3), beta=fake(4), A=fake(5), g_min=-5.0,
+                S0=None, o=fake(7), S_T=fake(8), B=1, T=64, H=2, d_k=32, d_v=32, n_seg=4,
+                dt=kda.KDA_F32, ws=fake(9), ws_bytes=0, stream=None)
+    args.update(over)
+    L = kda.lib()
+    st = L.kda_chunk_prefill_segmented(*(args[n] for n in ("q", "k", "v", "z", "beta", "A",
+                                                           "g_min", "S0", "o", "S_T", "B", "T",
+                                                           "H", "d_k", "d_v", "n_seg", "dt", "ws",
+                                                           "ws_bytes", "stream")))
+    return st, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_seg=0), "KDA_ERR_INVALID_SHAPE"),
+    (dict(n_seg=5), "KDA_ERR_INVALID_SHAPE"),              # does not divide T = 64
+    (dict(ws=None), "KDA_ERR_NULL_POINTER"),
+    (dict(), "KDA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(ws_bytes=1 << 33, o=fake(2)), "KDA_ERR_ALIASING"),
+    (dict(g_min=-7.0), "KDA_ERR_INVALID_VALUE"),
+])
+def test_segmented_rejects(over, code):
+    st, detail = segmented(**over)
+    assert st == E[code], (st, detail)
+    assert detail
+
+
+def test_segmented_workspace_query():
+    n1 = kda.kda_chunk_prefill_segmented_workspace_bytes(1, 4096, 32, 128, 128, 1, kda.KDA_BF16)
+    n4 = kda.kda_chunk_prefill_segmented_workspace_bytes(1, 4096, 32, 128, 128, 4, kda.KDA_BF16)
+    # a zero value tensor of v's size, and four state tensors per segment
+    assert n1 >= 4096 * 32 * 128 * 2 + 4 * 32 * 128 * 128 * 4
+    assert n4 >= 4096 * 32 * 128 * 2 + 4 * 4 * 32 * 128 * 128 * 4
+    assert kda.kda_chunk_prefill_segmented_workspace_bytes(1, 4096, 32, 128, 128, 3,
+                                                           kda.KDA_BF16) == 0
