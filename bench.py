@@ -72,15 +72,15 @@ def decode_alg_bytes(B, H, d, es=2):
 
 
 def measured_traffic(key):
-    """HBM bytes per launch recorded under profiles/traffic.json (calibrated
-    FETCH_SIZE + WRITE_SIZE), or None if the record is missing or the kernel
-    sources changed since the counters were taken."""
+    """HBM bytes per launch (or pass) recorded under profiles/traffic.json
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None if the record is missing or
+    the kernel sources it was taken on have changed since."""
     import hashlib
     try:
-        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["records"][key]
         h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read()
                                     for s in rec["sources"])).hexdigest()[:16]
-        return rec[key] if h == rec["kernel_sources_sha256_16"] else None
+        return rec["bytes"] if h == rec["sha256_16"] else None
     except (OSError, KeyError, ValueError):
         return None
 

@@ -348,7 +348,7 @@ size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
     if (B < 1 || T < 1 || H < 1 || (long long)B * H > (1LL << 26) ||
         (unsigned long long)B * T * H > (1ULL << 40) || (long long)H * d_k > (1LL << 24))
         return 0;
-    return kda::bwd_layout(B, T, H, d_k).total;
+    return kda::bwd_layout(B, T, H, d_k, dt == KDA_BF16).total;
 }
 
 kda_status kda_chunk_backward(const void* q, const void* k, const void* v, const void* z,
@@ -361,7 +361,7 @@ kda_status kda_chunk_backward(const void* q, const void* k, const void* v, const
     if (s != KDA_OK) return s;
     size_t nel, ntok;
     if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
-    const size_t need = kda::bwd_layout(B, T, H, d_k).total;
+    const size_t need = kda::bwd_layout(B, T, H, d_k, dt == KDA_BF16).total;
     const size_t es = dt == KDA_BF16 ? 2 : 4;
     const size_t sbytes = (size_t)B * H * d_k * d_v * sizeof(float);
     const Range r[] = {{"q", q, nel * es, 16},       {"k", k, nel * es, 16},

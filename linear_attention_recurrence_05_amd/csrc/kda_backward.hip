@@ -28,7 +28,11 @@
 // readlanes: no workgroup barrier and no LDS round trip per token.
 //   bwd_ckpt_kernel   forward over the sequence, storing the state slice at
 //                     the start of each 16-token chunk and the delta-rule
-//                     correction u = v - S'^T k of every token (HBM).
+//                     correction u = v - S'^T k of every token (HBM).  When
+//                     the sequence splits into R whole-chunk segments, the
+//                     segments run side by side from their start states,
+//                     which a segment scan of the chunkwise forward supplies
+//                     (kda_segscan.hip).
 //   bwd_seg_kernel    per chunk, last to first: recompute the chunk's states
 //                     from its checkpoint and the stored u (no reduction),
 //                     keeping them in LDS, then sweep the chunk in reverse;
@@ -236,21 +240,29 @@ template <typename E, int D>
 __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_ckpt_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ z,
     const float* __restrict__ beta, const float* __restrict__ A, float g_min,
-    const float* __restrict__ S0, float* __restrict__ ckpt, float* __restrict__ ucor, int B,
-    int T, int H) {
+    const float* __restrict__ S0, const float* __restrict__ Sseg, int nseg,
+    float* __restrict__ ckpt, float* __restrict__ ucor, int B, int T, int H) {
     using G = BwdGeom<D>;
     constexpr int N = G::N, R = G::RPT, W = G::W;
     __shared__ StageLds<E, R, W, false> sl;
     const int l = (int)threadIdx.x;
     const int cb = (int)(blockIdx.x % G::NCB);
-    const size_t u = blockIdx.x / G::NCB;
+    const size_t ur = blockIdx.x / G::NCB;
+    const int sg = (int)(ur % (size_t)nseg);
+    const size_t u = ur / nseg;
     const int b = (int)(u / (size_t)H), h = (int)(u % (size_t)H);
     const int NC = (T + kChunk - 1) / kChunk;
+    // chunks [n_beg, n_end) of segment sg (whole chunks: T is a multiple of
+    // 16 nseg when nseg > 1)
+    const int n_beg = (int)((long)NC * sg / nseg), n_end = (int)((long)NC * (sg + 1) / nseg);
     const GateConsts gc = make_gate(A[h], g_min);
+    // the segment's start state: S0 for one segment, else the scanned one
+    const float* s_in = nseg > 1 ? Sseg + (((size_t)b * nseg + sg) * H + h) * (size_t)D * D
+                                 : (S0 ? S0 + u * (size_t)D * D : nullptr);
     float S[R][N];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        if (S0) load8f(S0 + (u * D + R * l + i) * D + cb * N, S[i]);
+        if (s_in) load8f(s_in + (size_t)(R * l + i) * D + cb * N, S[i]);
         else
 #pragma unroll
             for (int j = 0; j < N; ++j) S[i][j] = 0.f;
@@ -260,11 +272,13 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_ckpt_kernel(
     const size_t vstride = (size_t)H * D;     // elements between tokens of a head
     const E* vb = v + ((size_t)b * T * H + h) * D + cb * N;
     Stage<E, R, false> st;
-    stage_load<E, E, D, false>(st, nullptr, k, z, beta, nullptr, vb, vstride, b, h, T, H, cb, 0);
-    for (int n = 0; n < NC; ++n) {
+    stage_load<E, E, D, false>(st, nullptr, k, z, beta, nullptr,
+                               vb + (size_t)n_beg * kChunk * vstride, vstride, b, h, T, H, cb,
+                               n_beg * kChunk);
+    for (int n = n_beg; n < n_end; ++n) {
         const int buf = n & 1;
         stage_store(st, sl, buf);
-        if (n + 1 < NC)
+        if (n + 1 < n_end)
             stage_load<E, E, D, false>(st, nullptr, k, z, beta, nullptr,
                                        vb + (size_t)(n + 1) * kChunk * vstride, vstride, b, h, T,
                                        H, cb, (n + 1) * kChunk);
@@ -531,8 +545,17 @@ __global__ __launch_bounds__(256) void bwd_dA_kernel(const float* __restrict__ d
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-BwdLayout bwd_layout(int B, int T, int H, int d) {
+BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     BwdLayout L;
+    // The forward sweep runs as R segments side by side, each from its start
+    // state out of a segment scan, when T splits into R whole-chunk segments
+    // of at least kBwdSegMin tokens.
+    L.R = 1;
+    for (int r : {8, 4, 2})
+        if (T % (kChunk * r) == 0 && T / r >= kBwdSegMin) {
+            L.R = r;
+            break;
+        }
     const size_t units = (size_t)B * H;
     const int NCB = d / kBwdCols;
     L.NC = (T + kChunk - 1) / kChunk;
@@ -561,6 +584,11 @@ BwdLayout bwd_layout(int B, int T, int H, int d) {
     L.pg = take(pel * d * sizeof(float));
     L.pb = take(pel * sizeof(float));
     L.dA_part = take(units * L.ntb * sizeof(float));
+    L.segws = L.oscr = 0;
+    if (L.R > 1) {
+        L.segws = take(seg_layout(B, T, H, d, is_bf16, L.R).total);
+        L.oscr = take((size_t)B * T * H * d * (is_bf16 ? 2 : 4));
+    }
     L.total = off;
     return L;
 }
@@ -568,7 +596,7 @@ BwdLayout bwd_layout(int B, int T, int H, int d) {
 template <typename E, int D>
 static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t stream) {
     using G = BwdGeom<D>;
-    const BwdLayout L = bwd_layout(a.B, a.T, a.H, D);
+    const BwdLayout L = bwd_layout(a.B, a.T, a.H, D, sizeof(E) == 2);
     const size_t units = (size_t)a.B * a.H;
     float* ckpt = (float*)(ws + L.ckpt);
     float* carry = (float*)(ws + L.carry);
@@ -583,10 +611,20 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
     const E* v = (const E*)a.v;
     const E* z = (const E*)a.z;
     const dim3 grid((unsigned)(units * G::NCB)), block(G::W);
-    hipLaunchKernelGGL((bwd_ckpt_kernel<E, D>), grid, block, 0, stream, k, v, z, a.beta, a.A,
-                       a.g_min, a.S0, ckpt, ucor, a.B, a.T, a.H);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    const float* Sseg = nullptr;
+    if (L.R > 1) {
+        // start states of the R segments by the segment scan of the forward
+        const SegLayout SL = seg_layout(a.B, a.T, a.H, D, sizeof(E) == 2, L.R);
+        PrefillArgs fa{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state(a.S0, nullptr),
+                       ws + L.oscr, a.B, a.T, a.H, D, sizeof(E) == 2};
+        if ((e = seg_start_states(fa, L.R, SL, ws + L.segws, stream)) != hipSuccess) return e;
+        Sseg = (const float*)(ws + L.segws + SL.Sin);
+    }
+    hipLaunchKernelGGL((bwd_ckpt_kernel<E, D>), dim3((unsigned)(units * L.R * G::NCB)), block, 0,
+                       stream, k, v, z, a.beta, a.A, a.g_min, a.S0, Sseg, L.R, ckpt, ucor, a.B,
+                       a.T, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     for (int t1 = a.T; t1 > 0;) {
         const int t0 = ((t1 - 1) / L.seg) * L.seg;
         hipLaunchKernelGGL((bwd_seg_kernel<E, D>), grid, block, 0, stream, q, k, z, a.beta, a.A,

@@ -94,15 +94,18 @@ struct BackwardArgs {
 constexpr int kBwdCols = 8;
 constexpr int kBwdTokBlock = 16;
 constexpr size_t kBwdPartialBudget = (size_t)256 << 20;
+// Shortest segment of a segment-parallel forward sweep in the backward.
+constexpr int kBwdSegMin = 256;
 
 // Byte offsets of the backward workspace regions (each 256-byte aligned).
 struct BwdLayout {
-    size_t ckpt, carry, ucor, pq, pk, pg, pb, dA_part, total;
+    size_t ckpt, carry, ucor, pq, pk, pg, pb, dA_part, segws, oscr, total;
+    int R;       // segments of the forward sweep run side by side (1: one sweep)
     int seg;     // tokens per reverse-sweep launch (multiple of kBwdTokBlock)
     int NC;      // chunks (checkpoints) per sequence
     int ntb;     // finalize token blocks per sequence
 };
-BwdLayout bwd_layout(int B, int T, int H, int d);
+BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16);
 
 // How a prefill is executed.
 enum class Plan {
@@ -148,6 +151,10 @@ struct SegLayout {
 SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R);
 // a.S: dense S0 (in, may be null) and S_T (out, may be null).
 hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t stream);
+// The scan alone: the start state of every segment into the layout's Sin
+// region ([B * R, H, d, d]) and S_T into a.S.out (if set); a.o is scratch.
+hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, char* ws,
+                            hipStream_t stream);
 hipError_t launch_gate_cumsum(const void* z, const float* A, float g_min, float* G, int B, int T,
                               int H, int d, bool is_bf16, hipStream_t stream);
 hipError_t launch_intra_diag(const void* q, const void* k, const void* z, const float* beta,

@@ -125,9 +125,8 @@ SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R) {
     return L;
 }
 
-hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t stream) {
-    const SegLayout L = seg_layout(a.B, a.T, a.H, a.d, a.is_bf16, R);
-    char* w = (char*)ws;
+hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, char* w,
+                            hipStream_t stream) {
     void* inner = L.inner.ws_bytes ? (void*)(w + L.inner_ws) : nullptr;
     float* ident = (float*)(w + L.ident);
     float* M = (float*)(w + L.M);
@@ -145,8 +144,7 @@ hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t s
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(identity_kernel, dim3(2048), dim3(256), 0, stream, ident, n_states, a.d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // M_r: v = 0 from the identity; N_r: v from zero.  o is scratch until the
-    // last pass overwrites it.
+    // M_r: v = 0 from the identity; N_r: v from zero.  o is scratch.
     PrefillArgs pm{a.q, a.k, w + L.vzero, a.z, a.beta, a.A, a.g_min, dense_state(ident, M), a.o,
                    Bs, Ts, a.H, a.d, a.is_bf16};
     if ((e = launch_prefill(pm, L.inner, inner, stream)) != hipSuccess) return e;
@@ -160,9 +158,17 @@ hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t s
     else
         hipLaunchKernelGGL(segscan_kernel<32>, dim3(grid), dim3(256), 0, stream, M, N, a.S.in,
                            Sin, a.S.out, a.H, R);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    PrefillArgs pf{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state(Sin, nullptr), a.o,
-                   Bs, Ts, a.H, a.d, a.is_bf16};
+    return hipGetLastError();
+}
+
+hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t stream) {
+    const SegLayout L = seg_layout(a.B, a.T, a.H, a.d, a.is_bf16, R);
+    char* w = (char*)ws;
+    hipError_t e = seg_start_states(a, R, L, w, stream);
+    if (e != hipSuccess) return e;
+    void* inner = L.inner.ws_bytes ? (void*)(w + L.inner_ws) : nullptr;
+    PrefillArgs pf{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state((float*)(w + L.Sin), nullptr),
+                   a.o, a.B * R, a.T / R, a.H, a.d, a.is_bf16};
     return launch_prefill(pf, L.inner, inner, stream);
 }
 

@@ -297,7 +297,9 @@ def test_backward_workspace_query():
     # the partial sums stay bounded as T grows (segments); the chunk-start
     # states and the per-token corrections grow with T
     n2 = kda.kda_chunk_backward_workspace_bytes(1, 8192, 32, 128, 128, kda.KDA_BF16)
-    extra = 32 * 256 * 128 * 128 * 4 + 32 * 4096 * 128 * 4   # states + corrections u
+    # chunk-start states + corrections u, and for the segment-parallel forward
+    # sweep a zero v and a scratch o (bf16) of the extra tokens
+    extra = 32 * 256 * 128 * 128 * 4 + 32 * 4096 * 128 * 4 + 2 * 32 * 4096 * 128 * 2
     assert extra <= n2 - n <= extra + (1 << 20)
     assert kda.kda_chunk_backward_workspace_bytes(0, 64, 2, 32, 32, kda.KDA_F32) == 0
     assert kda.kda_chunk_backward_workspace_bytes(1, 64, 2, 64, 64, kda.KDA_F32) == 0

@@ -104,3 +104,15 @@ def test_backward_decay_free_gate():
                           gr["dO"], gr["dST"])
     for n in ("dq", "dk", "dv", "dbeta", "dS0"):
         assert rel_err(g[n], ref[n]) < 1e-4, n
+
+
+@pytest.mark.parametrize("d,dt,T", [(32, "f32", 768), (128, "f32", 1024), (128, "bf16", 2048)])
+def test_backward_segmented_forward_sweep(d, dt, T):
+    """T splits into whole-chunk segments of >= 256 tokens (2, 4 and 8 of
+    them here): the forward sweep runs the segments side by side from start
+    states given by a segment scan of the chunkwise forward."""
+    dev = need_gpu()
+    x = prefill_inputs(1, T, 4, d, d, DT[dt], seed=700 + T, s0_std=0.1, device=dev)
+    gr = backward_grads(1, T, 4, d, d, DT[dt], seed=700 + T, device=dev)
+    g = run(x, gr)
+    compare(x, gr, g, TOL[DT[dt]], f"backward d={d} {dt} T={T} (segmented forward sweep)")
