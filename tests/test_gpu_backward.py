@@ -106,13 +106,17 @@ def test_backward_decay_free_gate():
         assert rel_err(g[n], ref[n]) < 1e-4, n
 
 
-@pytest.mark.parametrize("d,dt,T", [(32, "f32", 768), (128, "f32", 1024), (128, "bf16", 2048)])
-def test_backward_segmented_forward_sweep(d, dt, T):
+@pytest.mark.parametrize("B,d,dt,T,s0", [(1, 32, "f32", 768, True), (1, 128, "f32", 1024, True),
+                                          (1, 128, "bf16", 2048, True), (2, 128, "bf16", 1024, False),
+                                          (2, 32, "f32", 2080, False)])
+def test_backward_segmented_forward_sweep(B, d, dt, T, s0):
     """T splits into whole-chunk segments of >= 256 tokens (2, 4 and 8 of
-    them here): the forward sweep runs the segments side by side from start
-    states given by a segment scan of the chunkwise forward."""
+    them here; 2 x 65 chunks for T = 2080): the forward sweep runs the
+    segments side by side from start states given by a segment scan of the
+    chunkwise forward."""
     dev = need_gpu()
-    x = prefill_inputs(1, T, 4, d, d, DT[dt], seed=700 + T, s0_std=0.1, device=dev)
-    gr = backward_grads(1, T, 4, d, d, DT[dt], seed=700 + T, device=dev)
+    x = prefill_inputs(B, T, 4, d, d, DT[dt], seed=700 + T, s0_std=0.1 if s0 else None, device=dev)
+    gr = backward_grads(B, T, 4, d, d, DT[dt], seed=700 + T, device=dev)
     g = run(x, gr)
-    compare(x, gr, g, TOL[DT[dt]], f"backward d={d} {dt} T={T} (segmented forward sweep)")
+    compare(x, gr, g, TOL[DT[dt]], f"backward B={B} d={d} {dt} T={T} S0={s0} (segmented forward sweep)",
+            nthreads=16)
