@@ -160,8 +160,9 @@ kda_status kda_chunk_prefill_segmented(const void *q, const void *k,
  * arguments it would reject).  It holds the state at the start of every
  * 16-token chunk (B * H * ceil(T / 16) * d_k * d_v * 4 bytes), the delta-rule
  * correction v - S'^T k of every token (B * T * H * d_v * 4 bytes), one state
- * per (b, h) carried between launches, and partial sums of one segment of
- * the sequence (at most about 256 MiB, or one 16-token block). */
+ * per (b, h) carried between launches, partial sums of one segment of the
+ * sequence (about 256 MiB, or 128 tokens' worth if that is more) and, when T
+ * splits into segments of 256 or more tokens, a segment scan's buffers. */
 size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
                                           kda_dtype dt);
 

@@ -565,7 +565,10 @@ BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     const size_t per_tok = units * ((size_t)3 * NCB * d + NCB) * sizeof(float);
     size_t seg = kBwdPartialBudget / per_tok;
     seg = seg / kBwdTokBlock * kBwdTokBlock;
-    if (seg < (size_t)kBwdTokBlock) seg = kBwdTokBlock;
+    // at least kBwdSegTokensMin tokens per launch, so that many units do not
+    // turn the sweep into thousands of short launches (the partials then
+    // exceed the budget)
+    if (seg < (size_t)kBwdSegTokensMin) seg = kBwdSegTokensMin;
     const size_t Tr = round_up((size_t)T, kBwdTokBlock);
     if (seg > Tr) seg = Tr;
     L.seg = (int)seg;

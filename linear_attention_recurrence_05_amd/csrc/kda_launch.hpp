@@ -94,6 +94,8 @@ struct BackwardArgs {
 constexpr int kBwdCols = 8;
 constexpr int kBwdTokBlock = 16;
 constexpr size_t kBwdPartialBudget = (size_t)256 << 20;
+// Fewest tokens of one reverse-sweep launch (a multiple of kBwdTokBlock).
+constexpr int kBwdSegTokensMin = 128;
 // Shortest segment of a segment-parallel forward sweep in the backward.
 constexpr int kBwdSegMin = 256;
 

@@ -47,13 +47,13 @@ def test_backward_small(d, dt, T):
 
 
 def test_backward_many_segments():
-    """B2 H96, d = 128: the partial sums of one launch cover 48 tokens, so
-    T = 200 runs as five reverse-sweep launches carrying the state gradient."""
+    """B2 H96, d = 128: the partial sums of one launch cover 128 tokens, so
+    T = 200 runs as two reverse-sweep launches carrying the state gradient."""
     dev = need_gpu()
     x = prefill_inputs(2, 200, 96, 128, 128, torch.bfloat16, seed=77, s0_std=0.1, device=dev)
     gr = backward_grads(2, 200, 96, 128, 128, torch.bfloat16, seed=77, device=dev)
     g = run(x, gr)
-    compare(x, gr, g, TOL[torch.bfloat16], "backward B2 H96 T200 (5 segments)", nthreads=16)
+    compare(x, gr, g, TOL[torch.bfloat16], "backward B2 H96 T200 (2 launches)", nthreads=16)
 
 
 def test_backward_workload_0():
