@@ -400,42 +400,54 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_seg_kernel(
                 dov[j] = sl.dO[buf][r][j];
                 part[j] = 0.f;
             }
-            float a[R], kc[R], Sprev[R][N], Sp[R][N], dqc[R];
+            // S_t = a S_prev + k beta u^T (rows of this lane), so the products
+            // with S_t and S' = a S_prev reduce to row sums of S_prev:
+            //   dq = S_t dO = a (S_prev . dO) + k beta (u . dO)
+            //   dk = beta (dS . u) - beta a (S_prev . de)
+            //   dg = a (dS' . S_prev) = a ((dS . S_prev) - k beta (S_prev . de))
+            //   dS_prev = a dS' = a dS - a k beta de^T
+            float udo = 0.f;                         // u . dO, the same for every row
+#pragma unroll
+            for (int j = 0; j < N; ++j) udo += uu[j] * dov[j];
+            float a[R], kb[R], Sprev[R][N], sdo[R];
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 a[i] = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
-                kc[i] = to_f32(kr.x[i]);
+                const float kc = to_f32(kr.x[i]);
                 const float qc = to_f32(qr.x[i]);
+                kb[i] = kc * bt;
 #pragma unroll
                 for (int m = 0; m < N / 4; ++m) {
                     const f32x4 x = hist[r][i * (N / 4) + m][l];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) Sprev[i][4 * m + e] = x[e];
                 }
-                dqc[i] = 0.f;
+                float sd = 0.f;
 #pragma unroll
                 for (int j = 0; j < N; ++j) {
-                    Sp[i][j] = a[i] * Sprev[i][j];
-                    const float Scur = Sp[i][j] + kc[i] * bt * uu[j];
                     dS[i][j] += qc * dov[j];
-                    dqc[i] += Scur * dov[j];
-                    part[j] += kc[i] * dS[i][j];
+                    sd += Sprev[i][j] * dov[j];
+                    part[j] += kc * dS[i][j];
                 }
+                sdo[i] = sd;
             }
             wave_sum8<W>(part, de);
-            float dkc[R], dgc[R];
+            float dqc[R], dkc[R], dgc[R];
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                float dk_ = 0.f, da_ = 0.f;
+                float sde = 0.f, dsu = 0.f, dss = 0.f;   // S_prev . de, dS . u, dS . S_prev
 #pragma unroll
                 for (int j = 0; j < N; ++j) {
-                    dk_ += bt * (dS[i][j] * uu[j] - Sp[i][j] * de[j]);
-                    const float dSp = dS[i][j] - kc[i] * bt * de[j];
-                    da_ += dSp * Sprev[i][j];
-                    dS[i][j] = a[i] * dSp;
+                    sde += Sprev[i][j] * de[j];
+                    dsu += dS[i][j] * uu[j];
+                    dss += dS[i][j] * Sprev[i][j];
                 }
-                dkc[i] = dk_;
-                dgc[i] = da_ * a[i];
+                dqc[i] = a[i] * sdo[i] + kb[i] * udo;
+                dkc[i] = bt * dsu - bt * a[i] * sde;
+                dgc[i] = a[i] * (dss - kb[i] * sde);
+                const float akb = a[i] * kb[i];
+#pragma unroll
+                for (int j = 0; j < N; ++j) dS[i][j] = a[i] * dS[i][j] - akb * de[j];
             }
             const size_t prow = (((size_t)cb * B + b) * seg + (t - t0)) * H + h;
             *reinterpret_cast<Rows<float, R>*>(pq + prow * D + R * l) =
