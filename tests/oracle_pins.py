@@ -28,7 +28,7 @@ import os
 import numpy as np
 from scipy.special import expit
 
-from oracle.chunkwise import chunk_prefill
+from oracle.chunkwise import chunk_head_backward, chunk_prefill, gate_fp64
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -366,11 +366,40 @@ def pin_backward_beta_zero(orc):
     assert np.all(gr["dk"] == 0.0) and np.all(gr["dv"] == 0.0)
 
 
+def pin_backward_chunkwise_equivalence(orc):
+    """The token-by-token gradients equal those of the independent chunkwise
+    backward (oracle/chunkwise.py, the chunk equations differentiated step by
+    step) for chunk sizes 1, 5, 16 and T, including dz through the gate."""
+    rng = np.random.default_rng(33)
+    B, T, H, dk, dv = 2, 21, 2, 5, 4
+    q, k, v, z, beta, A, S0 = _inputs(rng, B, T, H, dk, dv)
+    dO = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    dST = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    g_min = -5.0
+    ref = orc.backward(q, k, v, z, beta, A, g_min, S0, dO, dST)
+    for b in range(B):
+        for h in range(H):
+            g = gate_fp64(z[b, :, h], float(A[h]), g_min)
+            x = np.exp(np.float64(A[h])) * z[b, :, h].astype(np.float64)
+            s = expit(x)
+            for C in (1, 5, 16, T):
+                c = chunk_head_backward(q[b, :, h], k[b, :, h], v[b, :, h], g, beta[b, :, h],
+                                        S0[b, h], dO[b, :, h], dST[b, h], C)
+                np.testing.assert_allclose(c["dq"], ref["dq"][b, :, h], rtol=0, atol=1e-12)
+                np.testing.assert_allclose(c["dk"], ref["dk"][b, :, h], rtol=0, atol=1e-12)
+                np.testing.assert_allclose(c["dv"], ref["dv"][b, :, h], rtol=0, atol=1e-12)
+                np.testing.assert_allclose(c["dbeta"], ref["dbeta"][b, :, h], rtol=0, atol=1e-12)
+                np.testing.assert_allclose(c["dS0"], ref["dS0"][b, h], rtol=0, atol=1e-12)
+                dz = c["dg"] * g_min * s * (1.0 - s) * np.exp(np.float64(A[h]))
+                np.testing.assert_allclose(dz, ref["dz"][b, :, h], rtol=0, atol=1e-12)
+
+
 PINS = [pin_gate_at_zero, pin_gate_library, pin_gate_bounds_printed, pin_chunk_cumsum,
         pin_scalar_ema, pin_beta_zero, pin_exact_retrieval, pin_linear_attention,
         pin_alpha_one_beta_zero, pin_chunkwise_equivalence, pin_continuation,
         pin_linearity, pin_structure, pin_decode_matches_prefill,
-        pin_backward_finite_difference, pin_backward_beta_zero]
+        pin_backward_finite_difference, pin_backward_beta_zero,
+        pin_backward_chunkwise_equivalence]
 
 
 def failing_pins(orc):
