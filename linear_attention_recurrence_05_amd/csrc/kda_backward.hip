@@ -564,7 +564,8 @@ BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     // of at least kBwdSegMin tokens.
     L.R = 1;
     for (int r : {8, 4, 2})
-        if (T % (kChunk * r) == 0 && T / r >= kBwdSegMin) {
+        if (T % (kChunk * r) == 0 && T / r >= kBwdSegMin &&
+            (long long)B * r * H <= (1LL << 26)) {   // the inner prefill's unit limit
             L.R = r;
             break;
         }
