@@ -99,3 +99,31 @@ def test_exact_retrieval(p, d, dt):
     eo = rel_err(o, f64(x["v"]))
     say(f"exact retrieval {p} d={d} {dt}: o - v {eo:.2e}")
     assert eo < TOL[DT[dt]]
+
+
+@pytest.mark.parametrize("d,dt", [(32, "f32"), (128, "f32"), (128, "bf16")])
+def test_decode_special_cases(d, dt):
+    """One decode step and a 5-token verify step: beta = 0 leaves
+    S = Diag(a) S_prev and o = S^T q; beta = 1 with q = k retrieves v."""
+    dev = need_gpu()
+    x = prefill_inputs(4, 5, 3, d, d, DT[dt], seed=64, s0_std=0.1, device=dev)
+    # beta = 0, one step
+    S = x["S0"].clone()
+    q1, k1, v1, z1 = (x[n][:, 0].contiguous() for n in ("q", "k", "v", "z"))
+    o = kda.decode_step(q1, k1, v1, z1, torch.zeros_like(x["beta"][:, 0]).contiguous(), x["A"], S,
+                        g_min=x["g_min"])
+    torch.cuda.synchronize()
+    a = np.exp(gate(z1[:, None], x["A"], x["g_min"])[:, 0])           # [B,H,dk]
+    S_ref = a[..., None] * f64(x["S0"])
+    o_ref = np.einsum("bhcj,bhc->bhj", S_ref, f64(q1))
+    eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+    say(f"decode beta = 0 d={d} {dt}: o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[DT[dt]] and es < 1e-5
+    # beta = 1, q = k: every token of a verify step retrieves its own v
+    k = x["k"]
+    o5, _ = kda.decode_tokens(k, k, x["v"], x["z"], torch.ones_like(x["beta"]), x["A"], x["S0"],
+                              g_min=x["g_min"])
+    torch.cuda.synchronize()
+    eo = rel_err(o5, f64(x["v"]))
+    say(f"verify exact retrieval d={d} {dt}: o - v {eo:.2e}")
+    assert eo < TOL[DT[dt]]
