@@ -183,7 +183,11 @@ size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
  *                     kda_chunk_backward_workspace_bytes(...) bytes, scratch
  *                     for this call only.
  * The sweep runs in fp32 whatever dt is.  dA and dbeta are summed over
- * value-column blocks and tokens in a fixed order (deterministic). */
+ * value-column blocks and tokens in a fixed order (deterministic).
+ * For tests and tuning the environment variable KDA_BACKWARD_PLAN=chain
+ * selects the chunk-level plan (a chain of per-chunk state gradients, then
+ * every chunk's reverse sweep at once) instead of the default sweep over the
+ * whole sequence; the workspace query honours the same variable. */
 kda_status kda_chunk_backward(const void *q, const void *k, const void *v,
                               const void *z, const float *beta, const float *A,
                               float g_min, const float *S0, const void *dO,

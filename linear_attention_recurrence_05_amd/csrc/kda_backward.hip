@@ -48,6 +48,9 @@
 // chain of VALU work per token (no contraction wide enough for MFMA: per
 // token a lane does O(16) FMAs per product); it is bounded by latency, with
 // HBM traffic for inputs, checkpoints, u and the partials.
+#include <cstdlib>
+#include <cstring>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -316,34 +319,52 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_ckpt_kernel(
 }
 
 // Reverse sweep over tokens [t0, t1) (t0 a multiple of the segment length, t1
-// = T or the next segment's start).  The state gradient starts from dS_T
-// (t1 == T) or the carry of the previous launch, and ends in dS0 (t0 == 0)
-// or the carry.  Partials are indexed by the token's place in the segment.
-template <typename E, int D>
+// = T or the next segment's start).  Partials are indexed by the token's place
+// in the segment.
+//   PAR = false: one workgroup per (b, h, column block) walks the chunks last
+//     to first; the state gradient starts from dS_T (t1 == T) or the carry of
+//     the previous launch, and ends in dS0 (t0 == 0) or the carry.
+//   PAR = true: one workgroup per (b, h, column block, chunk), all chunks of
+//     the range at once; each starts from the gradient of its chunk's end
+//     state, dSend (from bwd_chain_kernel), and the first chunk's workgroup
+//     writes dS0.
+// The chunk's states are recomputed and swept in windows of HW tokens (the
+// LDS a workgroup holds scales with HW; each window recomputes from the
+// chunk's checkpoint).
+template <typename E, int D, bool PAR, int HW>
 __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_seg_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ z,
     const float* __restrict__ beta, const float* __restrict__ A, float g_min,
     const E* __restrict__ dO, const float* __restrict__ dST, const float* __restrict__ ckpt,
     const float* __restrict__ ucor, float* __restrict__ carry, float* __restrict__ dS0,
     E* __restrict__ dv, float* __restrict__ pq, float* __restrict__ pk, float* __restrict__ pg,
-    float* __restrict__ pb, int B, int T, int H, int t0, int t1, int seg) {
+    float* __restrict__ pb, const float* __restrict__ dSend, int nch, int B, int T, int H,
+    int t0, int t1, int seg) {
     using G = BwdGeom<D>;
     constexpr int N = G::N, R = G::RPT, W = G::W;
-    // hist[r][m][l]: the state slice before token r of the chunk, lane l's
-    // rows, values 4m .. 4m+3 of row R l + m / 2 (lane l reads back only its own)
-    __shared__ f32x4 hist[kChunk][R * N / 4][W];
+    static_assert(HW >= 1 && HW <= kChunk, "window within a chunk");
+    // hist[r][m][l]: the state slice before token w0 + r of the chunk's
+    // current window, lane l's rows, values 4m .. 4m+3 of row R l + m / 2
+    // (lane l reads back only its own)
+    __shared__ f32x4 hist[HW][R * N / 4][W];
     __shared__ StageLds<E, R, W, true> sl;
     const int l = (int)threadIdx.x;
     const int cb = (int)(blockIdx.x % G::NCB);
-    const size_t u = blockIdx.x / G::NCB;
+    const size_t rest = blockIdx.x / G::NCB;
+    const int nl = PAR ? (int)(rest % (size_t)nch) : 0;
+    const size_t u = PAR ? rest / (size_t)nch : rest;
     const int b = (int)(u / (size_t)H), h = (int)(u % (size_t)H);
     const int NC = (T + kChunk - 1) / kChunk;
     const GateConsts gc = make_gate(A[h], g_min);
+    const int n_hi = PAR ? t0 / kChunk + nl : (t1 - 1) / kChunk;
+    const int n_lo = PAR ? n_hi : t0 / kChunk;
     float dS[R][N];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const size_t slice = (u * D + R * l + i) * D + cb * N;   // [b, h, row, cb * N]
-        if (t1 == T) {
+        if (PAR) {
+            load8f(dSend + (((u * NC + n_hi) * D + R * l + i) * D + cb * N), dS[i]);
+        } else if (t1 == T) {
             if (dST) load8f(dST + slice, dS[i]);
             else
 #pragma unroll
@@ -354,7 +375,6 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_seg_kernel(
     }
     const float* ck = ckpt + (u * G::NCB + cb) * (size_t)NC * (D * N) + (R * l) * N;
     const float* uc = ucor + (u * G::NCB + cb) * (size_t)T * N;
-    const int n_hi = (t1 - 1) / kChunk, n_lo = t0 / kChunk;
     Stage<E, R, true> st;
     stage_load<E, float, D, true>(st, q, k, z, beta, dO, uc + (size_t)n_hi * kChunk * N, N, b, h,
                                   T, H, cb, n_hi * kChunk);
@@ -367,115 +387,245 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_seg_kernel(
             stage_load<E, float, D, true>(st, q, k, z, beta, dO, uc + (size_t)(cs - kChunk) * N,
                                           N, b, h, T, H, cb, cs - kChunk);
         __syncthreads();
-        float S[R][N];
+        // (with HW = kChunk a single window: w0 is 0 at compile time)
+        for (int w0 = HW == kChunk ? 0 : ((L - 1) / HW) * HW; w0 >= 0; w0 -= HW) {
+            const int w1 = HW == kChunk ? L : min(L, w0 + HW);
+            float S[R][N];
 #pragma unroll
-        for (int i = 0; i < R; ++i) load8f(ck + (size_t)n * (D * N) + i * N, S[i]);
-        // recompute the chunk's states from the stored corrections
-        for (int r = 0; r < L; ++r) {
+            for (int i = 0; i < R; ++i) load8f(ck + (size_t)n * (D * N) + i * N, S[i]);
+            // recompute the chunk's states up to the window's end from the stored
+            // corrections, keeping those of the window
+            for (int r = 0; r < w1; ++r) {
+                if (HW == kChunk || r >= w0) {
 #pragma unroll
-            for (int i = 0; i < R; ++i)
+                    for (int i = 0; i < R; ++i)
 #pragma unroll
-                for (int m = 0; m < N / 4; ++m)
-                    hist[r][i * (N / 4) + m][l] =
-                        f32x4{S[i][4 * m], S[i][4 * m + 1], S[i][4 * m + 2], S[i][4 * m + 3]};
-            const Rows<E, R> zr = sl.z[r][l], kr = sl.k[r][l];
-            const float bt = sl.beta[buf][r];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const float a = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
-                const float kb = to_f32(kr.x[i]) * bt;
-#pragma unroll
-                for (int j = 0; j < N; ++j) S[i][j] = a * S[i][j] + kb * sl.x[buf][r][j];
-            }
-        }
-        // reverse sweep
-        for (int r = L - 1; r >= 0; --r) {
-            const int t = cs + r;
-            const Rows<E, R> zr = sl.z[r][l], kr = sl.k[r][l], qr = sl.q[r][l];
-            const float bt = sl.beta[buf][r];
-            float uu[N], dov[N], part[N], de[N];
-#pragma unroll
-            for (int j = 0; j < N; ++j) {
-                uu[j] = sl.x[buf][r][j];
-                dov[j] = sl.dO[buf][r][j];
-                part[j] = 0.f;
-            }
-            // S_t = a S_prev + k beta u^T (rows of this lane), so the products
-            // with S_t and S' = a S_prev reduce to row sums of S_prev:
-            //   dq = S_t dO = a (S_prev . dO) + k beta (u . dO)
-            //   dk = beta (dS . u) - beta a (S_prev . de)
-            //   dg = a (dS' . S_prev) = a ((dS . S_prev) - k beta (S_prev . de))
-            //   dS_prev = a dS' = a dS - a k beta de^T
-            float udo = 0.f;                         // u . dO, the same for every row
-#pragma unroll
-            for (int j = 0; j < N; ++j) udo += uu[j] * dov[j];
-            float a[R], kb[R], Sprev[R][N], sdo[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                a[i] = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
-                const float kc = to_f32(kr.x[i]);
-                const float qc = to_f32(qr.x[i]);
-                kb[i] = kc * bt;
-#pragma unroll
-                for (int m = 0; m < N / 4; ++m) {
-                    const f32x4 x = hist[r][i * (N / 4) + m][l];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Sprev[i][4 * m + e] = x[e];
+                        for (int m = 0; m < N / 4; ++m)
+                            hist[r - w0][i * (N / 4) + m][l] =
+                                f32x4{S[i][4 * m], S[i][4 * m + 1], S[i][4 * m + 2], S[i][4 * m + 3]};
                 }
-                float sd = 0.f;
+                const Rows<E, R> zr = sl.z[r][l], kr = sl.k[r][l];
+                const float bt = sl.beta[buf][r];
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const float a = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
+                    const float kb = to_f32(kr.x[i]) * bt;
+#pragma unroll
+                    for (int j = 0; j < N; ++j) S[i][j] = a * S[i][j] + kb * sl.x[buf][r][j];
+                }
+            }
+            // reverse sweep of the window
+            for (int r = w1 - 1; r >= w0; --r) {
+                const int t = cs + r;
+                const Rows<E, R> zr = sl.z[r][l], kr = sl.k[r][l], qr = sl.q[r][l];
+                const float bt = sl.beta[buf][r];
+                float uu[N], dov[N], part[N], de[N];
 #pragma unroll
                 for (int j = 0; j < N; ++j) {
-                    dS[i][j] += qc * dov[j];
-                    sd += Sprev[i][j] * dov[j];
-                    part[j] += kc * dS[i][j];
+                    uu[j] = sl.x[buf][r][j];
+                    dov[j] = sl.dO[buf][r][j];
+                    part[j] = 0.f;
                 }
-                sdo[i] = sd;
-            }
-            wave_sum8<W>(part, de);
-            float dqc[R], dkc[R], dgc[R];
+                // S_t = a S_prev + k beta u^T (rows of this lane), so the products
+                // with S_t and S' = a S_prev reduce to row sums of S_prev:
+                //   dq = S_t dO = a (S_prev . dO) + k beta (u . dO)
+                //   dk = beta (dS . u) - beta a (S_prev . de)
+                //   dg = a (dS' . S_prev) = a ((dS . S_prev) - k beta (S_prev . de))
+                //   dS_prev = a dS' = a dS - a k beta de^T
+                float udo = 0.f;                         // u . dO, the same for every row
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                float sde = 0.f, dsu = 0.f, dss = 0.f;   // S_prev . de, dS . u, dS . S_prev
+                for (int j = 0; j < N; ++j) udo += uu[j] * dov[j];
+                float a[R], kb[R], Sprev[R][N], sdo[R];
 #pragma unroll
-                for (int j = 0; j < N; ++j) {
-                    sde += Sprev[i][j] * de[j];
-                    dsu += dS[i][j] * uu[j];
-                    dss += dS[i][j] * Sprev[i][j];
+                for (int i = 0; i < R; ++i) {
+                    a[i] = gate_alpha(gc, gate_sigmoid(gc, to_f32(zr.x[i])));
+                    const float kc = to_f32(kr.x[i]);
+                    const float qc = to_f32(qr.x[i]);
+                    kb[i] = kc * bt;
+#pragma unroll
+                    for (int m = 0; m < N / 4; ++m) {
+                        const f32x4 x = hist[r - w0][i * (N / 4) + m][l];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Sprev[i][4 * m + e] = x[e];
+                    }
+                    float sd = 0.f;
+#pragma unroll
+                    for (int j = 0; j < N; ++j) {
+                        dS[i][j] += qc * dov[j];
+                        sd += Sprev[i][j] * dov[j];
+                        part[j] += kc * dS[i][j];
+                    }
+                    sdo[i] = sd;
                 }
-                dqc[i] = a[i] * sdo[i] + kb[i] * udo;
-                dkc[i] = bt * dsu - bt * a[i] * sde;
-                dgc[i] = a[i] * (dss - kb[i] * sde);
-                const float akb = a[i] * kb[i];
+                wave_sum8<W>(part, de);
+                float dqc[R], dkc[R], dgc[R];
 #pragma unroll
-                for (int j = 0; j < N; ++j) dS[i][j] = a[i] * dS[i][j] - akb * de[j];
-            }
-            const size_t prow = (((size_t)cb * B + b) * seg + (t - t0)) * H + h;
-            *reinterpret_cast<Rows<float, R>*>(pq + prow * D + R * l) =
-                *reinterpret_cast<const Rows<float, R>*>(dqc);
-            *reinterpret_cast<Rows<float, R>*>(pk + prow * D + R * l) =
-                *reinterpret_cast<const Rows<float, R>*>(dkc);
-            *reinterpret_cast<Rows<float, R>*>(pg + prow * D + R * l) =
-                *reinterpret_cast<const Rows<float, R>*>(dgc);
-            if (l == 0) {
-                float db = 0.f, dvv[N];
+                for (int i = 0; i < R; ++i) {
+                    float sde = 0.f, dsu = 0.f, dss = 0.f;   // S_prev . de, dS . u, dS . S_prev
 #pragma unroll
-                for (int j = 0; j < N; ++j) {
-                    db += de[j] * uu[j];
-                    dvv[j] = bt * de[j];
+                    for (int j = 0; j < N; ++j) {
+                        sde += Sprev[i][j] * de[j];
+                        dsu += dS[i][j] * uu[j];
+                        dss += dS[i][j] * Sprev[i][j];
+                    }
+                    dqc[i] = a[i] * sdo[i] + kb[i] * udo;
+                    dkc[i] = bt * dsu - bt * a[i] * sde;
+                    dgc[i] = a[i] * (dss - kb[i] * sde);
+                    const float akb = a[i] * kb[i];
+#pragma unroll
+                    for (int j = 0; j < N; ++j) dS[i][j] = a[i] * dS[i][j] - akb * de[j];
                 }
-                pb[prow] = db;
-                store8(dv + (((size_t)b * T + t) * H + h) * D + cb * N, dvv);
+                const size_t prow = (((size_t)cb * B + b) * seg + (t - t0)) * H + h;
+                *reinterpret_cast<Rows<float, R>*>(pq + prow * D + R * l) =
+                    *reinterpret_cast<const Rows<float, R>*>(dqc);
+                *reinterpret_cast<Rows<float, R>*>(pk + prow * D + R * l) =
+                    *reinterpret_cast<const Rows<float, R>*>(dkc);
+                *reinterpret_cast<Rows<float, R>*>(pg + prow * D + R * l) =
+                    *reinterpret_cast<const Rows<float, R>*>(dgc);
+                if (l == 0) {
+                    float db = 0.f, dvv[N];
+#pragma unroll
+                    for (int j = 0; j < N; ++j) {
+                        db += de[j] * uu[j];
+                        dvv[j] = bt * de[j];
+                    }
+                    pb[prow] = db;
+                    store8(dv + (((size_t)b * T + t) * H + h) * D + cb * N, dvv);
+                }
             }
         }
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const size_t slice = (u * D + R * l + i) * D + cb * N;
-        if (t0 == 0) {
+        if (PAR) {
+            if (n_lo == 0 && dS0) store8f(dS0 + slice, dS[i]);
+        } else if (t0 == 0) {
             if (dS0) store8f(dS0 + slice, dS[i]);
         } else {
             store8f(carry + slice, dS[i]);
         }
+    }
+}
+
+// Gradients of the chunk end states, chunk by chunk from the last: with the
+// chunk's factors K~ = k e^G, Q~ = q e^G, Kdec = k e^{G_L - G}, gamma = e^{G_L}
+// (G the chunk-local cumulative log-decay), Tm and Aqk (the intra-chunk
+// stage's exports), the state gradient at the chunk's start is
+//   dS_start = Diag(gamma) dS_end + Q~^T dO - K~^T Tm^T (Kdec dS_end + Aqk^T dO)
+// (the chunk equations differentiated; the same recurrence the token-level
+// reverse sweep runs 16 steps at a time).  One workgroup of 256 threads per
+// (b, h, 16 value columns); per chunk three small products through LDS.
+// Writes dSend[(u * NC + n)] = the gradient of chunk n's end state.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_chain_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ Gc,
+    const float* __restrict__ Tm, const float* __restrict__ Aqk, const float* __restrict__ gam,
+    const E* __restrict__ dO, const float* __restrict__ dST, float* __restrict__ dSend, int T,
+    int H) {
+    constexpr int CB = 16;                  // value columns per workgroup
+    constexpr int TPR = 256 / D;            // threads per state row
+    constexpr int CPT = CB / TPR;           // state columns per thread
+    constexpr int FE = kChunk * D / 256;    // factor elements per thread
+    constexpr int DP = D + 4;               // padded row (16-byte aligned rows)
+    __shared__ __attribute__((aligned(16))) float sKd[kChunk][DP];
+    __shared__ __attribute__((aligned(16))) float sKt[kChunk][DP];
+    __shared__ __attribute__((aligned(16))) float sQt[kChunk][DP];
+    __shared__ __attribute__((aligned(16))) float sST[CB][DP];          // dS_end, transposed
+    __shared__ __attribute__((aligned(16))) float sdO[kChunk][CB], sY[kChunk][CB];
+    __shared__ float sTm[kChunk][17], sAq[kChunk][17], sZ[kChunk][17], sg[D];
+    const int tid = (int)threadIdx.x;
+    const int nct = D / CB;
+    const int ct = (int)(blockIdx.x % nct);
+    const size_t u = blockIdx.x / nct;
+    const int b = (int)(u / (size_t)H), h = (int)(u % (size_t)H);
+    const int NC = (T + kChunk - 1) / kChunk;
+    const int c = tid / TPR, j0 = (tid % TPR) * CPT;   // state entries: row c, columns j0 ..
+    const int zr = tid / CB, zj = tid % CB;            // 16x16 products: row zr, column zj
+    const size_t col0 = (size_t)ct * CB;
+    float dS[CPT];
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) dS[x] = dST ? dST[(u * D + c) * D + col0 + j0 + x] : 0.f;
+    // one chunk's inputs, loaded a chunk ahead
+    struct In {
+        float k[FE], q[FE], g[FE], gm[FE];
+        float tm, aq, dO, gg;
+    };
+    auto load = [&](int n, In& in) {
+        const int cs = n * kChunk, L = min(kChunk, T - cs);
+        const size_t cidx = u * NC + n;
+#pragma unroll
+        for (int x = 0; x < FE; ++x) {
+            const int e = tid + 256 * x, r = e / D, cc = e % D;
+            if (r < L) {
+                const size_t i = (((size_t)b * T + cs + r) * H + h) * D + cc;
+                in.k[x] = to_f32(k[i]);
+                in.q[x] = to_f32(q[i]);
+                in.g[x] = Gc[i];
+            } else {
+                in.k[x] = in.q[x] = in.g[x] = 0.f;
+            }
+            in.gm[x] = gam[cidx * D + cc];
+        }
+        in.tm = Tm[cidx * 256 + tid];
+        in.aq = Aqk[cidx * 256 + tid];
+        in.dO = zr < L ? to_f32(dO[(((size_t)b * T + cs + zr) * H + h) * D + col0 + zj]) : 0.f;
+        in.gg = tid < D ? gam[cidx * D + tid] : 0.f;
+    };
+    In cur, nxt;
+    load(NC - 1, cur);
+    for (int n = NC - 1; n >= 0; --n) {
+        const size_t cidx = u * NC + n;
+        // the chunk's factors into LDS (rows past its end are zero)
+#pragma unroll
+        for (int x = 0; x < FE; ++x) {
+            const int e = tid + 256 * x, r = e / D, cc = e % D;
+            const float ex = expf(cur.g[x]);
+            sKt[r][cc] = cur.k[x] * ex;
+            sQt[r][cc] = cur.q[x] * ex;
+            sKd[r][cc] = ex > 0.f ? cur.k[x] * (cur.gm[x] / ex) : 0.f;
+        }
+        sTm[zr][zj] = cur.tm;
+        sAq[zr][zj] = cur.aq;
+        sdO[zr][zj] = cur.dO;
+        if (tid < D) sg[tid] = cur.gg;
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) {
+            sST[j0 + x][c] = dS[x];
+            dSend[(cidx * D + c) * D + col0 + j0 + x] = dS[x];
+        }
+        if (n > 0) load(n - 1, nxt);
+        __syncthreads();
+        // Z = Kdec dS_end + Aqk^T dO
+        float z = 0.f;
+#pragma unroll 4
+        for (int cc = 0; cc < D; cc += 4) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sKd[zr][cc]);
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sST[zj][cc]);
+            z += a4[0] * s4[0] + a4[1] * s4[1] + a4[2] * s4[2] + a4[3] * s4[3];
+        }
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) z += sAq[i][zr] * sdO[i][zj];
+        sZ[zr][zj] = z;
+        __syncthreads();
+        // Y = Tm^T Z
+        float y = 0.f;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) y += sTm[i][zr] * sZ[i][zj];
+        sY[zr][zj] = y;
+        __syncthreads();
+        // dS_start = Diag(gamma) dS_end + Q~^T dO - K~^T Y (row c, columns j0 ..)
+        const float gc = sg[c];
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) dS[x] *= gc;
+#pragma unroll
+        for (int r = 0; r < kChunk; ++r) {
+            const float qr = sQt[r][c], kr = sKt[r][c];
+#pragma unroll
+            for (int x = 0; x < CPT; ++x) dS[x] += qr * sdO[r][j0 + x] - kr * sY[r][j0 + x];
+        }
+        __syncthreads();   // before the next chunk's factors overwrite LDS
+        if (n > 0) cur = nxt;
     }
 }
 
@@ -557,6 +707,16 @@ __global__ __launch_bounds__(256) void bwd_dA_kernel(const float* __restrict__ d
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Plan of the reverse sweep: "sweep" (one token-level sweep per (b, h,
+// column block) over the whole sequence, the default) or, with
+// KDA_BACKWARD_PLAN=chain and more than one chunk, "chain" (the chunk-level
+// state-gradient chain, then every chunk's token-level sweep at once; on
+// MI355X it is slower for now: its chain kernel runs ~8 us per chunk).
+bool bwd_plan_chain(int T) {
+    const char* env = std::getenv("KDA_BACKWARD_PLAN");
+    return env && std::strcmp(env, "chain") == 0 && T > kChunk;
+}
+
 BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     BwdLayout L;
     // The forward sweep runs as R segments side by side, each from its start
@@ -600,6 +760,17 @@ BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     L.pg = take(pel * d * sizeof(float));
     L.pb = take(pel * sizeof(float));
     L.dA_part = take(units * L.ntb * sizeof(float));
+    // chain plan: the gate and intra-chunk exports, and the end-state
+    // gradient of every chunk
+    L.chain = bwd_plan_chain(T);
+    L.Gc = L.Tm = L.Aqk = L.gam = L.dSend = 0;
+    if (L.chain) {
+        L.Gc = take(units * (size_t)T * d * sizeof(float));
+        L.Tm = take(units * L.NC * (size_t)256 * sizeof(float));
+        L.Aqk = take(units * L.NC * (size_t)256 * sizeof(float));
+        L.gam = take(units * L.NC * (size_t)d * sizeof(float));
+        L.dSend = take(units * L.NC * (size_t)d * d * sizeof(float));
+    }
     L.segws = L.oscr = 0;
     if (L.R > 1) {
         L.segws = take(seg_layout(B, T, H, d, is_bf16, L.R).total);
@@ -641,11 +812,40 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
                        stream, k, v, z, a.beta, a.A, a.g_min, a.S0, Sseg, L.R, ckpt, ucor, a.B,
                        a.T, a.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const float* dSend = nullptr;
+    if (L.chain) {
+        // chunk factors (the intra-chunk stage's exports) and the chain
+        float* Gc = (float*)(ws + L.Gc);
+        float* Tm = (float*)(ws + L.Tm);
+        float* Aqk = (float*)(ws + L.Aqk);
+        float* gam = (float*)(ws + L.gam);
+        if ((e = launch_gate_cumsum(a.z, a.A, a.g_min, Gc, a.B, a.T, a.H, D, sizeof(E) == 2,
+                                    stream)) != hipSuccess)
+            return e;
+        if ((e = launch_intra_diag(a.q, a.k, a.z, a.beta, a.A, a.g_min, Tm, Aqk, gam, a.B, a.T, a.H,
+                                   D, sizeof(E) == 2, stream)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL((bwd_chain_kernel<E, D>), dim3((unsigned)(units * (D / 16))), dim3(256),
+                           0, stream, q, k, Gc, Tm, Aqk, gam, (const E*)a.dO, a.dST,
+                           (float*)(ws + L.dSend), a.T, a.H);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        dSend = (const float*)(ws + L.dSend);
+    }
     for (int t1 = a.T; t1 > 0;) {
         const int t0 = ((t1 - 1) / L.seg) * L.seg;
-        hipLaunchKernelGGL((bwd_seg_kernel<E, D>), grid, block, 0, stream, q, k, z, a.beta, a.A,
-                           a.g_min, (const E*)a.dO, a.dST, ckpt, ucor, carry, a.dS0, (E*)a.dv, pq,
-                           pk, pg, pb, a.B, a.T, a.H, t0, t1, L.seg);
+        if (L.chain) {
+            const int nch = (t1 - t0 + kChunk - 1) / kChunk;
+            hipLaunchKernelGGL((bwd_seg_kernel<E, D, true, kBwdHistPar>),
+                               dim3((unsigned)(units * nch * G::NCB)), block, 0, stream, q, k, z,
+                               a.beta, a.A, a.g_min, (const E*)a.dO, a.dST, ckpt, ucor, carry,
+                               a.dS0, (E*)a.dv, pq, pk, pg, pb, dSend, nch, a.B, a.T, a.H, t0, t1,
+                               L.seg);
+        } else {
+            hipLaunchKernelGGL((bwd_seg_kernel<E, D, false, kChunk>), grid, block, 0, stream, q, k,
+                               z, a.beta, a.A, a.g_min, (const E*)a.dO, a.dST, ckpt, ucor, carry,
+                               a.dS0, (E*)a.dv, pq, pk, pg, pb, nullptr, 1, a.B, a.T, a.H, t0, t1,
+                               L.seg);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int n_tok = t1 - t0;
         const int nsb = (n_tok + kBwdTokBlock - 1) / kBwdTokBlock;

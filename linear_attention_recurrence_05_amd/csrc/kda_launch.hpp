@@ -94,6 +94,8 @@ struct BackwardArgs {
 constexpr int kBwdCols = 8;
 constexpr int kBwdTokBlock = 16;
 constexpr size_t kBwdPartialBudget = (size_t)256 << 20;
+// Recompute window (tokens) of the chunk-parallel reverse sweep.
+constexpr int kBwdHistPar = 4;
 // Fewest tokens of one reverse-sweep launch (a multiple of kBwdTokBlock).
 constexpr int kBwdSegTokensMin = 128;
 // Shortest segment of a segment-parallel forward sweep in the backward.
@@ -101,13 +103,15 @@ constexpr int kBwdSegMin = 256;
 
 // Byte offsets of the backward workspace regions (each 256-byte aligned).
 struct BwdLayout {
-    size_t ckpt, carry, ucor, pq, pk, pg, pb, dA_part, segws, oscr, total;
+    size_t ckpt, carry, ucor, pq, pk, pg, pb, dA_part, segws, oscr, Gc, Tm, Aqk, gam, dSend, total;
     int R;       // segments of the forward sweep run side by side (1: one sweep)
+    bool chain;  // reverse sweep by the chunk-level chain, chunks in parallel
     int seg;     // tokens per reverse-sweep launch (multiple of kBwdTokBlock)
     int NC;      // chunks (checkpoints) per sequence
     int ntb;     // finalize token blocks per sequence
 };
 BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16);
+bool bwd_plan_chain(int T);
 
 // How a prefill is executed.
 enum class Plan {

@@ -298,9 +298,20 @@ def test_backward_workspace_query():
     # states and the per-token corrections grow with T
     n2 = kda.kda_chunk_backward_workspace_bytes(1, 8192, 32, 128, 128, kda.KDA_BF16)
     # chunk-start states + corrections u, and for the segment-parallel forward
-    # sweep a zero v and a scratch o (bf16) of the extra tokens
+    # sweep a zero v and a scratch o (bf16), for the 4096 extra tokens
+    # (256 chunks) of 32 heads
     extra = 32 * 256 * 128 * 128 * 4 + 32 * 4096 * 128 * 4 + 2 * 32 * 4096 * 128 * 2
     assert extra <= n2 - n <= extra + (1 << 20)
+    # the chain plan adds the cumulative log-decay, Tm, Aqk, gamma and the
+    # end-state gradient of every chunk
+    os.environ["KDA_BACKWARD_PLAN"] = "chain"
+    try:
+        nc = kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_BF16)
+    finally:
+        del os.environ["KDA_BACKWARD_PLAN"]
+    chain = (32 * 4096 * 128 * 4 + 2 * 32 * 256 * 256 * 4 + 32 * 256 * 128 * 4
+             + 32 * 256 * 128 * 128 * 4)
+    assert chain <= nc - n <= chain + (1 << 20)
     assert kda.kda_chunk_backward_workspace_bytes(0, 64, 2, 32, 32, kda.KDA_F32) == 0
     assert kda.kda_chunk_backward_workspace_bytes(1, 64, 2, 64, 64, kda.KDA_F32) == 0
 

@@ -120,3 +120,25 @@ def test_backward_segmented_forward_sweep(B, d, dt, T, s0):
     g = run(x, gr)
     compare(x, gr, g, TOL[DT[dt]], f"backward B={B} d={d} {dt} T={T} S0={s0} (segmented forward sweep)",
             nthreads=16)
+
+
+@pytest.mark.parametrize("bplan", ["sweep", "chain"])
+@pytest.mark.parametrize("d,dt,T", [(32, "f32", 100), (128, "f32", 300), (128, "bf16", 520)])
+def test_backward_plans(bplan, d, dt, T):
+    """Both reverse-sweep plans against the oracle: one token-level sweep per
+    (b, h, column block) over the sequence, and the chunk-level chain of end-
+    state gradients followed by every chunk's sweep at once."""
+    dev = need_gpu()
+    x = prefill_inputs(2, T, 3, d, d, DT[dt], seed=800 + T, s0_std=0.1, device=dev)
+    gr = backward_grads(2, T, 3, d, d, DT[dt], seed=800 + T, device=dev)
+    import os
+    old = os.environ.get("KDA_BACKWARD_PLAN")
+    os.environ["KDA_BACKWARD_PLAN"] = bplan
+    try:
+        g = run(x, gr)
+    finally:
+        if old is None:
+            os.environ.pop("KDA_BACKWARD_PLAN", None)
+        else:
+            os.environ["KDA_BACKWARD_PLAN"] = old
+    compare(x, gr, g, TOL[DT[dt]], f"backward plan {bplan} d={d} {dt} T={T}")
