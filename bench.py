@@ -264,6 +264,18 @@ def main():
         dms = sorted(reps)[1] / n
         db = decode_alg_bytes(c.B, c.H, c.dk)
         dgbs = db / (dms * 1e-3) / 1e9
+        # practical ceiling: a device copy of the same 512 MiB state (read
+        # once, written once), the same byte count as a decode step's state
+        cps = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            S_save.copy_(S)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cps.append(e0.elapsed_time(e1))
+        copy_gbs = 2 * S.numel() * 4 / (sorted(cps)[2] * 1e-3) / 1e9
         line["decode"] = {
             "metric": "KDA decode steps/s", "value": 1e3 / dms, "unit": "steps/s",
             "ms_per_step": dms, "steps": n, "repetitions": 3,
@@ -273,7 +285,8 @@ def main():
                          "frac": dgbs / HBM_PEAK_GBS,
                          "traffic": measured_traffic("decode_B256_H32_d128_bf16_step_bytes"),
                          "traffic_unit": "bytes per step",
-                         "kernel": "decode_kernel", "alg_bytes_per_step": db},
+                         "kernel": "decode_kernel", "alg_bytes_per_step": db,
+                         "copy_ceiling_gbs": copy_gbs, "frac_of_copy": dgbs / copy_gbs},
         }
         del stg, S, S_save
 
