@@ -514,20 +514,24 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_seg_kernel(
 // stage's exports), the state gradient at the chunk's start is
 //   dS_start = Diag(gamma) dS_end + Q~^T dO - K~^T Tm^T (Kdec dS_end + Aqk^T dO)
 // (the chunk equations differentiated; the same recurrence the token-level
-// reverse sweep runs 16 steps at a time).  One workgroup of 256 threads per
-// (b, h, 16 value columns); per chunk three small products through LDS.
+// reverse sweep runs 16 steps at a time).  One workgroup of kBwdChainThreads per
+// (b, h, 16 value columns); per chunk three small products through LDS, the
+// inputs of chunks n - 1 .. n - 4 loading meanwhile.
 // Writes dSend[(u * NC + n)] = the gradient of chunk n's end state.
 template <typename E, int D>
-__global__ __launch_bounds__(256) void bwd_chain_kernel(
+__global__ __launch_bounds__(kBwdChainThreads) void bwd_chain_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ Gc,
     const float* __restrict__ Tm, const float* __restrict__ Aqk, const float* __restrict__ gam,
     const E* __restrict__ dO, const float* __restrict__ dST, float* __restrict__ dSend, int T,
     int H) {
+    constexpr int NT = kBwdChainThreads;
     constexpr int CB = 16;                  // value columns per workgroup
-    constexpr int TPR = 256 / D;            // threads per state row
+    constexpr int TPR = NT / D;             // threads per state row
     constexpr int CPT = CB / TPR;           // state columns per thread
-    constexpr int FE = kChunk * D / 256;    // factor elements per thread
+    constexpr int FE = kChunk * D / NT;     // factor elements per thread
     constexpr int DP = D + 4;               // padded row (16-byte aligned rows)
+    static_assert(CPT >= 1 && FE >= 1, "thread layout");
+    constexpr int kAhead = 4;               // chunks of inputs in flight
     __shared__ __attribute__((aligned(16))) float sKd[kChunk][DP];
     __shared__ __attribute__((aligned(16))) float sKt[kChunk][DP];
     __shared__ __attribute__((aligned(16))) float sQt[kChunk][DP];
@@ -541,12 +545,13 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(
     const int b = (int)(u / (size_t)H), h = (int)(u % (size_t)H);
     const int NC = (T + kChunk - 1) / kChunk;
     const int c = tid / TPR, j0 = (tid % TPR) * CPT;   // state entries: row c, columns j0 ..
-    const int zr = tid / CB, zj = tid % CB;            // 16x16 products: row zr, column zj
+    const bool zt = tid < 256;                         // threads of the 16x16 products
+    const int zr = (tid & 255) / CB, zj = tid % CB;
     const size_t col0 = (size_t)ct * CB;
     float dS[CPT];
 #pragma unroll
     for (int x = 0; x < CPT; ++x) dS[x] = dST ? dST[(u * D + c) * D + col0 + j0 + x] : 0.f;
-    // one chunk's inputs, loaded a chunk ahead
+    // one chunk's inputs in registers, loaded two chunks ahead of use
     struct In {
         float k[FE], q[FE], g[FE], gm[FE];
         float tm, aq, dO, gg;
@@ -556,7 +561,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(
         const size_t cidx = u * NC + n;
 #pragma unroll
         for (int x = 0; x < FE; ++x) {
-            const int e = tid + 256 * x, r = e / D, cc = e % D;
+            const int e = tid + NT * x, r = e / D, cc = e % D;
             if (r < L) {
                 const size_t i = (((size_t)b * T + cs + r) * H + h) * D + cc;
                 in.k[x] = to_f32(k[i]);
@@ -567,52 +572,59 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(
             }
             in.gm[x] = gam[cidx * D + cc];
         }
-        in.tm = Tm[cidx * 256 + tid];
-        in.aq = Aqk[cidx * 256 + tid];
-        in.dO = zr < L ? to_f32(dO[(((size_t)b * T + cs + zr) * H + h) * D + col0 + zj]) : 0.f;
+        if (zt) {
+            in.tm = Tm[cidx * 256 + tid];
+            in.aq = Aqk[cidx * 256 + tid];
+            in.dO = zr < L ? to_f32(dO[(((size_t)b * T + cs + zr) * H + h) * D + col0 + zj]) : 0.f;
+        }
         in.gg = tid < D ? gam[cidx * D + tid] : 0.f;
     };
-    In cur, nxt;
-    load(NC - 1, cur);
-    for (int n = NC - 1; n >= 0; --n) {
+    // chunk n from `cur`, whose registers then take chunk n - kAhead's inputs
+    auto step = [&](int n, In& cur) {
         const size_t cidx = u * NC + n;
         // the chunk's factors into LDS (rows past its end are zero)
 #pragma unroll
         for (int x = 0; x < FE; ++x) {
-            const int e = tid + 256 * x, r = e / D, cc = e % D;
+            const int e = tid + NT * x, r = e / D, cc = e % D;
             const float ex = expf(cur.g[x]);
             sKt[r][cc] = cur.k[x] * ex;
             sQt[r][cc] = cur.q[x] * ex;
-            sKd[r][cc] = ex > 0.f ? cur.k[x] * (cur.gm[x] / ex) : 0.f;
+            sKd[r][cc] = cur.k[x] * (cur.gm[x] / ex);
         }
-        sTm[zr][zj] = cur.tm;
-        sAq[zr][zj] = cur.aq;
-        sdO[zr][zj] = cur.dO;
+        if (zt) {
+            sTm[zr][zj] = cur.tm;
+            sAq[zr][zj] = cur.aq;
+            sdO[zr][zj] = cur.dO;
+        }
         if (tid < D) sg[tid] = cur.gg;
 #pragma unroll
         for (int x = 0; x < CPT; ++x) {
             sST[j0 + x][c] = dS[x];
             dSend[(cidx * D + c) * D + col0 + j0 + x] = dS[x];
         }
-        if (n > 0) load(n - 1, nxt);
+        if (n >= kAhead) load(n - kAhead, cur);
         __syncthreads();
         // Z = Kdec dS_end + Aqk^T dO
-        float z = 0.f;
+        if (zt) {
+            float z = 0.f;
 #pragma unroll 4
-        for (int cc = 0; cc < D; cc += 4) {
-            const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sKd[zr][cc]);
-            const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sST[zj][cc]);
-            z += a4[0] * s4[0] + a4[1] * s4[1] + a4[2] * s4[2] + a4[3] * s4[3];
-        }
+            for (int cc = 0; cc < D; cc += 4) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sKd[zr][cc]);
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sST[zj][cc]);
+                z += a4[0] * s4[0] + a4[1] * s4[1] + a4[2] * s4[2] + a4[3] * s4[3];
+            }
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) z += sAq[i][zr] * sdO[i][zj];
-        sZ[zr][zj] = z;
+            for (int i = 0; i < kChunk; ++i) z += sAq[i][zr] * sdO[i][zj];
+            sZ[zr][zj] = z;
+        }
         __syncthreads();
         // Y = Tm^T Z
-        float y = 0.f;
+        if (zt) {
+            float y = 0.f;
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) y += sTm[i][zr] * sZ[i][zj];
-        sY[zr][zj] = y;
+            for (int i = 0; i < kChunk; ++i) y += sTm[i][zr] * sZ[i][zj];
+            sY[zr][zj] = y;
+        }
         __syncthreads();
         // dS_start = Diag(gamma) dS_end + Q~^T dO - K~^T Y (row c, columns j0 ..)
         const float gc = sg[c];
@@ -625,7 +637,17 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(
             for (int x = 0; x < CPT; ++x) dS[x] += qr * sdO[r][j0 + x] - kr * sY[r][j0 + x];
         }
         __syncthreads();   // before the next chunk's factors overwrite LDS
-        if (n > 0) cur = nxt;
+    };
+    In r0, r1, r2, r3;   // chunks n, n - 1, n - 2, n - 3 (static register sets)
+    load(NC - 1, r0);
+    if (NC >= 2) load(NC - 2, r1);
+    if (NC >= 3) load(NC - 3, r2);
+    if (NC >= 4) load(NC - 4, r3);
+    for (int n = NC - 1; n >= 0; n -= kAhead) {
+        step(n, r0);
+        if (n >= 1) step(n - 1, r1);
+        if (n >= 2) step(n - 2, r2);
+        if (n >= 3) step(n - 3, r3);
     }
 }
 
@@ -825,7 +847,8 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
         if ((e = launch_intra_diag(a.q, a.k, a.z, a.beta, a.A, a.g_min, Tm, Aqk, gam, a.B, a.T, a.H,
                                    D, sizeof(E) == 2, stream)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL((bwd_chain_kernel<E, D>), dim3((unsigned)(units * (D / 16))), dim3(256),
+        hipLaunchKernelGGL((bwd_chain_kernel<E, D>), dim3((unsigned)(units * (D / 16))),
+                           dim3(kBwdChainThreads),
                            0, stream, q, k, Gc, Tm, Aqk, gam, (const E*)a.dO, a.dST,
                            (float*)(ws + L.dSend), a.T, a.H);
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -94,6 +94,8 @@ struct BackwardArgs {
 constexpr int kBwdCols = 8;
 constexpr int kBwdTokBlock = 16;
 constexpr size_t kBwdPartialBudget = (size_t)256 << 20;
+// Threads of a chunk-level chain workgroup (16 value columns of one head).
+constexpr int kBwdChainThreads = 512;
 // Recompute window (tokens) of the chunk-parallel reverse sweep.
 constexpr int kBwdHistPar = 4;
 // Fewest tokens of one reverse-sweep launch (a multiple of kBwdTokBlock).
