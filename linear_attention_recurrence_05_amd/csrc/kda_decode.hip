@@ -13,8 +13,8 @@
 // The step is HBM-bound (S is read and written once: 2 * 4 * d_k * d_v bytes
 // against ~7 d_k d_v flops), so the kernel is laid out for streaming: one
 // workgroup per (b, h); each thread owns 4 adjacent value columns of
-// RPT = d_k / 8 key rows, so every wave instruction moves 1 KiB (d = 128) of
-// S with 16-byte accesses.  S is held in registers between the read and the
+// RPT key rows (8 for d = 128, over 512 threads), so every wave instruction
+// moves 1 KiB (d = 128) of S with 16-byte accesses.  S is held in registers between the read and the
 // write, the two reductions come from the same read, and the update is
 // written back with non-temporal stores.
 #include "kda_device.hpp"
@@ -22,17 +22,16 @@
 
 namespace kda {
 
-template <typename E, int D>
-__global__ __launch_bounds__(2 * D) void decode_kernel(
+template <typename E, int D, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
     float g_min, StateIO io, E* __restrict__ o, int H) {
-    constexpr int NT = 2 * D;          // threads
     constexpr int CG = D / 4;          // column groups of 4 (float4)
-    constexpr int RG = NT / CG;        // row groups (= 8)
+    constexpr int RG = NT / CG;        // row groups
     constexpr int RPT = D / RG;        // rows per thread
     constexpr int NWAVE = NT / kWave;
-    static_assert(RG == 8, "layout assumes 8 row groups");
+    static_assert(NT % CG == 0 && D % RG == 0 && CG <= kWave, "decode layout");
 
     __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
     __shared__ float s_red[NWAVE][CG][9];
@@ -43,18 +42,16 @@ __global__ __launch_bounds__(2 * D) void decode_kernel(
     const size_t vec = unit * (size_t)D;
     if (io.skip(bi)) return;           // uniform over the workgroup
 
-    if (tid < D) {
-        GateConsts gc = make_gate(A[h], g_min);
-        float zz = to_f32(z[vec + tid]);
-        s_alpha[tid] = gate_alpha(gc, gate_sigmoid(gc, zz));
-        s_k[tid] = to_f32(k[vec + tid]);
-        s_q[tid] = to_f32(q[vec + tid]);
-        s_v[tid] = to_f32(v[vec + tid]);
-    }
-    __syncthreads();
-
     const int cg = tid % CG, rg = tid / CG;
     f32x4* Sv = reinterpret_cast<f32x4*>(io.out_at(bi, h, H, D));   // in place: in == out
+    const GateConsts gc = make_gate(A[h], g_min);
+    for (int c = tid; c < D; c += NT) {
+        s_alpha[c] = gate_alpha(gc, gate_sigmoid(gc, to_f32(z[vec + c])));
+        s_k[c] = to_f32(k[vec + c]);
+        s_q[c] = to_f32(q[vec + c]);
+        s_v[c] = to_f32(v[vec + c]);
+    }
+    __syncthreads();
     f32x4 st[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&Sv[(rg + RG * i) * CG + cg]);
@@ -99,7 +96,8 @@ __global__ __launch_bounds__(2 * D) void decode_kernel(
     for (int x = 0; x < 4; ++x) e[x] = b * (s_v[4 * cg + x] - tot[x]);
     if (rg == 0) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) o[vec + 4 * cg + x] = from_f32<E>(tot[4 + x] + tot[8] * e[x]);
+        for (int x = 0; x < 4; ++x)
+            o[vec + 4 * cg + x] = from_f32<E>(tot[4 + x] + tot[8] * e[x]);
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -116,17 +114,16 @@ __global__ __launch_bounds__(2 * D) void decode_kernel(
 // rejected draft is replayed from).  Same layout and per-token arithmetic as decode_kernel,
 // with S kept in registers across the tokens: S is read and written once
 // for all T tokens.  Three workgroup barriers per token.
-template <typename E, int D>
-__global__ __launch_bounds__(2 * D) void tokens_kernel(
+template <typename E, int D, int NT>
+__global__ __launch_bounds__(NT) void tokens_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
     float g_min, StateIO io, E* __restrict__ o, int T, int H) {
-    constexpr int NT = 2 * D;
     constexpr int CG = D / 4;
     constexpr int RG = NT / CG;
     constexpr int RPT = D / RG;
     constexpr int NWAVE = NT / kWave;
-    static_assert(RG == 8, "layout assumes 8 row groups");
+    static_assert(NT % CG == 0 && D % RG == 0 && NT >= D && CG <= kWave, "tokens layout");
 
     __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
     __shared__ float s_red[NWAVE][CG][9];
@@ -203,13 +200,24 @@ __global__ __launch_bounds__(2 * D) void tokens_kernel(
     for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(st[i], &So[(rg + RG * i) * CG + cg]);
 }
 
-template <typename E, int D>
-static hipError_t launch_tokens_t(const TokensArgs& a, hipStream_t stream) {
+template <typename E, int D, int NT>
+static hipError_t launch_tokens_v(const TokensArgs& a, hipStream_t stream) {
     const size_t units = (size_t)a.B * a.H;
-    hipLaunchKernelGGL((tokens_kernel<E, D>), dim3((unsigned)units), dim3(2 * D), 0, stream,
+    hipLaunchKernelGGL((tokens_kernel<E, D, NT>), dim3((unsigned)units), dim3(NT), 0, stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.z, a.beta, a.A,
                        a.g_min, a.S, (E*)a.o, a.T, a.H);
     return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t launch_tokens_t(const TokensArgs& a, hipStream_t stream) {
+    if constexpr (D == 32) {
+        return launch_tokens_v<E, D, 2 * D>(a, stream);
+    } else {
+        // 512 threads (as the single-token step) was 8-10% slower here: the
+        // per-token barriers span twice the waves.
+        return launch_tokens_v<E, D, 2 * D>(a, stream);
+    }
 }
 
 hipError_t launch_tokens(const TokensArgs& a, hipStream_t stream) {
@@ -219,13 +227,23 @@ hipError_t launch_tokens(const TokensArgs& a, hipStream_t stream) {
     return a.d == 128 ? launch_tokens_t<float, 128>(a, stream) : launch_tokens_t<float, 32>(a, stream);
 }
 
+template <typename E, int D, int NT>
+static hipError_t launch_decode_v(const DecodeArgs& a, hipStream_t stream) {
+    const size_t units = (size_t)a.B * a.H;
+    hipLaunchKernelGGL((decode_kernel<E, D, NT>), dim3((unsigned)units),
+                       dim3(NT), 0, stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
+                       (const E*)a.z, a.beta, a.A, a.g_min, a.S, (E*)a.o, a.H);
+    return hipGetLastError();
+}
+
+// d = 128: 512 threads of 8 rows each (68 VGPRs, seven waves per SIMD);
+// d = 32: 64 threads.
 template <typename E, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    const size_t units = (size_t)a.B * a.H;
-    hipLaunchKernelGGL((decode_kernel<E, D>), dim3((unsigned)units), dim3(2 * D), 0, stream,
-                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.z, a.beta, a.A,
-                       a.g_min, a.S, (E*)a.o, a.H);
-    return hipGetLastError();
+    if constexpr (D == 32)
+        return launch_decode_v<E, D, 2 * D>(a, stream);
+    else
+        return launch_decode_v<E, D, 4 * D>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
