@@ -142,9 +142,10 @@ size_t kda_chunk_prefill_segmented_workspace_bytes(int B, int T, int H, int d_k,
  * = 0 from S0 = I; v from S0 = 0); a scan gives every segment's start state
  * and S_T; a last prefill from those start states writes o.  Same arguments,
  * layouts, aliasing rules and results (up to rounding) as kda_chunk_prefill;
- * the chunk grid restarts at every segment start.  It costs three prefill
- * passes plus the scan, and is the building block of a prefill split across
- * devices by sequence position.
+ * the chunk grid restarts at every segment start.  It costs three passes
+ * over the tokens plus the scan (the two map passes read neither q nor, for
+ * M, v and write no o where B * n_seg * H >= 128 and d = 128), and is the
+ * building block of a prefill split across devices by sequence position.
  *   workspace : at least kda_chunk_prefill_segmented_workspace_bytes(...)
  *               bytes (never NULL). */
 kda_status kda_chunk_prefill_segmented(const void *q, const void *k,

@@ -795,8 +795,12 @@ BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     }
     L.segws = L.oscr = 0;
     if (L.R > 1) {
-        L.segws = take(seg_layout(B, T, H, d, is_bf16, L.R).total);
-        L.oscr = take((size_t)B * T * H * d * (is_bf16 ? 2 : 4));
+        // the segment scan's passes write no outputs where the plan allows
+        // it; otherwise they need a scratch o
+        const SegLayout SL = seg_layout(B, T, H, d, is_bf16, L.R);
+        L.segws = take(SL.total);
+        if (!prefill_state_only_ok(SL.inner, d))
+            L.oscr = take((size_t)B * T * H * d * (is_bf16 ? 2 : 4));
     }
     L.total = off;
     return L;

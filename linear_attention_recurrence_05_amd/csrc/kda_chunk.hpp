@@ -175,7 +175,8 @@ __device__ __forceinline__ void unpack_seg(const uint32_t (&w)[NW], float (&f)[N
     }
 }
 
-template <typename E, int D>
+// WQ = false: q is not read (a pass that produces only the end state).
+template <typename E, int D, bool WQ = true>
 __device__ __forceinline__ void prod_load(ProdIn<E, D>& in, const E* __restrict__ q,
                                           const E* __restrict__ k, const E* __restrict__ z,
                                           const float* __restrict__ beta, const ChunkPos& c) {
@@ -190,7 +191,7 @@ __device__ __forceinline__ void prod_load(ProdIn<E, D>& in, const E* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int off = c0 * ES + r * rowb;
-        load_seg<E, B::NCL>(rq, off, in.q[r]);
+        if constexpr (WQ) load_seg<E, B::NCL>(rq, off, in.q[r]);
         load_seg<E, B::NCL>(rk, off, in.k[r]);
         load_seg<E, B::NCL>(rz, off, in.z[r]);
     }
@@ -204,7 +205,8 @@ __device__ __forceinline__ void prod_load(ProdIn<E, D>& in, const E* __restrict_
 // Gate + intra-chunk stage of one chunk (one wave).  Writes the factor block
 // `blk` (LDS) using the wave-private scratch `scr` (LDS).  With DIAG, fp32
 // copies of Tm [16][16], Aqk [16][16] and gam [D] also go to dTm, dAqk, dgam.
-template <typename E, int D, bool DIAG>
+// WQ = false: the output factors (Qt, Aqk) are neither formed nor written.
+template <typename E, int D, bool DIAG, bool WQ = true>
 __device__ __forceinline__ void prod_compute(const ProdIn<E, D>& in, const GateConsts& gc,
                                              char* __restrict__ blk, char* __restrict__ scr,
                                              float* dTm, float* dAqk, float* dgam) {
@@ -249,12 +251,12 @@ __device__ __forceinline__ void prod_compute(const ProdIn<E, D>& in, const GateC
     for (int r = 0; r < 16; ++r) {
         float kf[NCL], qf[NCL];
         unpack_seg<E, NCL, B::NWORD>(in.k[r], kf);
-        unpack_seg<E, NCL, B::NWORD>(in.q[r], qf);
+        if constexpr (WQ) unpack_seg<E, NCL, B::NWORD>(in.q[r], qf);
         float kt[NCL], qt[NCL], kh[NCL];
 #pragma unroll
         for (int e = 0; e < NCL; ++e) {
             kt[e] = kf[e] * P[r][e];
-            qt[e] = qf[e] * P[r][e];
+            qt[e] = WQ ? qf[e] * P[r][e] : 0.f;
             const float kd = kf[e] * Qs[r][e];
             kh[e] = kd * rgam[e];
             Qs[r][e] = kd;                          // keep Kd for the transposed tile
@@ -264,15 +266,15 @@ __device__ __forceinline__ void prod_compute(const ProdIn<E, D>& in, const GateC
             if constexpr (NCL == 2 && B::kBF16) {
                 bf16x2 a{(bf16)kt[0], (bf16)kt[1]}, b{(bf16)qt[0], (bf16)qt[1]}, c{(bf16)kh[0], (bf16)kh[1]};
                 *reinterpret_cast<bf16x2*>(blk + B::KT + off) = a;
-                *reinterpret_cast<bf16x2*>(blk + B::QT + off) = b;
+                if constexpr (WQ) *reinterpret_cast<bf16x2*>(blk + B::QT + off) = b;
                 *reinterpret_cast<bf16x2*>(scr + B::SCR_KH + off) = c;
             } else if constexpr (NCL == 2) {
                 *reinterpret_cast<f32x2*>(blk + B::KT + off) = f32x2{kt[0], kt[1]};
-                *reinterpret_cast<f32x2*>(blk + B::QT + off) = f32x2{qt[0], qt[1]};
+                if constexpr (WQ) *reinterpret_cast<f32x2*>(blk + B::QT + off) = f32x2{qt[0], qt[1]};
                 *reinterpret_cast<f32x2*>(scr + B::SCR_KH + off) = f32x2{kh[0], kh[1]};
             } else {
                 *reinterpret_cast<E*>(blk + B::KT + off) = from_f32<E>(kt[0]);
-                *reinterpret_cast<E*>(blk + B::QT + off) = from_f32<E>(qt[0]);
+                if constexpr (WQ) *reinterpret_cast<E*>(blk + B::QT + off) = from_f32<E>(qt[0]);
                 *reinterpret_cast<E*>(scr + B::SCR_KH + off) = from_f32<E>(kh[0]);
             }
         }
@@ -299,16 +301,20 @@ __device__ __forceinline__ void prod_compute(const ProdIn<E, D>& in, const GateC
     for (int s = 0; s < B::NSLOT; ++s) {
         const int off = B::arow_chunk(s, g, ci);
         const V16<E> kt = *reinterpret_cast<const V16<E>*>(blk + B::KT + off);
-        const V16<E> qt = *reinterpret_cast<const V16<E>*>(blk + B::QT + off);
         const V16<E> kh = *reinterpret_cast<const V16<E>*>(scr + B::SCR_KH + off);
         if constexpr (B::kBF16) {
             akk = mma_bf16_k32(kt, kh, akk);
-            aqk = mma_bf16_k32(qt, kh, aqk);
+            if constexpr (WQ) {
+                const V16<E> qt = *reinterpret_cast<const V16<E>*>(blk + B::QT + off);
+                aqk = mma_bf16_k32(qt, kh, aqk);
+            }
         } else {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                akk = mma_f32_k4(kt[p], kh[p], akk);
-                aqk = mma_f32_k4(qt[p], kh[p], aqk);
+            for (int p = 0; p < 4; ++p) akk = mma_f32_k4(kt[p], kh[p], akk);
+            if constexpr (WQ) {
+                const V16<E> qt = *reinterpret_cast<const V16<E>*>(blk + B::QT + off);
+#pragma unroll
+                for (int p = 0; p < 4; ++p) aqk = mma_f32_k4(qt[p], kh[p], aqk);
             }
         }
     }
@@ -319,11 +325,13 @@ __device__ __forceinline__ void prod_compute(const ProdIn<E, D>& in, const GateC
         const int r = 4 * g + p;
         const float br = __shfl(in.bj, r);
         akk_s[r * 16 + ci] = ci < r ? br * akk[p] : 0.f;
-        const float aq = ci <= r ? aqk[p] : 0.f;
-        // A layout for the 16x16x16 / 16x16x4 consumer: lane (r, ci/4), element ci%4
-        *reinterpret_cast<E*>(blk + B::AQ + ((ci >> 2) * 16 + r) * B::OPB + (ci & 3) * B::ES) =
-            from_f32<E>(aq);
-        if constexpr (DIAG) dAqk[r * 16 + ci] = aq;
+        if constexpr (WQ) {
+            const float aq = ci <= r ? aqk[p] : 0.f;
+            // A layout for the 16x16x16 / 16x16x4 consumer: lane (r, ci/4), element ci%4
+            *reinterpret_cast<E*>(blk + B::AQ + ((ci >> 2) * 16 + r) * B::OPB + (ci & 3) * B::ES) =
+                from_f32<E>(aq);
+            if constexpr (DIAG) dAqk[r * 16 + ci] = aq;
+        }
     }
     wave_sync_lds();
 
@@ -380,7 +388,8 @@ struct BufSrc {
     }
 };
 
-template <typename E, int D, typename Src>
+// WQ = false: the output factors (Qt, Aqk) are not read.
+template <typename E, int D, typename Src, bool WQ = true>
 __device__ __forceinline__ void cops_load(COps<E, D>& c, const Src& src) {
     using B = Blk<E, D>;
     const int lane = lane_id(), g = lane >> 4, r = lane & 15;
@@ -388,7 +397,7 @@ __device__ __forceinline__ void cops_load(COps<E, D>& c, const Src& src) {
     for (int s = 0; s < B::NSLOT; ++s) {
         const int off = B::arow_chunk(s, g, r);
         c.kt[s] = src.template ld<V16<E>>(B::KT + off);
-        c.qt[s] = src.template ld<V16<E>>(B::QT + off);
+        if constexpr (WQ) c.qt[s] = src.template ld<V16<E>>(B::QT + off);
     }
 #pragma unroll
     for (int m = 0; m < B::MT; ++m) {
@@ -396,7 +405,7 @@ __device__ __forceinline__ void cops_load(COps<E, D>& c, const Src& src) {
         c.gam[m] = src.template ld<f32x4>(B::GAM + (16 * m + 4 * g) * 4);
     }
     c.tm = src.template ld<V4<E>>(B::TM + lane * B::OPB);
-    c.aq = src.template ld<V4<E>>(B::AQ + lane * B::OPB);
+    if constexpr (WQ) c.aq = src.template ld<V4<E>>(B::AQ + lane * B::OPB);
 }
 
 // V of one chunk for NB 16-column blocks, accumulator layout (rows 4g + p),
@@ -446,8 +455,9 @@ __device__ __forceinline__ void o_store(const f32x4 (&O)[NB], E* __restrict__ o,
         }
 }
 
-// One chunk of the state chain for NB 16-column blocks of S.
-template <typename E, int D, int NB>
+// One chunk of the state chain for NB 16-column blocks of S.  WQ = false:
+// the state only (O is left unset).
+template <typename E, int D, int NB, bool WQ = true>
 __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D / 16],
                                            const f32x4 (&Vf)[NB], f32x4 (&O)[NB]) {
     using B = Blk<E, D>;
@@ -460,7 +470,7 @@ __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D
             for (int s = 0; s < B::NSLOT; ++s) {
                 const bf16x8 sb = pack8(S[nb][2 * s], S[nb][2 * s + 1]);
                 x = mma_bf16_k32(c.kt[s], sb, x);      // Kt S
-                o = mma_bf16_k32(c.qt[s], sb, o);      // Qt S
+                if constexpr (WQ) o = mma_bf16_k32(c.qt[s], sb, o);      // Qt S
             }
             const f32x4 y = V - x;
             const f32x4 u = mma_bf16_k16(c.tm, pack4(y), zero4());   // U = Tm (V - Kt S)
@@ -468,7 +478,7 @@ __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D
             // Aqk U goes to its own accumulator: an MFMA of one shape must not
             // take as srcC the result of an MFMA of another shape still in
             // flight (16x16x32 -> 16x16x16 chains read stale srcC on gfx950).
-            o += mma_bf16_k16(c.aq, ub, zero4());                    // + Aqk U
+            if constexpr (WQ) o += mma_bf16_k16(c.aq, ub, zero4());  // + Aqk U
 #pragma unroll
             for (int m = 0; m < B::MT; ++m)
                 S[nb][m] = mma_bf16_k16(c.kd[m], ub, S[nb][m] * c.gam[m]);  // Diag(gam) S + Kd^T U
@@ -478,14 +488,16 @@ __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     x = mma_f32_k4(c.kt[m][p], S[nb][m][p], x);
-                    o = mma_f32_k4(c.qt[m][p], S[nb][m][p], o);
+                    if constexpr (WQ) o = mma_f32_k4(c.qt[m][p], S[nb][m][p], o);
                 }
             const f32x4 y = V - x;
             f32x4 u = zero4();
 #pragma unroll
             for (int p = 0; p < 4; ++p) u = mma_f32_k4(c.tm[p], y[p], u);
+            if constexpr (WQ) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) o = mma_f32_k4(c.aq[p], u[p], o);
+                for (int p = 0; p < 4; ++p) o = mma_f32_k4(c.aq[p], u[p], o);
+            }
 #pragma unroll
             for (int m = 0; m < B::MT; ++m) {
                 f32x4 s = S[nb][m] * c.gam[m];
@@ -494,7 +506,7 @@ __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D
                 S[nb][m] = s;
             }
         }
-        O[nb] = o;
+        if constexpr (WQ) O[nb] = o;
     }
 }
 

@@ -136,6 +136,9 @@ static_assert(kSegChunks % 2 == 0, "segments hold whole pairs of chunks");
 
 // Chosen execution plan for these sizes (pure function of the sizes).
 PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16);
+// Whether launch_prefill runs this plan as a state-only pass: a null o (no
+// outputs; q is not read) and optionally a null v (v taken as zero).
+bool prefill_state_only_ok(const PlanInfo& p, int d);
 // Bytes of one two-chunk factor block of the split plan.
 size_t pair_block_bytes(int d, bool is_bf16);
 // Whether the split plan compiles an inter kernel with ncol value columns per

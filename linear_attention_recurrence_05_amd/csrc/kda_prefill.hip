@@ -112,8 +112,9 @@ struct FusedCfg {
 // Step m: the producers fill ring half (m+1)&1 with the next NPROD chunks
 // while the consumers run the state chain over half m&1.  Each role runs its
 // own loop (so neither keeps the other's registers live); both execute
-// 1 + NM barriers.
-template <typename E, int D, int NB, int NCW>
+// 1 + NM barriers.  WQ = false: only the end state (q and o are not
+// touched); VZ: v is taken as zero (v is not read).
+template <typename E, int D, int NB, int NCW, bool WQ = true, bool VZ = false>
 __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ v, const E* __restrict__ z,
                                                     const float* __restrict__ beta,
@@ -139,19 +140,23 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
         ProdIn<E, D> cur, nxt;
         cur.L = 0;
         nxt.L = 0;
-        if (w < NC) prod_load<E, D>(cur, q, k, z, beta, chunk_pos<D>(b, h, w, T, H));
-        if (NPROD + w < NC) prod_load<E, D>(nxt, q, k, z, beta, chunk_pos<D>(b, h, NPROD + w, T, H));
+        if (w < NC) prod_load<E, D, WQ>(cur, q, k, z, beta, chunk_pos<D>(b, h, w, T, H));
+        if (NPROD + w < NC)
+            prod_load<E, D, WQ>(nxt, q, k, z, beta, chunk_pos<D>(b, h, NPROD + w, T, H));
         if (cur.L > 0)
-            prod_compute<E, D, false>(cur, gc, smem + w * Bk::BYTES, myscr, nullptr, nullptr, nullptr);
+            prod_compute<E, D, false, WQ>(cur, gc, smem + w * Bk::BYTES, myscr, nullptr, nullptr,
+                                          nullptr);
         wg_barrier();
         for (int m = 0; m < NM; ++m) {
             cur = nxt;
             nxt.L = 0;
             const int n_next = (m + 2) * NPROD + w;
-            if (n_next < NC) prod_load<E, D>(nxt, q, k, z, beta, chunk_pos<D>(b, h, n_next, T, H));
+            if (n_next < NC)
+                prod_load<E, D, WQ>(nxt, q, k, z, beta, chunk_pos<D>(b, h, n_next, T, H));
             if (cur.L > 0)
-                prod_compute<E, D, false>(cur, gc, smem + (((m + 1) & 1) * NPROD + w) * Bk::BYTES,
-                                          myscr, nullptr, nullptr, nullptr);
+                prod_compute<E, D, false, WQ>(cur, gc,
+                                              smem + (((m + 1) & 1) * NPROD + w) * Bk::BYTES,
+                                              myscr, nullptr, nullptr, nullptr);
             wg_barrier();
         }
         return;
@@ -169,34 +174,40 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
     constexpr int ES = (int)sizeof(E);
     u32x4 Vc[NPROD][NB], Vn[NPROD][NB];
     state_load<D, NB>(S, io.in_at(b, h, H, D), col0);
+    if constexpr (!VZ) {
 #pragma unroll
-    for (int cc = 0; cc < NPROD; ++cc)
-        if (cc < NC) v_load<D, NB>(Vc[cc], v, ES, chunk_pos<D>(b, h, cc, T, H), col0);
+        for (int cc = 0; cc < NPROD; ++cc)
+            if (cc < NC) v_load<D, NB>(Vc[cc], v, ES, chunk_pos<D>(b, h, cc, T, H), col0);
+    }
     wg_barrier();
     for (int m = 0; m < NM; ++m) {
+        if constexpr (!VZ) {
 #pragma unroll
-        for (int cc = 0; cc < NPROD; ++cc) {
-            const int nn = (m + 1) * NPROD + cc;
-            if (nn < NC) v_load<D, NB>(Vn[cc], v, ES, chunk_pos<D>(b, h, nn, T, H), col0);
+            for (int cc = 0; cc < NPROD; ++cc) {
+                const int nn = (m + 1) * NPROD + cc;
+                if (nn < NC) v_load<D, NB>(Vn[cc], v, ES, chunk_pos<D>(b, h, nn, T, H), col0);
+            }
         }
 #pragma unroll
         for (int cc = 0; cc < NPROD; ++cc) {
             const int n = m * NPROD + cc;
             if (n < NC) {
                 COps<E, D> c;
-                cops_load<E, D>(c, LdsSrc{smem + ((m & 1) * NPROD + cc) * Bk::BYTES});
+                cops_load<E, D, LdsSrc, WQ>(c, LdsSrc{smem + ((m & 1) * NPROD + cc) * Bk::BYTES});
                 f32x4 O[NB];
                 f32x4 Vf[NB];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) Vf[nb] = v_widen<E>(Vc[cc][nb]);
-                chunk_step<E, D, NB>(c, S, Vf, O);
-                o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n, T, H), col0);
+                for (int nb = 0; nb < NB; ++nb) Vf[nb] = VZ ? zero4() : v_widen<E>(Vc[cc][nb]);
+                chunk_step<E, D, NB, WQ>(c, S, Vf, O);
+                if constexpr (WQ) o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n, T, H), col0);
             }
         }
+        if constexpr (!VZ) {
 #pragma unroll
-        for (int cc = 0; cc < NPROD; ++cc)
+            for (int cc = 0; cc < NPROD; ++cc)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) Vc[cc][nb] = Vn[cc][nb];
+                for (int nb = 0; nb < NB; ++nb) Vc[cc][nb] = Vn[cc][nb];
+        }
         wg_barrier();
     }
     if (io.out) state_store<D, NB>(S, io.out_at(b, h, H, D), col0);
@@ -284,6 +295,33 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PlanInfo& p, void
     if (p.plan == Plan::kFused) {
         const int nct = D / p.ncol;
         const dim3 grid(grid_units(units, nct)), block(512);
+        if (!o || !v) {
+            // state-only passes (o null; v null = zero), d = 128 with 128 or
+            // 64 columns per workgroup (prefill_state_only_ok); a null v
+            // with outputs is not a pass any caller makes
+            if (D != 128 || o != nullptr || (p.ncol != 128 && p.ncol != 64))
+                return hipErrorInvalidValue;
+            if (p.ncol == 128) {
+                if (v)
+                    hipLaunchKernelGGL((fused_kernel<E, D, 2, 4, false, false>), grid, block, 0,
+                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
+                                       a.H, nct);
+                else
+                    hipLaunchKernelGGL((fused_kernel<E, D, 2, 4, false, true>), grid, block, 0,
+                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
+                                       a.H, nct);
+            } else {
+                if (v)
+                    hipLaunchKernelGGL((fused_kernel<E, D, 1, 4, false, false>), grid, block, 0,
+                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
+                                       a.H, nct);
+                else
+                    hipLaunchKernelGGL((fused_kernel<E, D, 1, 4, false, true>), grid, block, 0,
+                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
+                                       a.H, nct);
+            }
+            return hipGetLastError();
+        }
         if (p.ncol == 128 && D == 128)
             hipLaunchKernelGGL((fused_kernel<E, D, 2, 4>), grid, block, 0, stream, q, k, v, z, a.beta,
                                a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
@@ -300,6 +338,10 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PlanInfo& p, void
     }
     (void)ws;
     return hipErrorInvalidValue;   // the split plan runs through launch_split
+}
+
+bool prefill_state_only_ok(const PlanInfo& p, int d) {
+    return p.plan == Plan::kFused && d == 128 && (p.ncol == 128 || p.ncol == 64);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream) {

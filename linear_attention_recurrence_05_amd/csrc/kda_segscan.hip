@@ -16,10 +16,11 @@
 //   S_in(0) = S0,   S_in(r + 1) = M_r S_in(r) + N_r,   S_T = S_in(R),
 // and a last prefill of all segments from their start states writes o.  On
 // P GPUs each would hold one segment and all-gather the (M_r, N_r) pairs;
-// here the segments share one GPU, so the path costs three prefill passes
-// plus the scan, and its use on one GPU is more parallel work per launch
-// (B * R * H units instead of B * H) for sequences whose own chains are too
-// few to fill the chip.
+// here the segments share one GPU, so the path costs three passes over the
+// tokens plus the scan (the two map passes state-only where the plan has
+// such passes: no q, no outputs, and no v for M_r), and its use on one GPU
+// is more parallel work per launch (B * R * H units instead of B * H) for
+// sequences whose own chains are too few to fill the chip.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -116,7 +117,7 @@ SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R) {
         return o;
     };
     L.inner_ws = take(L.inner.ws_bytes);
-    L.vzero = take((size_t)B * T * H * d * es);
+    L.vzero = prefill_state_only_ok(L.inner, d) ? off : take((size_t)B * T * H * d * es);
     L.ident = take(states);
     L.M = take(states);
     L.N = take(states);
@@ -134,21 +135,27 @@ hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, cha
     float* Sin = (float*)(w + L.Sin);
     const int Bs = a.B * R, Ts = a.T / R;
     const size_t n_states = (size_t)Bs * a.H;
-    // v has d (a multiple of 32) elements per token-head: whole 16-byte words
-    const size_t vwords = (size_t)a.B * a.T * a.H * a.d * (a.is_bf16 ? 2 : 4) / 16;
-    size_t zblocks = (vwords + 255) / 256;
-    if (zblocks > 16384) zblocks = 16384;
-    hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream,
-                       (u32x4*)(w + L.vzero), vwords);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // Plans that have state-only passes skip q, o and (for M_r) v; the others
+    // run ordinary prefills with a zero v buffer and o as scratch.
+    const bool state_only = prefill_state_only_ok(L.inner, a.d);
+    hipError_t e;
+    if (!state_only) {
+        // v has d (a multiple of 32) elements per token-head: whole 16-byte words
+        const size_t vwords = (size_t)a.B * a.T * a.H * a.d * (a.is_bf16 ? 2 : 4) / 16;
+        size_t zblocks = (vwords + 255) / 256;
+        if (zblocks > 16384) zblocks = 16384;
+        hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream,
+                           (u32x4*)(w + L.vzero), vwords);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(identity_kernel, dim3(2048), dim3(256), 0, stream, ident, n_states, a.d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // M_r: v = 0 from the identity; N_r: v from zero.  o is scratch.
-    PrefillArgs pm{a.q, a.k, w + L.vzero, a.z, a.beta, a.A, a.g_min, dense_state(ident, M), a.o,
-                   Bs, Ts, a.H, a.d, a.is_bf16};
+    // M_r: v = 0 from the identity; N_r: v from zero.
+    void* o_scr = state_only ? nullptr : a.o;
+    PrefillArgs pm{a.q, a.k, state_only ? nullptr : (const void*)(w + L.vzero), a.z, a.beta, a.A,
+                   a.g_min, dense_state(ident, M), o_scr, Bs, Ts, a.H, a.d, a.is_bf16};
     if ((e = launch_prefill(pm, L.inner, inner, stream)) != hipSuccess) return e;
-    PrefillArgs pn{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state(nullptr, N), a.o,
+    PrefillArgs pn{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state(nullptr, N), o_scr,
                    Bs, Ts, a.H, a.d, a.is_bf16};
     if ((e = launch_prefill(pn, L.inner, inner, stream)) != hipSuccess) return e;
     const unsigned grid = (unsigned)((size_t)a.B * a.H * (a.d / 16));

@@ -297,10 +297,10 @@ def test_backward_workspace_query():
     # the partial sums stay bounded as T grows (segments); the chunk-start
     # states and the per-token corrections grow with T
     n2 = kda.kda_chunk_backward_workspace_bytes(1, 8192, 32, 128, 128, kda.KDA_BF16)
-    # chunk-start states + corrections u, and for the segment-parallel forward
-    # sweep a zero v and a scratch o (bf16), for the 4096 extra tokens
-    # (256 chunks) of 32 heads
-    extra = 32 * 256 * 128 * 128 * 4 + 32 * 4096 * 128 * 4 + 2 * 32 * 4096 * 128 * 2
+    # chunk-start states + corrections u for the 4096 extra tokens (256
+    # chunks) of 32 heads; the segment scan behind the segment-parallel
+    # forward sweep runs state-only passes here (no zero v, no scratch o)
+    extra = 32 * 256 * 128 * 128 * 4 + 32 * 4096 * 128 * 4
     assert extra <= n2 - n <= extra + (1 << 20)
     # the chain plan adds the cumulative log-decay, Tm, Aqk, gamma and the
     # end-state gradient of every chunk
@@ -346,8 +346,11 @@ def test_segmented_rejects(over, code):
 def test_segmented_workspace_query():
     n1 = kda.kda_chunk_prefill_segmented_workspace_bytes(1, 4096, 32, 128, 128, 1, kda.KDA_BF16)
     n4 = kda.kda_chunk_prefill_segmented_workspace_bytes(1, 4096, 32, 128, 128, 4, kda.KDA_BF16)
-    # a zero value tensor of v's size, and four state tensors per segment
+    # one segment: 32 units run the split plan, whose passes need a zero value
+    # tensor of v's size; four state tensors per segment
     assert n1 >= 4096 * 32 * 128 * 2 + 4 * 32 * 128 * 128 * 4
-    assert n4 >= 4096 * 32 * 128 * 2 + 4 * 4 * 32 * 128 * 128 * 4
+    # four segments: 128 units run the fused plan's state-only passes (no zero
+    # v); the four state tensors per segment remain
+    assert 4 * 4 * 32 * 128 * 128 * 4 <= n4 < 4096 * 32 * 128 * 2 + 4 * 4 * 32 * 128 * 128 * 4
     assert kda.kda_chunk_prefill_segmented_workspace_bytes(1, 4096, 32, 128, 128, 3,
                                                            kda.KDA_BF16) == 0
