@@ -134,6 +134,9 @@ def main():
                                                              cfg.dtype)
     else:
         nb = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, cfg.dtype)
+    # segments the plain prefill entry point chooses by itself (1: direct plan)
+    auto_seg = 1 if args.segments > 1 else kda.kda_chunk_prefill_segments(B, T, H, d, d, cfg.dtype)
+    n_seg = args.segments if args.segments > 1 else auto_seg
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
     stream = torch.cuda.current_stream()
     # Cold inputs without a flush kernel: the steps cycle through n_rot copies
@@ -221,15 +224,18 @@ def main():
                    "S0": "zeros" if x["S0"] is None else "N(0, 0.01)",
                    "parallelism": "single GPU",
                    "plan": (f"segment scan over {args.segments} segments" if args.segments > 1
+                            else f"segment scan over {auto_seg} segments (chosen by "
+                                 "kda_chunk_prefill)" if auto_seg > 1
                             else ("split" if nb else "fused")),
                    "workspace_bytes": nb},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": (None if args.segments > 1 else measured_traffic(
+                     "traffic": (None if n_seg > 1 else measured_traffic(
                          f"prefill_{args.workload}_pass_bytes_{'split' if nb else 'fused'}")),
                      "traffic_unit": "bytes per pass",
-                     "kernel": ("segment-scan prefill (three prefill passes + segscan_kernel)"
-                                if args.segments > 1 else
+                     "kernel": ("segment-scan prefill (two map passes, segscan_kernel, one "
+                                "full prefill pass)"
+                                if n_seg > 1 else
                                 "prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
                                 else "prefill pass (fused_kernel)"),
                      "alg_bytes_per_step": alg_b,

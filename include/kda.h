@@ -97,6 +97,15 @@ const char *kda_last_error(void);
 size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v,
                                          kda_dtype dt);
 
+/* Segments kda_chunk_prefill splits each sequence into for these sizes: 1
+ * for a direct plan, R > 1 when it runs the segment scan of
+ * kda_chunk_prefill_segmented with n_seg = R (same context parallelism
+ * passage as there).  It does so for long sequences of few heads, where the
+ * heads' own state chains cannot fill the device: bf16 inputs, d = 128,
+ * T >= 65536, B * H <= 32, with B * R * H >= 128 and T / R >= 4096.  Returns
+ * 0 for arguments kda_chunk_prefill would reject. */
+int kda_chunk_prefill_segments(int B, int T, int H, int d_k, int d_v, kda_dtype dt);
+
 /* Chunkwise prefill over T tokens (any T >= 1; chunks of KDA_CHUNK tokens
  * start at t = 0 and the last may be short).  Computes o for every token and,
  * if S_T != NULL, the final state.
@@ -106,10 +115,13 @@ size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v,
  *   workspace       : device memory of at least
  *                     kda_chunk_prefill_workspace_bytes(...) bytes, used as
  *                     scratch for this call only (may be NULL if that is 0).
- * The execution plan (one fused kernel, or an intra-chunk kernel writing the
- * workspace followed by an inter-chunk kernel) is a function of the sizes.
- * For tests and tuning the environment variable KDA_PREFILL_PLAN overrides
- * it: "split" (default inter-chunk variant), "split:<n>:<b>" (n value
+ * The execution plan (one fused kernel, an intra-chunk kernel writing the
+ * workspace followed by an inter-chunk kernel, or the segment scan of
+ * kda_chunk_prefill_segmented with kda_chunk_prefill_segments(...) segments)
+ * is a function of the sizes; the segment scan restarts the chunk grid at
+ * every segment start, so results agree with the direct plans up to
+ * rounding.  For tests and tuning the environment variable KDA_PREFILL_PLAN
+ * overrides it (and then no segment scan is chosen): "split" (default inter-chunk variant), "split:<n>:<b>" (n value
  * columns per inter-chunk workgroup, b 16-column blocks per state chain:
  * b = 1 with n in {16, 32} or, for bf16 with d = 128, 64; b = 2 for bf16
  * with d = 128, n in {32, 64}), or "fused:<n>" with n value columns per

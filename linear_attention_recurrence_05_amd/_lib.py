@@ -38,6 +38,7 @@ _SIGNATURES = {
     "kda_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "kda_last_error": ([], ctypes.c_char_p),
     "kda_chunk_prefill_workspace_bytes": ([_i, _i, _i, _i, _i, _i], ctypes.c_size_t),
+    "kda_chunk_prefill_segments": ([_i, _i, _i, _i, _i, _i], _i),
     "kda_chunk_prefill": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6
                           + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "kda_decode_step": ([_vp] * 6 + [ctypes.c_float, _vp, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
@@ -118,6 +119,12 @@ def _require_contiguous(**tensors):
 def kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype) -> int:
     code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
     return int(lib().kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, code))
+
+
+def kda_chunk_prefill_segments(B, T, H, d_k, d_v, dtype) -> int:
+    """C entry point kda_chunk_prefill_segments (1: a direct plan)."""
+    code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+    return int(lib().kda_chunk_prefill_segments(B, T, H, d_k, d_v, code))
 
 
 def kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace=None, stream=None):

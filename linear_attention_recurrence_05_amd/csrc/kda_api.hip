@@ -145,10 +145,24 @@ const char* kda_status_string(kda_status s) {
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
+// Workspace of the dense prefill: the segment scan's when it runs one, else
+// the chosen plan's.
+static size_t prefill_ws_bytes(int B, int T, int H, int d, bool is_bf16, int R) {
+    return R > 1 ? kda::seg_layout(B, T, H, d, is_bf16, R).total
+                 : kda::choose_plan(B, T, H, d, is_bf16).ws_bytes;
+}
+
 size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, kda_dtype dt) {
     size_t a, b;
     if (check_common(d_k, d_v, dt, -5.0f) != KDA_OK || check_shape(B, T, H, d_k, a, b) != KDA_OK) return 0;
-    return kda::choose_plan(B, T, H, d_k, dt == KDA_BF16).ws_bytes;
+    const bool bf = dt == KDA_BF16;
+    return prefill_ws_bytes(B, T, H, d_k, bf, kda::auto_segments(B, T, H, d_k, bf));
+}
+
+int kda_chunk_prefill_segments(int B, int T, int H, int d_k, int d_v, kda_dtype dt) {
+    size_t a, b;
+    if (check_common(d_k, d_v, dt, -5.0f) != KDA_OK || check_shape(B, T, H, d_k, a, b) != KDA_OK) return 0;
+    return kda::auto_segments(B, T, H, d_k, dt == KDA_BF16);
 }
 
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* z,
@@ -161,17 +175,19 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     if ((s = check_shape(B, T, H, d_k, nel, ntok)) != KDA_OK) return s;
     const size_t es = dt == KDA_BF16 ? 2 : 4;
     const size_t st_bytes = (size_t)B * H * d_k * d_v * sizeof(float);
-    const kda::PlanInfo plan = kda::choose_plan(B, T, H, d_k, dt == KDA_BF16);
+    const bool bf = dt == KDA_BF16;
+    const int nseg = kda::auto_segments(B, T, H, d_k, bf);
+    const size_t need = prefill_ws_bytes(B, T, H, d_k, bf, nseg);
     const Range r[] = {{"q", q, nel * es, 16},          {"k", k, nel * es, 16},
                        {"v", v, nel * es, 16},          {"z", z, nel * es, 16},
                        {"beta", beta, ntok * 4, 4},     {"A", A, (size_t)H * 4, 4},
                        {"S0", S0, st_bytes, 4},         {"o", o, nel * es, 16},
-                       {"S_T", S_T, st_bytes, 4},       {"workspace", workspace, plan.ws_bytes, 16}};
-    const bool req[] = {true, true, true, true, true, true, false, true, false, plan.ws_bytes > 0};
+                       {"S_T", S_T, st_bytes, 4},       {"workspace", workspace, need, 16}};
+    const bool req[] = {true, true, true, true, true, true, false, true, false, need > 0};
     if ((s = check_ptrs(r, 10, req)) != KDA_OK) return s;
-    if (workspace_bytes < plan.ws_bytes)
+    if (workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes,
-                    plan.ws_bytes);
+                    need);
     // outputs (o, S_T, workspace) against every other range; S_T == S0 exactly is allowed
     for (int out : {7, 8, 9}) {
         for (int i = 0; i < 10; ++i) {
@@ -183,6 +199,10 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     }
     kda::PrefillArgs a{q, k, v, z, beta, A, g_min, kda::dense_state(S0, S_T), o, B, T, H, d_k,
                        dt == KDA_BF16};
+    if (nseg > 1)
+        return hip_status(kda::launch_segmented(a, nseg, workspace, (hipStream_t)stream),
+                          "kda_chunk_prefill launch (segment scan)");
+    const kda::PlanInfo plan = kda::choose_plan(B, T, H, d_k, bf);
     return hip_status(kda::launch_prefill(a, plan, workspace, (hipStream_t)stream), "kda_chunk_prefill launch");
 }
 

@@ -162,6 +162,9 @@ struct SegLayout {
 SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R);
 // a.S: dense S0 (in, may be null) and S_T (out, may be null).
 hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t stream);
+// Segments the dense prefill entry point uses by itself for these sizes (1:
+// none, the direct plan).
+int auto_segments(int B, int T, int H, int d, bool is_bf16);
 // The scan alone: the start state of every segment into the layout's Sin
 // region ([B * R, H, d, d]) and S_T into a.S.out (if set); a.o is scratch.
 hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, char* ws,

@@ -21,6 +21,7 @@
 // such passes: no q, no outputs, and no v for M_r), and its use on one GPU
 // is more parallel work per launch (B * R * H units instead of B * H) for
 // sequences whose own chains are too few to fill the chip.
+#include <cstdlib>
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -103,6 +104,25 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
 }
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Segments kda_chunk_prefill splits a sequence into by itself.  A head's state
+// chain runs its chunks one after another, so B * H heads of a long sequence
+// keep only B * H * d / 16 chains busy; with 32 or fewer heads and bf16
+// inputs at d = 128 the segment scan (R segments as B * R * H >= 128 units of
+// the fused plan, whose map passes are state-only) was measured faster from
+// 65,536 tokens on: 1.12-1.20x at B * H = 32 (R = 8), 1.26-1.70x at 16
+// (R = 16), and slower at 64 heads or below 4,096 tokens per segment.  A
+// plan forced by KDA_PREFILL_PLAN runs as forced (1: no segments).
+int auto_segments(int B, int T, int H, int d, bool is_bf16) {
+    if (std::getenv("KDA_PREFILL_PLAN")) return 1;
+    if (!is_bf16 || d != 128 || T < 65536) return 1;
+    const long units = (long)B * H;
+    if (units > 32) return 1;
+    int R = 1;
+    while (units * R * 2 <= 256) R *= 2;
+    while (R > 1 && (T % (kChunk * R) != 0 || T / R < 4096)) R /= 2;
+    return units * R >= 128 ? R : 1;
+}
 
 SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R) {
     SegLayout L;

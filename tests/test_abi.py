@@ -354,3 +354,33 @@ def test_segmented_workspace_query():
     assert 4 * 4 * 32 * 128 * 128 * 4 <= n4 < 4096 * 32 * 128 * 2 + 4 * 4 * 32 * 128 * 128 * 4
     assert kda.kda_chunk_prefill_segmented_workspace_bytes(1, 4096, 32, 128, 128, 3,
                                                            kda.KDA_BF16) == 0
+
+
+def test_prefill_segment_choice():
+    """Which sizes kda_chunk_prefill runs as a segment scan (host logic)."""
+    f = kda.kda_chunk_prefill_segments
+    bf, f32 = kda.KDA_BF16, kda.KDA_F32
+    assert f(1, 4096, 32, 128, 128, bf) == 1          # short: direct
+    assert f(1, 32768, 32, 128, 128, bf) == 1         # below 65,536 tokens
+    assert f(1, 65536, 32, 128, 128, bf) == 8         # 32 heads -> 256 units
+    assert f(1, 1048576, 32, 128, 128, bf) == 8
+    assert f(1, 65536, 16, 128, 128, bf) == 16
+    assert f(1, 65536, 24, 128, 128, bf) == 8         # 192 units
+    assert f(2, 65536, 32, 128, 128, bf) == 1         # 64 heads fill the chip
+    # 2 or 4 heads: at most 16 segments of >= 4,096 tokens, too few units
+    # (32, 64 < 128) for the fused plan's state-only passes: direct
+    assert f(1, 65536, 2, 128, 128, bf) == 1
+    assert f(1, 65536, 4, 128, 128, bf) == 1
+    assert f(1, 1048576, 2, 128, 128, bf) == 128      # 256 units of 8,192 tokens
+    assert f(1, 1048576, 32, 128, 128, f32) == 1      # fp32: direct
+    assert f(1, 1048576, 32, 32, 32, bf) == 1         # d = 32: direct
+    assert f(1, 65536 + 16, 32, 128, 128, bf) == 1    # T not a multiple of 16 R: direct
+    assert f(0, 65536, 32, 128, 128, bf) == 0         # rejected arguments
+    # the workspace query follows the choice
+    assert (kda.kda_chunk_prefill_workspace_bytes(1, 65536, 32, 128, 128, bf)
+            == kda.kda_chunk_prefill_segmented_workspace_bytes(1, 65536, 32, 128, 128, 8, bf))
+    os.environ["KDA_PREFILL_PLAN"] = "split"
+    try:
+        assert f(1, 1048576, 32, 128, 128, bf) == 1   # a forced plan runs as forced
+    finally:
+        del os.environ["KDA_PREFILL_PLAN"]

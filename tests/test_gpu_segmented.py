@@ -10,7 +10,7 @@ import linear_attention_recurrence_05_amd as kda
 from linear_attention_recurrence_05_amd.inputs import config_inputs, prefill_inputs
 import oracle
 
-from gpu_common import TOL, need_gpu, rel_err, say
+from gpu_common import TOL, need_gpu, plan, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +85,36 @@ def test_segmented_mid_workload():
     say(f"segmented mid workload n_seg=8: o {eo:.2e} S_T {es:.2e}; "
         f"vs direct o {rel_err(o, od.float().cpu().numpy()):.2e}")
     assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+@pytest.mark.parametrize("H,R", [(32, 8), (24, 8), (16, 16)])
+def test_prefill_chooses_segment_scan_for_long_sequences_of_few_heads(H, R):
+    """kda_chunk_prefill runs the segment scan by itself for T = 65,536 with
+    few heads (fused state-only passes with 128 columns per workgroup at
+    B * R * H = 256, 64 at 192): bit-identical to the explicit segmented call,
+    within tolerance of the direct plan and of the oracle."""
+    dev = need_gpu()
+    T = 65536
+    assert kda.kda_chunk_prefill_segments(1, T, H, 128, 128, torch.bfloat16) == R
+    x = prefill_inputs(1, T, H, 128, 128, torch.bfloat16, seed=77 + H, s0_std=0.1, device=dev)
+    args = (x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"])
+    o, ST = kda.chunk_prefill(*args, g_min=x["g_min"], S0=x["S0"])
+    o_s, S_s = seg(x, R)
+    assert torch.equal(o, o_s) and torch.equal(ST, S_s)
+    with plan("split"):
+        o_d, S_d = kda.chunk_prefill(*args, g_min=x["g_min"], S0=x["S0"])
+    torch.cuda.synchronize()
+    ed_o, ed_s = rel_err(o, _np(o_d)), rel_err(ST, _np(S_d))
+    # the oracle on the first 1,024 tokens (inside the first segment)
+    P = 1024
+    o_ref, _ = oracle.prefill(*(t[:, :P] for t in (x["q"], x["k"], x["v"], x["z"], x["beta"])),
+                              x["A"], x["g_min"], x["S0"], want_state=False)
+    eo = rel_err(o[:, :P], o_ref)
+    say(f"auto segments H={H} R={R}: vs direct o {ed_o:.2e} S_T {ed_s:.2e}; "
+        f"vs oracle prefix {eo:.2e}")
+    assert ed_o < TOL[torch.bfloat16] and ed_s < TOL[torch.bfloat16]
+    assert eo < TOL[torch.bfloat16]
