@@ -118,3 +118,14 @@ def test_prefill_chooses_segment_scan_for_long_sequences_of_few_heads(H, R):
         f"vs oracle prefix {eo:.2e}")
     assert ed_o < TOL[torch.bfloat16] and ed_s < TOL[torch.bfloat16]
     assert eo < TOL[torch.bfloat16]
+    if H == 32:
+        # in place (S_T aliases S0) and without S_T, through the plain entry point
+        S = x["S0"].clone()
+        o2 = torch.empty_like(o)
+        ws = torch.empty(kda.kda_chunk_prefill_workspace_bytes(1, T, H, 128, 128, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+        kda.kda_chunk_prefill(*args, x["g_min"], S, o2, S, ws)
+        o3 = torch.empty_like(o)
+        kda.kda_chunk_prefill(*args, x["g_min"], x["S0"], o3, None, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(S, ST) and torch.equal(o2, o) and torch.equal(o3, o)
