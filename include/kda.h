@@ -139,8 +139,9 @@ kda_status kda_chunk_prefill(const void *q, const void *k, const void *v,
 
 /* Bytes of device workspace kda_chunk_prefill_segmented needs (0 for
  * arguments it would reject): the inner prefill's workspace for B * n_seg
- * rows of T / n_seg tokens, a zero value tensor of the size of v, and four
- * state tensors [B * n_seg, H, d_k, d_v] fp32. */
+ * rows of T / n_seg tokens, four state tensors [B * n_seg, H, d_k, d_v] fp32,
+ * and, unless the map passes are state-only (d = 128 and B * n_seg * H >=
+ * 128), a zero value tensor of the size of v. */
 size_t kda_chunk_prefill_segmented_workspace_bytes(int B, int T, int H, int d_k,
                                                    int d_v, int n_seg,
                                                    kda_dtype dt);
