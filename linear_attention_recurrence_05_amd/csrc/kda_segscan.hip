@@ -45,10 +45,11 @@ __global__ __launch_bounds__(256) void identity_kernel(float* __restrict__ p, si
 }
 
 // Scan over the R segments of each (b, h), one workgroup per 16 value
-// columns: S <- M_r S + N_r, with M_r staged in LDS.  Writes S_in(r) of every
-// segment to Sin[(b R + r), h] and the end state to S_T[b, h] (if given).
-// Reads S0 (null: zeros) before any write, and only its own columns, so S_T
-// may alias S0.
+// columns: S <- M_r S + N_r, with M_r staged in LDS and M_{r+1} loaded into
+// registers while step r computes.  Writes S_in(r) of every segment to
+// Sin[(b R + r), h] and the end state to S_T[b, h] (if given).  Reads S0
+// (null: zeros) before any write, and only its own columns, so S_T may alias
+// S0.
 template <int D>
 __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ M,
                                                       const float* __restrict__ Nst,
@@ -56,6 +57,7 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
                                                       float* S_T, int H, int R) {
     constexpr int CB = 16;                  // value columns per workgroup
     constexpr int OPT = D * CB / 256;       // outputs per thread
+    constexpr int MPT = D * D / 256;        // elements of M per thread
     __shared__ float Ms[D][D + 1];
     __shared__ float Ss[D][CB];
     const int tid = (int)threadIdx.x;
@@ -71,6 +73,12 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
         const int c = e / CB, j = e % CB;
         Ss[c][j] = S0 ? S0[(bh * D + c) * D + col0 + j] : 0.0f;
     }
+    float mreg[MPT];
+    {
+        const float* m = state(M, b * R);
+#pragma unroll
+        for (int x = 0; x < MPT; ++x) mreg[x] = m[tid + 256 * x];
+    }
     __syncthreads();
     for (int r = 0; r < R; ++r) {
         const size_t row = b * R + r;
@@ -79,9 +87,17 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
             const int c = e / CB, j = e % CB;
             sin[(size_t)c * D + col0 + j] = Ss[c][j];
         }
-        const float* m = state(M, row);
-        for (int e = tid; e < D * D; e += 256) Ms[e / D][e % D] = m[e];
+#pragma unroll
+        for (int x = 0; x < MPT; ++x) {
+            const int e = tid + 256 * x;
+            Ms[e / D][e % D] = mreg[x];
+        }
         __syncthreads();
+        if (r + 1 < R) {   // the next map, in flight while this step computes
+            const float* m = state(M, row + 1);
+#pragma unroll
+            for (int x = 0; x < MPT; ++x) mreg[x] = m[tid + 256 * x];
+        }
         const float* nr = state(Nst, row);
         float acc[OPT];
 #pragma unroll
