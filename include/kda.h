@@ -109,6 +109,13 @@ int kda_chunk_prefill_segments(int B, int T, int H, int d_k, int d_v, kda_dtype 
 /* Chunkwise prefill over T tokens (any T >= 1; chunks of KDA_CHUNK tokens
  * start at t = 0 and the last may be short).  Computes o for every token and,
  * if S_T != NULL, the final state.
+ * Source: dev.to "Kimi K3 Architecture ...", section "The Sequence
+ * Bottleneck: Hybrid KDA and Gated MLA" -- the gated delta rule run as
+ * chunkwise parallel execution over 16-token tiles, the within-tile and
+ * state ("diagonal" and "off-diagonal") parts as dense matrix products, the
+ * tiles' cumulative log-decay inside (-80, 0) for g_min = -5; terrencekim.net
+ * "Kimi K3 - Sparsity Mechanics ...", section 2, Temporal Sequence (KDA)
+ * card -- a fixed-size state per head carried from one token to the next.
  *   S0 == NULL      : the initial state is zero.
  *   S_T may alias S0 exactly (in-place continuation); no other overlap of
  *   outputs (o, S_T, workspace) with inputs is allowed.
@@ -120,8 +127,10 @@ int kda_chunk_prefill_segments(int B, int T, int H, int d_k, int d_v, kda_dtype 
  * kda_chunk_prefill_segmented with kda_chunk_prefill_segments(...) segments)
  * is a function of the sizes; the segment scan restarts the chunk grid at
  * every segment start, so results agree with the direct plans up to
- * rounding.  For tests and tuning the environment variable KDA_PREFILL_PLAN
- * overrides it (and then no segment scan is chosen): "split" (default inter-chunk variant), "split:<n>:<b>" (n value
+ * rounding.  Test and tuning hook only (production callers leave it unset):
+ * the environment variable KDA_PREFILL_PLAN overrides the plan (and then no
+ * segment scan is chosen): "split" (default inter-chunk variant),
+ * "split:<n>:<b>" (n value
  * columns per inter-chunk workgroup, b 16-column blocks per state chain:
  * b = 1 with n in {16, 32} or, for bf16 with d = 128, 64; b = 2 for bf16
  * with d = 128, n in {32, 64}), or "fused:<n>" with n value columns per
@@ -198,8 +207,8 @@ size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
  *                     for this call only.
  * The sweep runs in fp32 whatever dt is.  dA and dbeta are summed over
  * value-column blocks and tokens in a fixed order (deterministic).
- * For tests and tuning the environment variable KDA_BACKWARD_PLAN=chain
- * selects the chunk-level plan (a chain of per-chunk state gradients, then
+ * Test and tuning hook only (production callers leave it unset): the
+ * environment variable KDA_BACKWARD_PLAN=chain selects the chunk-level plan (a chain of per-chunk state gradients, then
  * every chunk's reverse sweep at once) instead of the default sweep over the
  * whole sequence; the workspace query honours the same variable. */
 kda_status kda_chunk_backward(const void *q, const void *k, const void *v,
@@ -213,7 +222,13 @@ kda_status kda_chunk_backward(const void *q, const void *k, const void *v,
 
 /* One recurrent decode step: for every (b, h) the state S [B, H, d_k, d_v]
  * (fp32) is read once and overwritten in place with S_t; o receives
- * S_t^T q_t.  o must not overlap S or the inputs. */
+ * S_t^T q_t.  o must not overlap S or the inputs.
+ * Source: terrencekim.net "Kimi K3 - Sparsity Mechanics ...", section 2,
+ * Temporal Sequence (KDA) card -- a fixed-size associative memory in place of
+ * a growing KV cache, updated per token by a Householder-style delta rule
+ * with channel-wise forget gates; dev.to "Kimi K3 Architecture ...", section
+ * "The Sequence Bottleneck: Hybrid KDA and Gated MLA" -- the state shape and
+ * the gate equation. */
 kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const void *z, const float *beta, const float *A,
                            float g_min, float *S, void *o, int B, int H,
@@ -253,9 +268,19 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
  * may not overlap any other argument, nor o; the slot tables may coincide.
  * Returns KDA_ERR_INVALID_SHAPE for n_slots < 1. */
 
+/* Bytes of device workspace kda_chunk_prefill_paged needs for these sizes
+ * (0: none; also 0 for arguments it would reject).  It differs from
+ * kda_chunk_prefill_workspace_bytes where the dense call runs the segment
+ * scan (which the paged call never does), so query each call with its own
+ * function. */
+size_t kda_chunk_prefill_paged_workspace_bytes(int B, int T, int H, int d_k, int d_v,
+                                               kda_dtype dt);
+
 /* kda_chunk_prefill from pool row slots_in[b] (NULL: zero initial states)
- * into pool row slots_out[b] (NULL: no state written).  Workspace as for
- * kda_chunk_prefill (the same size query). */
+ * into pool row slots_out[b] (NULL: no state written), always by a direct
+ * plan (never the segment scan).
+ *   workspace : at least kda_chunk_prefill_paged_workspace_bytes(...) bytes
+ *               (may be NULL if that is 0). */
 kda_status kda_chunk_prefill_paged(const void *q, const void *k, const void *v,
                                    const void *z, const float *beta,
                                    const float *A, float g_min, float *pool,

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "kda_decode_step": ([_vp] * 6 + [ctypes.c_float, _vp, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
     "kda_decode_tokens": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6 + [_vp],
                           ctypes.c_int),
+    "kda_chunk_prefill_paged_workspace_bytes": ([_i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "kda_chunk_prefill_paged": ([_vp] * 6 + [ctypes.c_float, _vp, _i, _vp, _vp, _vp] + [_i] * 6
                                 + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "kda_decode_step_paged": ([_vp] * 6 + [ctypes.c_float, _vp, _i, _vp, _vp] + [_i] * 5 + [_vp],
@@ -110,15 +111,83 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"q/k/v/z/o must be bfloat16 or float32, got {t.dtype}")
 
 
-def _require_contiguous(**tensors):
-    for name, t in tensors.items():
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+# Device type every tensor argument must live on (HIP devices are "cuda" in
+# torch).  CPU-only tests of the checks below substitute "cpu" here to reach
+# the dtype and shape checks without a GPU; they only make calls that fail.
+_DEVICE_TYPE = "cuda"
+
+
+class _Args:
+    """Host-side checks of the tensors of one call, before any pointer crosses
+    the C ABI: every tensor on q's CUDA device, contiguous, of the dtype and
+    element count kda.h documents.  The C library sizes every range from the
+    scalar sizes it is given (taken from q), so a host tensor, a wrongly
+    typed or an undersized one must never reach it."""
+
+    def __init__(self, where, ref):
+        self.where = where
+        if not isinstance(ref, torch.Tensor):
+            raise TypeError(f"{where}: expected a torch.Tensor, got {type(ref).__name__}")
+        if ref.device.type != _DEVICE_TYPE:
+            raise ValueError(f"{where}: tensors must be on a CUDA device, got {ref.device}")
+        if ref.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"{where}: q must be bfloat16 or float32, got {ref.dtype}")
+        self.dev = ref.device
+        self.dt = ref.dtype
+
+    def __call__(self, name, t, dtype, shape, required=True):
+        if t is None:
+            if required:
+                raise ValueError(f"{self.where}: {name} is required")
+            return
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.where}: {name} must be a torch.Tensor")
+        if t.device != self.dev:
+            raise ValueError(f"{self.where}: {name} is on {t.device}, q on {self.dev}")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{self.where}: {name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.where}: {name} must be contiguous")
+        if shape is not None:
+            n = 1
+            for e in shape:
+                n *= int(e)
+            if t.numel() != n:
+                raise ValueError(f"{self.where}: {name} has shape {tuple(t.shape)}, "
+                                 f"expected {tuple(shape)}")
+
+    def workspace(self, ws):
+        """Any dtype; its byte size is passed to the library, which checks it."""
+        self("workspace", ws, None, None, required=False)
+        return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def _tokens(c, q, k, v, z, beta, A, ndim=4):
+    """Checks q, k, z [B, (T,) H, dk], v [B, (T,) H, dv] (q's dtype), beta
+    [B, (T,) H] and A [H] (fp32); returns the leading sizes and dk, dv."""
+    if q.dim() != ndim:
+        raise ValueError(f"{c.where}: q must have {ndim} dimensions, got shape {tuple(q.shape)}")
+    if not isinstance(v, torch.Tensor) or v.dim() != ndim:
+        raise ValueError(f"{c.where}: v must be a tensor with {ndim} dimensions")
+    lead = tuple(q.shape[:-1])
+    dk, dv = int(q.shape[-1]), int(v.shape[-1])
+    c("k", k, c.dt, lead + (dk,))
+    c("z", z, c.dt, lead + (dk,))
+    c("v", v, c.dt, lead + (dv,))
+    c("beta", beta, torch.float32, lead)
+    c("A", A, torch.float32, (lead[-1],))
+    return lead, dk, dv
 
 
 def kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype) -> int:
     code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
     return int(lib().kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, code))
+
+
+def kda_chunk_prefill_paged_workspace_bytes(B, T, H, d_k, d_v, dtype) -> int:
+    """C entry point kda_chunk_prefill_paged_workspace_bytes."""
+    code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+    return int(lib().kda_chunk_prefill_paged_workspace_bytes(B, T, H, d_k, d_v, code))
 
 
 def kda_chunk_prefill_segments(B, T, H, d_k, d_v, dtype) -> int:
@@ -129,10 +198,12 @@ def kda_chunk_prefill_segments(B, T, H, d_k, d_v, dtype) -> int:
 
 def kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace=None, stream=None):
     """C entry point kda_chunk_prefill on torch tensors (layouts of kda.h)."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0, o=o, S_T=S_T)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = _Args("kda_chunk_prefill", q)
+    (B, T, H), dk, dv = _tokens(c, q, k, v, z, beta, A)
+    c("S0", S0, torch.float32, (B, H, dk, dv), required=False)
+    c("o", o, c.dt, (B, T, H, dv))
+    c("S_T", S_T, torch.float32, (B, H, dk, dv), required=False)
+    ws_bytes = c.workspace(workspace)
     st = lib().kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
                                  float(g_min), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
                                  _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream))
@@ -141,9 +212,10 @@ def kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace=None, st
 
 def kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream=None):
     """C entry point kda_decode_step on torch tensors; S is updated in place."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S=S, o=o)
-    B, H, dk = q.shape
-    dv = v.shape[-1]
+    c = _Args("kda_decode_step", q)
+    (B, H), dk, dv = _tokens(c, q, k, v, z, beta, A, ndim=3)
+    c("S", S, torch.float32, (B, H, dk, dv))
+    c("o", o, c.dt, (B, H, dv))
     st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
                                float(g_min), _ptr(S), _ptr(o), B, H, dk, dv, _dtype_code(q),
                                _stream(stream))
@@ -153,20 +225,28 @@ def kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream=None):
 def kda_decode_tokens(q, k, v, z, beta, A, g_min, S, S_out, o, stream=None):
     """C entry point kda_decode_tokens on torch tensors: T = q.shape[1] steps from
     the state S; the state after them goes to S_out (which may be S)."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S=S, S_out=S_out, o=o)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    c = _Args("kda_decode_tokens", q)
+    (B, T, H), dk, dv = _tokens(c, q, k, v, z, beta, A)
+    c("S", S, torch.float32, (B, H, dk, dv))
+    c("S_out", S_out, torch.float32, (B, H, dk, dv))
+    c("o", o, c.dt, (B, T, H, dv))
     st = lib().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
                                  float(g_min), _ptr(S), _ptr(S_out), _ptr(o), B, T, H, dk, dv,
                                  _dtype_code(q), _stream(stream))
     _check(st, "kda_decode_tokens")
 
 
-def _slots(t, B):
-    if t is None:
-        return None
-    if t.dtype != torch.int32 or t.numel() != B:
-        raise ValueError("a slot table is an int32 tensor of B entries")
+def _pool(c, pool, H, dk, dv):
+    """The state pool [n_slots, H, dk, dv] fp32; returns n_slots."""
+    if not isinstance(pool, torch.Tensor) or pool.dim() != 4:
+        raise ValueError(f"{c.where}: pool must be a tensor [n_slots, H, d_k, d_v]")
+    c("pool", pool, torch.float32, (pool.shape[0], H, dk, dv))
+    return int(pool.shape[0])
+
+
+def _slots(c, name, t, B, required=False):
+    """A slot table: int32 [B] on q's device (values are checked by the kernels)."""
+    c(name, t, torch.int32, (B,), required=required)
     return t
 
 
@@ -174,14 +254,15 @@ def kda_chunk_prefill_paged(q, k, v, z, beta, A, g_min, pool, slots_in, slots_ou
                             workspace=None, stream=None):
     """C entry point kda_chunk_prefill_paged: states from pool[slots_in[b]] into
     pool[slots_out[b]] (either table may be None)."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, pool=pool, slots_in=slots_in,
-                        slots_out=slots_out, o=o)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = _Args("kda_chunk_prefill_paged", q)
+    (B, T, H), dk, dv = _tokens(c, q, k, v, z, beta, A)
+    n_slots = _pool(c, pool, H, dk, dv)
+    c("o", o, c.dt, (B, T, H, dv))
+    ws_bytes = c.workspace(workspace)
     st = lib().kda_chunk_prefill_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
-                                       float(g_min), _ptr(pool), pool.shape[0],
-                                       _ptr(_slots(slots_in, B)), _ptr(_slots(slots_out, B)),
+                                       float(g_min), _ptr(pool), n_slots,
+                                       _ptr(_slots(c, "slots_in", slots_in, B)),
+                                       _ptr(_slots(c, "slots_out", slots_out, B)),
                                        _ptr(o), B, T, H, dk, dv, _dtype_code(q), _ptr(workspace),
                                        ws_bytes, _stream(stream))
     _check(st, "kda_chunk_prefill_paged")
@@ -189,12 +270,13 @@ def kda_chunk_prefill_paged(q, k, v, z, beta, A, g_min, pool, slots_in, slots_ou
 
 def kda_decode_step_paged(q, k, v, z, beta, A, g_min, pool, slots, o, stream=None):
     """C entry point kda_decode_step_paged: pool[slots[b]] updated in place."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, pool=pool, slots=slots, o=o)
-    B, H, dk = q.shape
-    dv = v.shape[-1]
+    c = _Args("kda_decode_step_paged", q)
+    (B, H), dk, dv = _tokens(c, q, k, v, z, beta, A, ndim=3)
+    n_slots = _pool(c, pool, H, dk, dv)
+    c("o", o, c.dt, (B, H, dv))
     st = lib().kda_decode_step_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
-                                     float(g_min), _ptr(pool), pool.shape[0],
-                                     _ptr(_slots(slots, B)), _ptr(o), B, H, dk, dv,
+                                     float(g_min), _ptr(pool), n_slots,
+                                     _ptr(_slots(c, "slots", slots, B, required=True)), _ptr(o), B, H, dk, dv,
                                      _dtype_code(q), _stream(stream))
     _check(st, "kda_decode_step_paged")
 
@@ -203,28 +285,37 @@ def kda_decode_tokens_paged(q, k, v, z, beta, A, g_min, pool, slots_in, slots_ou
                             stream=None):
     """C entry point kda_decode_tokens_paged: T steps from pool[slots_in[b]] into
     pool[slots_out[b]]."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, pool=pool, slots_in=slots_in,
-                        slots_out=slots_out, o=o)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    c = _Args("kda_decode_tokens_paged", q)
+    (B, T, H), dk, dv = _tokens(c, q, k, v, z, beta, A)
+    n_slots = _pool(c, pool, H, dk, dv)
+    c("o", o, c.dt, (B, T, H, dv))
     st = lib().kda_decode_tokens_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
-                                       float(g_min), _ptr(pool), pool.shape[0],
-                                       _ptr(_slots(slots_in, B)), _ptr(_slots(slots_out, B)),
+                                       float(g_min), _ptr(pool), n_slots,
+                                       _ptr(_slots(c, "slots_in", slots_in, B, required=True)),
+                                       _ptr(_slots(c, "slots_out", slots_out, B, required=True)),
                                        _ptr(o), B, T, H, dk, dv, _dtype_code(q), _stream(stream))
     _check(st, "kda_decode_tokens_paged")
 
 
 def kda_gate_chunk_cumsum(z, A, g_min, G, stream=None):
-    _require_contiguous(z=z, A=A, G=G)
-    B, T, H, dk = z.shape
+    c = _Args("kda_gate_chunk_cumsum", z)
+    if z.dim() != 4:
+        raise ValueError(f"{c.where}: z must be [B, T, H, d_k], got shape {tuple(z.shape)}")
+    B, T, H, dk = (int(e) for e in z.shape)
+    c("A", A, torch.float32, (H,))
+    c("G", G, torch.float32, (B, T, H, dk))
     st = lib().kda_gate_chunk_cumsum(_ptr(z), _ptr(A), float(g_min), _ptr(G), B, T, H, dk,
                                      _dtype_code(z), _stream(stream))
     _check(st, "kda_gate_chunk_cumsum")
 
 
 def kda_intra_chunk(q, k, z, beta, A, g_min, Tm, Aqk, gamma, stream=None):
-    _require_contiguous(q=q, k=k, z=z, beta=beta, A=A, Tm=Tm, Aqk=Aqk, gamma=gamma)
-    B, T, H, dk = q.shape
+    c = _Args("kda_intra_chunk", q)
+    (B, T, H), dk, _ = _tokens(c, q, k, q, z, beta, A)
+    NC = (T + KDA_CHUNK - 1) // KDA_CHUNK
+    c("Tm", Tm, torch.float32, (B, H, NC, 16, 16))
+    c("Aqk", Aqk, torch.float32, (B, H, NC, 16, 16))
+    c("gamma", gamma, torch.float32, (B, H, NC, dk))
     st = lib().kda_intra_chunk(_ptr(q), _ptr(k), _ptr(z), _ptr(beta), _ptr(A), float(g_min),
                                _ptr(Tm), _ptr(Aqk), _ptr(gamma), B, T, H, dk, _dtype_code(q),
                                _stream(stream))
@@ -255,10 +346,12 @@ def kda_chunk_prefill_segmented_workspace_bytes(B, T, H, d_k, d_v, n_seg, dtype)
 def kda_chunk_prefill_segmented(q, k, v, z, beta, A, g_min, S0, o, S_T, n_seg, workspace,
                                 stream=None):
     """C entry point kda_chunk_prefill_segmented on torch tensors (layouts of kda.h)."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0, o=o, S_T=S_T)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = _Args("kda_chunk_prefill_segmented", q)
+    (B, T, H), dk, dv = _tokens(c, q, k, v, z, beta, A)
+    c("S0", S0, torch.float32, (B, H, dk, dv), required=False)
+    c("o", o, c.dt, (B, T, H, dv))
+    c("S_T", S_T, torch.float32, (B, H, dk, dv), required=False)
+    ws_bytes = c.workspace(workspace)
     st = lib().kda_chunk_prefill_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta),
                                            _ptr(A), float(g_min), _ptr(S0), _ptr(o), _ptr(S_T),
                                            B, T, H, dk, dv, int(n_seg), _dtype_code(q),
@@ -288,11 +381,19 @@ def kda_chunk_backward_workspace_bytes(B, T, H, d_k, d_v, dtype) -> int:
 def kda_chunk_backward(q, k, v, z, beta, A, g_min, S0, dO, dS_T, dq, dk, dv, dz, dbeta, dA, dS0,
                        workspace, stream=None):
     """C entry point kda_chunk_backward on torch tensors (layouts of kda.h)."""
-    _require_contiguous(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0, dO=dO, dS_T=dS_T, dq=dq,
-                        dk=dk, dv=dv, dz=dz, dbeta=dbeta, dA=dA, dS0=dS0)
-    B, T, H, dkk = q.shape
-    dvv = v.shape[-1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = _Args("kda_chunk_backward", q)
+    (B, T, H), dkk, dvv = _tokens(c, q, k, v, z, beta, A)
+    c("S0", S0, torch.float32, (B, H, dkk, dvv), required=False)
+    c("dO", dO, c.dt, (B, T, H, dvv))
+    c("dS_T", dS_T, torch.float32, (B, H, dkk, dvv), required=False)
+    c("dq", dq, c.dt, (B, T, H, dkk))
+    c("dk", dk, c.dt, (B, T, H, dkk))
+    c("dv", dv, c.dt, (B, T, H, dvv))
+    c("dz", dz, c.dt, (B, T, H, dkk))
+    c("dbeta", dbeta, torch.float32, (B, T, H))
+    c("dA", dA, torch.float32, (H,))
+    c("dS0", dS0, torch.float32, (B, H, dkk, dvv), required=False)
+    ws_bytes = c.workspace(workspace)
     st = lib().kda_chunk_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
                                   float(g_min), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dq),
                                   _ptr(dk), _ptr(dv), _ptr(dz), _ptr(dbeta), _ptr(dA), _ptr(dS0),

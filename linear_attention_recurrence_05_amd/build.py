@@ -20,31 +20,51 @@ def library_path() -> str:
     return os.path.join(PKG, "libkda.so")
 
 
-def hipcc_command(out: str) -> list[str]:
-    hipcc = os.environ.get("HIPCC", "hipcc")
-    return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def hipcc_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             # packed fp32 VALU ops are kept out of every HIP build
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # MFMA results in arch VGPRs: the state is scaled by VALU every
             # chunk, and VALU cannot read accumulation registers
             "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", os.path.join(ROOT, "include"),
-            "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+            "-I", os.path.join(ROOT, "include")]
+
+
+def hipcc_command(out: str) -> list[str]:
+    """One hipcc command building the whole library (used by tests that
+    inspect the generated code)."""
+    hipcc = os.environ.get("HIPCC", "hipcc")
+    return [hipcc] + hipcc_flags() + ["-shared", "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
 def build(verbose: bool = False) -> str:
+    """Compiles every source to an object in parallel, then links libkda.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hipcc = os.environ.get("HIPCC", "hipcc")
     out = library_path()
-    tmp = out + ".tmp"
-    cmd = hipcc_command(tmp)
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[hipcc] + hipcc_flags() + ["-c", "-o", o, os.path.join(CSRC, s)]
+            for s, o in zip(SOURCES, objs)]
+    workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(run, cmds))
+    tmp = out + ".tmp"
+    run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, out)
     return out
 

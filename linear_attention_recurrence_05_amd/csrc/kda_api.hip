@@ -259,6 +259,13 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const 
     return hip_status(kda::launch_tokens(a, (hipStream_t)stream), "kda_decode_tokens launch");
 }
 
+size_t kda_chunk_prefill_paged_workspace_bytes(int B, int T, int H, int d_k, int d_v,
+                                               kda_dtype dt) {
+    size_t a, b;
+    if (check_common(d_k, d_v, dt, -5.0f) != KDA_OK || check_shape(B, T, H, d_k, a, b) != KDA_OK) return 0;
+    return kda::choose_plan(B, T, H, d_k, dt == KDA_BF16).ws_bytes;
+}
+
 kda_status kda_chunk_prefill_paged(const void* q, const void* k, const void* v, const void* z,
                                    const float* beta, const float* A, float g_min, float* pool,
                                    int n_slots, const int* slots_in, const int* slots_out, void* o,
@@ -273,8 +280,9 @@ kda_status kda_chunk_prefill_paged(const void* q, const void* k, const void* v, 
                          T, H, d_k, dt, workspace, plan.ws_bytes)) != KDA_OK)
         return s;
     if (workspace_bytes < plan.ws_bytes)
-        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes,
-                    plan.ws_bytes);
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace of %zu bytes, %zu needed (kda_chunk_prefill_paged_workspace_bytes)",
+                    workspace_bytes, plan.ws_bytes);
     kda::PrefillArgs a{q, k, v, z, beta, A, g_min, paged_state(pool, n_slots, slots_in, slots_out), o,
                        B, T, H, d_k, dt == KDA_BF16};
     return hip_status(kda::launch_prefill(a, plan, workspace, (hipStream_t)stream),

@@ -556,17 +556,38 @@ __device__ __forceinline__ void wg_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Bounded poll of an LDS flag: returns once *flag >= target or after
-// kSpinLimit polls (a protocol error then corrupts results but never hangs).
+// Bounded poll of an LDS flag: true once *flag >= target, false after
+// kSpinLimit polls.  The flag protocols of the split plan never need the
+// bound (every wait is released by a wave that does not wait on the waiter;
+// tests/test_flag_protocol.py checks this on a model of the protocol); it only
+// turns a protocol error into a visible one instead of a hang: a wave that
+// gives up poisons what it produces with NaN (poison_state, kNaNWord), so the
+// outputs and the final state of its columns come out NaN.
 constexpr int kSpinLimit = 1 << 22;
 
-__device__ __forceinline__ void spin_until_ge(const int* flag, int target) {
+__device__ __forceinline__ bool spin_until_ge(const int* flag, int target) {
+    bool ok = false;
     for (int it = 0; it < kSpinLimit; ++it) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+            ok = true;
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
     // later LDS reads stay after the poll that released them
     asm volatile("" ::: "memory");
+    return ok;
+}
+
+// A 32-bit word that is NaN read as one fp32 value or as two bf16 values.
+constexpr uint32_t kNaNWord = 0x7FC07FC0u;
+
+// Sets a state tile held in registers to NaN (a wave that gave up a wait).
+template <int N>
+__device__ __forceinline__ void poison_state(f32x4 (&S)[N]) {
+    const float nan = __builtin_bit_cast(float, kNaNWord);
+#pragma unroll
+    for (int m = 0; m < N; ++m) S[m] = f32x4{nan, nan, nan, nan};
 }
 
 }  // namespace kda

@@ -801,7 +801,7 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
         // outputs of pair q, left by the chains in its entry's V area (same
         // word-major layout), to o: 16 bytes per lane-piece; rows past T are
         // outside the buffer and dropped
-        auto flush = [&](int q) {
+        auto flush = [&](int q, bool ok) {
             const uint32_t* vd = reinterpret_cast<const uint32_t*>(ring + (q % NPAIR) * ENT + P::BYTES);
             const int t0 = (n_first + 2 * q) * kChunk;
             const int Lr = min(2 * kChunk, T - t0);
@@ -814,20 +814,26 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
                 const int q2 = i * kWave + lane, r = q2 / RP, c = q2 % RP;
                 u32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = vd[(4 * c + e) * Cfg::VSTR + r];
+                for (int e = 0; e < 4; ++e) x[e] = ok ? vd[(4 * c + e) * Cfg::VSTR + r] : kNaNWord;
                 buf_store_u32x4(ro, (int)((r * rs + c * EPP) * ES), x);
             }
         };
         auto wait_released = [&](int q) {   // every chain has released pair q
+            bool ok = true;
 #pragma unroll
-            for (int c = 0; c < NCW; ++c) spin_until_ge(&done[q % NPAIR][c], q);
+            for (int c = 0; c < NCW; ++c) ok = spin_until_ge(&done[q % NPAIR][c], q) && ok;
+            return ok;
         };
         if (L < NP) issue(L);
         for (int p = L; p < NP; p += NL) {
             const int e = p % NPAIR;
             if (p >= NPAIR) {   // the entry's previous pair: released, outputs out
-                wait_released(p - NPAIR);
-                flush(p - NPAIR);
+                const bool ok = wait_released(p - NPAIR);
+                flush(p - NPAIR, ok);
+                if (!ok) {   // a chain may still read the entry: poison the V it gets
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) vbuf[i] = u32x4{kNaNWord, kNaNWord, kNaNWord, kNaNWord};
+                }
             }
             write(p);
             // publish: the data stores complete before the flag store
@@ -839,8 +845,7 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
         // have written pair q + NPAIR writes pair q's outputs out
         for (int q = NP - NPAIR > 0 ? NP - NPAIR : 0; q < NP; ++q) {
             if ((q + NPAIR) % NL != L) continue;
-            wait_released(q);
-            flush(q);
+            flush(q, wait_released(q));
         }
         return;
     }
@@ -904,13 +909,17 @@ __global__ __launch_bounds__((PairCfg<E, D, NCW, NB>::THREADS)) void pair_inter_
     // after its ready flag (LDS executes a wave's operations in order, so the
     // data read after a flag that shows the pair published is that pair's);
     // the rare re-read happens at the top of the next step.
-    spin_until_ge(&ready[0], 0);
+    if (!spin_until_ge(&ready[0], 0))
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) poison_state(S[nb]);
     pops_load_k<E, D>(c, entry(0));
     int fl = 0;
     for (int s = 0; s < NP; ++s) {
         const char* ent = entry(s);
         if (fl < s) {
-            spin_until_ge(&ready[s % NPAIR], s);
+            if (!spin_until_ge(&ready[s % NPAIR], s))
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) poison_state(S[nb]);
             pops_load_k<E, D>(c, ent);
         }
         f32x4 Va[NB], Vb[NB], Oa[NB], Ob[NB];
@@ -1024,6 +1033,12 @@ __global__ __launch_bounds__((RoleCfg<E, D, NCW>::THREADS)) void pair_roles_kern
         }
         if (lane < NCW) uready[lane] = -1;
     }
+    // chain wave c and output wave NCW + c start from the initial state of
+    // the same 16 columns; both read it before the barrier, so the chain
+    // wave's final store (S_T may alias S0) cannot overtake the output wave's
+    // read
+    f32x4 S[1][D / 16];
+    if (w < NREAD) state_load<D, 1>(S, io.in_at(b, h, H, D), tile0 + 16 * (w % NCW));
     wg_barrier();   // the only barrier: flags initialised
     auto entry = [&](int p) { return ring + (p % NPAIR) * ENT; };
 
@@ -1031,9 +1046,11 @@ __global__ __launch_bounds__((RoleCfg<E, D, NCW>::THREADS)) void pair_roles_kern
         // ------------------------------------------------ loader waves
         const int L = w - NREAD;
         for (int p = L; p < NP; p += NL) {
+            bool ok = true;
             if (p >= NPAIR) {   // every reader has released the entry's previous pair
 #pragma unroll
-                for (int c = 0; c < NREAD; ++c) spin_until_ge(&done[p % NPAIR][c], p - NPAIR);
+                for (int c = 0; c < NREAD; ++c)
+                    ok = spin_until_ge(&done[p % NPAIR][c], p - NPAIR) && ok;
             }
             char* dst = entry(p);
             // V (rows t0 .. t0+31 of the tile's columns; rows past T read 0)
@@ -1059,13 +1076,15 @@ __global__ __launch_bounds__((RoleCfg<E, D, NCW>::THREADS)) void pair_roles_kern
                     buf_load_lds16(rws, (p * BLK16 + piece) * 16, dst + i * kWave * 16);
             }
             vm_wait_all();   // V and every piece of the block have landed
-            // V area: word-major (word w of row r at w * VSTR + r)
+            // V area: word-major (word w of row r at w * VSTR + r); after a
+            // wait that gave up, NaN, so the readers still on the entry's
+            // previous pair, and this pair's readers, produce NaN
             uint32_t* vd = reinterpret_cast<uint32_t*>(dst + P::BYTES);
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int q = i * kWave + lane, r = q / RP, c = q % RP;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vd[(4 * c + e) * Cfg::VSTR + r] = vbuf[i][e];
+                for (int e = 0; e < 4; ++e) vd[(4 * c + e) * Cfg::VSTR + r] = ok ? vbuf[i][e] : kNaNWord;
             }
             // publish: the V stores complete before the flag store
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -1092,18 +1111,16 @@ __global__ __launch_bounds__((RoleCfg<E, D, NCW>::THREADS)) void pair_roles_kern
             x &= 0xFFFF0000u;
             return __builtin_bit_cast(f32x4, x);
         };
-        f32x4 S[1][D / 16];
-        state_load<D, 1>(S, io.in_at(b, h, H, D), col0);
         POps<E, D> c;
         // one basic block per step but for the rare re-read of a pair whose
         // first operands were read ahead of its publication
-        spin_until_ge(&ready[0], 0);
+        if (!spin_until_ge(&ready[0], 0)) poison_state(S[0]);
         pops_load_k<E, D>(c, entry(0));
         int fl = 0;
         for (int s = 0; s < NP; ++s) {
             char* ent = entry(s);
             if (fl < s) {
-                spin_until_ge(&ready[s % NPAIR], s);
+                if (!spin_until_ge(&ready[s % NPAIR], s)) poison_state(S[0]);
                 pops_load_k<E, D>(c, ent);
             }
             const u32x4 ra = v_read(ent, 0), rb = v_read(ent, 1);
@@ -1131,27 +1148,21 @@ __global__ __launch_bounds__((RoleCfg<E, D, NCW>::THREADS)) void pair_roles_kern
     // ---------------------------------------------------- output waves
     const int wc = w - NCW;                 // the chain this wave follows
     const int col0 = tile0 + 16 * wc;
-    f32x4 S[D / 16];
-    {
-        f32x4 S1[1][D / 16];
-        state_load<D, 1>(S1, io.in_at(b, h, H, D), col0);
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) S[m] = S1[0][m];
-    }
+    f32x4 (&Sr)[D / 16] = S[0];             // the replica of chain wc's state
     POps<E, D> c;
     for (int s = 0; s < NP; ++s) {
         char* ent = entry(s);
-        spin_until_ge(&uready[wc], s);
+        if (!spin_until_ge(&uready[wc], s)) poison_state(Sr);
         const bf16x8 u2 = *reinterpret_cast<const bf16x8*>(ent + UOFF + (wc * kWave + lane) * 16);
         pops_load_out<E, D>(c, ent);
         pops_load_supd<E, D>(c, ent);
         pin_issued();
         bf16x8 sb[P::NSLOT];
 #pragma unroll
-        for (int k = 0; k < P::NSLOT; ++k) sb[k] = pack8(S[2 * k], S[2 * k + 1]);
+        for (int k = 0; k < P::NSLOT; ++k) sb[k] = pack8(Sr[2 * k], Sr[2 * k + 1]);
         f32x4 Oa, Ob;
         pair_out<E, D>(c, sb, u2, Oa, Ob);
-        pair_supdate<E, D>(c, S, u2);
+        pair_supdate<E, D>(c, Sr, u2);
         // outputs: rows 4g + (j & 3) of each chunk, columns 4 (j >> 2) .. +3
         // of this block, 8 bytes per lane and chunk; rows past T are dropped
         {

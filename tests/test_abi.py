@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
               "kda_decode_tokens", "kda_chunk_prefill_paged", "kda_decode_step_paged",
               "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk",
               "kda_chunk_backward_workspace_bytes", "kda_chunk_backward",
-              "kda_chunk_prefill_segmented_workspace_bytes", "kda_chunk_prefill_segmented"]:
+              "kda_chunk_prefill_segmented_workspace_bytes", "kda_chunk_prefill_segmented",
+              "kda_chunk_prefill_paged_workspace_bytes"]:
         assert n in names
 
 
@@ -217,7 +218,7 @@ def test_paged_prefill_and_tokens_reject():
                                        fake(6), 4, fake(7), fake(7), fake(8), 1, 64, 2, 32, 32,
                                        kda.KDA_F32, None, 0, None)
         assert st == E["KDA_ERR_NULL_POINTER"]
-        need = kda.kda_chunk_prefill_workspace_bytes(1, 64, 2, 32, 32, kda.KDA_F32)
+        need = kda.kda_chunk_prefill_paged_workspace_bytes(1, 64, 2, 32, 32, kda.KDA_F32)
         st = L.kda_chunk_prefill_paged(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), -5.0,
                                        fake(6), 4, None, None, fake(8), 1, 64, 2, 32, 32,
                                        kda.KDA_F32, fake(9), need - 1, None)
@@ -235,6 +236,24 @@ def test_paged_prefill_and_tokens_reject():
     assert st == E["KDA_ERR_INVALID_SHAPE"]
 
 
+def test_paged_prefill_workspace_query_is_its_own():
+    """At sizes where the dense prefill runs the segment scan (a smaller
+    workspace), the paged prefill asks for exactly its own query's size."""
+    L = kda.lib()
+    B, T, H, d = 1, 65536, 32, 128
+    assert kda.kda_chunk_prefill_segments(B, T, H, d, d, kda.KDA_BF16) > 1
+    dense = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, kda.KDA_BF16)
+    need = kda.kda_chunk_prefill_paged_workspace_bytes(B, T, H, d, d, kda.KDA_BF16)
+    assert need > dense > 0
+    st = L.kda_chunk_prefill_paged(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), -5.0,
+                                   fake(6), 4, fake(7), fake(7), fake(8), B, T, H, d, d,
+                                   kda.KDA_BF16, fake(9), need - 1, None)
+    detail = L.kda_last_error().decode()
+    assert st == E["KDA_ERR_WORKSPACE_TOO_SMALL"]
+    assert f"{need} needed" in detail, detail
+    assert kda.kda_chunk_prefill_paged_workspace_bytes(B, T, H, 64, 64, kda.KDA_BF16) == 0
+
+
 def test_gate_and_intra_reject():
     L = kda.lib()
     st = L.kda_gate_chunk_cumsum(fake(0), fake(1), -5.0, None, 1, 16, 1, 32, kda.KDA_F32, None)
@@ -247,10 +266,106 @@ def test_gate_and_intra_reject():
 
 
 def test_binding_raises_named_errors():
-    import torch
-    x = torch.zeros(1, 16, 1, 48)   # d = 48 unsupported, caught on the host
+    # a status code from the library becomes a KdaError naming it, with the
+    # thread's detail string
+    L = kda.lib()
+    st = L.kda_gate_chunk_cumsum(fake(0), fake(1), -5.0, fake(2), 1, 16, 1, 48, kda.KDA_F32, None)
     with pytest.raises(kda.KdaError, match="KDA_ERR_UNSUPPORTED"):
-        kda.kda_gate_chunk_cumsum(x, torch.zeros(1), -5.0, torch.zeros_like(x), stream=0)
+        _lib._check(st, "kda_gate_chunk_cumsum")
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 16, 2, 32)
+    with pytest.raises(ValueError, match="CUDA device"):
+        kda.kda_gate_chunk_cumsum(x, torch.zeros(2), -5.0, torch.zeros_like(x), stream=0)
+    with pytest.raises(ValueError, match="CUDA device"):
+        kda.kda_chunk_prefill(x, x, x, x, torch.zeros(1, 16, 2), torch.zeros(2), -5.0, None,
+                              torch.zeros_like(x), None, None, stream=0)
+
+
+def _prefill_args(B=1, T=16, H=2, d=32, dt=None):
+    import torch
+    dt = dt or torch.float32
+    t = lambda *s, dtype=dt: torch.zeros(*s, dtype=dtype)
+    return dict(q=t(B, T, H, d), k=t(B, T, H, d), v=t(B, T, H, d), z=t(B, T, H, d),
+                beta=t(B, T, H, dtype=torch.float32), A=t(H, dtype=torch.float32), g_min=-5.0,
+                S0=t(B, H, d, d, dtype=torch.float32), o=t(B, T, H, d),
+                S_T=t(B, H, d, d, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("name,bad,match", [
+    ("beta", lambda a: a["beta"].to(__import__("torch").bfloat16), "beta must be"),
+    ("A", lambda a: a["A"].double(), "A must be"),
+    ("k", lambda a: a["k"].to(__import__("torch").bfloat16), "k must be"),
+    ("o", lambda a: a["o"].to(__import__("torch").bfloat16), "o must be"),
+    ("S0", lambda a: a["S0"][:, :1].contiguous(), "S0 has shape"),       # undersized state
+    ("S_T", lambda a: a["S_T"].reshape(-1)[:100], "S_T has shape"),
+    ("v", lambda a: a["v"][:, :8].contiguous(), "v has shape"),
+    ("z", lambda a: a["z"].transpose(1, 2), "z must be contiguous"),
+    ("beta", lambda a: None, "beta is required"),
+])
+def test_binding_rejects_mistyped_and_undersized(monkeypatch, name, bad, match):
+    monkeypatch.setattr(_lib, "_DEVICE_TYPE", "cpu")
+    a = _prefill_args()
+    a[name] = bad(a)
+    with pytest.raises(ValueError, match=match):
+        kda.kda_chunk_prefill(a["q"], a["k"], a["v"], a["z"], a["beta"], a["A"], a["g_min"],
+                              a["S0"], a["o"], a["S_T"], None, stream=0)
+
+
+def test_binding_rejects_mixed_devices(monkeypatch):
+    import torch
+    monkeypatch.setattr(_lib, "_DEVICE_TYPE", "cpu")
+    a = _prefill_args()
+    k = torch.zeros(1, 16, 2, 32, device="meta")
+    with pytest.raises(ValueError, match="k is on meta"):
+        kda.kda_chunk_prefill(a["q"], k, a["v"], a["z"], a["beta"], a["A"], -5.0, None,
+                              a["o"], None, None, stream=0)
+
+
+def test_binding_checks_decode_and_paged(monkeypatch):
+    import torch
+    monkeypatch.setattr(_lib, "_DEVICE_TYPE", "cpu")
+    B, H, d = 3, 2, 32
+    q = torch.zeros(B, H, d)
+    beta, A = torch.zeros(B, H), torch.zeros(H)
+    with pytest.raises(ValueError, match="S has shape"):   # a state too small for B
+        kda.kda_decode_step(q, q, q, q, beta, A, -5.0, torch.zeros(B - 1, H, d, d),
+                            torch.zeros(B, H, d), stream=0)
+    with pytest.raises(ValueError, match="pool must be"):
+        kda.kda_decode_step_paged(q, q, q, q, beta, A, -5.0, torch.zeros(4, H, d, d).double(),
+                                  torch.zeros(B, dtype=torch.int32), torch.zeros(B, H, d),
+                                  stream=0)
+    with pytest.raises(ValueError, match="slots must be"):
+        kda.kda_decode_step_paged(q, q, q, q, beta, A, -5.0, torch.zeros(4, H, d, d),
+                                  torch.zeros(B, dtype=torch.int64), torch.zeros(B, H, d),
+                                  stream=0)
+    with pytest.raises(ValueError, match="slots has shape"):
+        kda.kda_decode_step_paged(q, q, q, q, beta, A, -5.0, torch.zeros(4, H, d, d),
+                                  torch.zeros(B + 1, dtype=torch.int32), torch.zeros(B, H, d),
+                                  stream=0)
+    x = torch.zeros(B, 4, H, d)
+    with pytest.raises(ValueError, match="S_out has shape"):
+        kda.kda_decode_tokens(x, x, x, x, torch.zeros(B, 4, H), A, -5.0,
+                              torch.zeros(B, H, d, d), torch.zeros(B, H, d, d - 1), x.clone(),
+                              stream=0)
+
+
+def test_binding_checks_backward(monkeypatch):
+    import torch
+    monkeypatch.setattr(_lib, "_DEVICE_TYPE", "cpu")
+    a = _prefill_args()
+    g = {n: torch.zeros_like(a[n]) for n in ("q", "k", "v", "z")}
+    with pytest.raises(ValueError, match="dbeta must be"):
+        kda.kda_chunk_backward(a["q"], a["k"], a["v"], a["z"], a["beta"], a["A"], -5.0, None,
+                               a["o"], None, g["q"], g["k"], g["v"], g["z"],
+                               torch.zeros(1, 16, 2, dtype=torch.bfloat16), torch.zeros(2),
+                               None, None, stream=0)
+    with pytest.raises(ValueError, match="dA has shape"):
+        kda.kda_chunk_backward(a["q"], a["k"], a["v"], a["z"], a["beta"], a["A"], -5.0, None,
+                               a["o"], None, g["q"], g["k"], g["v"], g["z"],
+                               torch.zeros(1, 16, 2), torch.zeros(3), None, None, stream=0)
 
 
 def backward(**over):

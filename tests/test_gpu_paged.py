@@ -88,7 +88,7 @@ def test_prefill_paged_equals_dense(p, tables):
         o_dense, S_dense = kda.chunk_prefill(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"],
                                              x["g_min"], S0)
         o = torch.empty_like(o_dense)
-        nbytes = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, torch.float32)
+        nbytes = kda.kda_chunk_prefill_paged_workspace_bytes(B, T, H, d, d, torch.float32)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
         kda.kda_chunk_prefill_paged(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
                                     pool, t_in, t_out, o, ws)
@@ -112,7 +112,7 @@ def test_prefill_paged_segments_against_oracle():
     S0 = pool[s_in.long()].clone()
     o = torch.empty_like(x["v"])
     with plan("split"):
-        nbytes = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, torch.float32)
+        nbytes = kda.kda_chunk_prefill_paged_workspace_bytes(B, T, H, d, d, torch.float32)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         kda.kda_chunk_prefill_paged(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
                                     pool, s_in, s_out, o, ws)
@@ -135,7 +135,7 @@ def test_out_of_range_slot_is_skipped(p):
     x = prefill_inputs(B, T, H, d, d, torch.float32, seed=16, device=dev)
     o = torch.full_like(x["v"], 7.0)
     with plan(p):
-        nbytes = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, torch.float32)
+        nbytes = kda.kda_chunk_prefill_paged_workspace_bytes(B, T, H, d, d, torch.float32)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
         kda.kda_chunk_prefill_paged(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
                                     pool, s_bad, s_bad, o, ws)
@@ -154,3 +154,58 @@ def test_out_of_range_slot_is_skipped(p):
     torch.cuda.synchronize()
     assert torch.all(od[0] == 7.0) and not torch.all(od[1] == 7.0)
     assert torch.equal(pool[int(s_in[0])], pool1[int(s_in[0])])
+
+
+def test_decode_and_verify_paged_against_oracle():
+    """Paged decode (two steps in place) and the paged 5-token verify step
+    (snapshot kept) against the fp64 oracle directly, bf16 at d = 128."""
+    dev = need_gpu()
+    B, H, d, n_slots, T = 6, 4, 128, 13, 5
+    pool, slots, s_out = pool_and_slots(B, H, d, n_slots, dev, seed=21)
+    gen, A, _ = decode_state(B, H, d, d, seed=22, device=dev)
+    S_ref = pool[slots.long()].double().cpu().numpy().copy()
+    for step in range(2):
+        x = decode_step_inputs(gen, B, H, d, d, torch.bfloat16, dev)
+        o = torch.empty(B, H, d, dtype=torch.bfloat16, device=dev)
+        kda.kda_decode_step_paged(x["q"], x["k"], x["v"], x["z"], x["beta"], A, -5.0, pool, slots, o)
+        torch.cuda.synchronize()
+        o_ref = oracle.decode(x["q"], x["k"], x["v"], x["z"], x["beta"], A, -5.0, S_ref)
+        eo, es = rel_err(o, o_ref), rel_err(pool[slots.long()], S_ref)
+        say(f"paged decode step {step + 1}: o {eo:.2e} S {es:.2e}")
+        assert eo < TOL[torch.bfloat16] and es < 1e-4
+    xv = prefill_inputs(B, T, H, d, d, torch.bfloat16, seed=23, device=dev)
+    S_in = pool[slots.long()].clone()
+    ov = torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev)
+    kda.kda_decode_tokens_paged(xv["q"], xv["k"], xv["v"], xv["z"], xv["beta"], A, -5.0, pool,
+                                slots, s_out, ov)
+    torch.cuda.synchronize()
+    o_ref, S_T_ref = oracle.prefill(xv["q"], xv["k"], xv["v"], xv["z"], xv["beta"], A, -5.0, S_in)
+    eo, es = rel_err(ov, o_ref), rel_err(pool[s_out.long()], S_T_ref)
+    say(f"paged verify T={T}: o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[torch.bfloat16] and es < 1e-4
+    assert torch.equal(pool[slots.long()], S_in)   # the snapshot rows stay
+
+
+@pytest.mark.parametrize("p", ["auto", "fused:128", "fused:64"])
+def test_prefill_paged_bf16_d128_against_oracle(p):
+    """Paged prefill, bf16 at d = 128, from pool rows into other pool rows,
+    against the oracle; 'auto' picks the fused plan at B * H = 128."""
+    dev = need_gpu()
+    B, T, H, d, n_slots = 32, 77, 4, 128, 70
+    pool, s_in, s_out = pool_and_slots(B, H, d, n_slots, dev, seed=24)
+    x = prefill_inputs(B, T, H, d, d, torch.bfloat16, seed=25, device=dev)
+    S0 = pool[s_in.long()].clone()
+    o = torch.empty_like(x["v"])
+    with plan(p):
+        nbytes = kda.kda_chunk_prefill_paged_workspace_bytes(B, T, H, d, d, torch.bfloat16)
+        assert p != "auto" or nbytes == 0   # the fused plan needs no workspace
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+        kda.kda_chunk_prefill_paged(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
+                                    pool, s_in, s_out, o, ws)
+        torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
+                                  S0, nthreads=16)
+    eo, es = rel_err(o, o_ref), rel_err(pool[s_out.long()], S_ref)
+    say(f"paged prefill bf16 d128 plan {p}: o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[torch.bfloat16] and es < TOL[torch.bfloat16]
+    assert torch.equal(pool[s_in.long()], S0)

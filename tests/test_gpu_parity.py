@@ -246,6 +246,34 @@ def test_prefill_config3_prefix(config3):
     assert eo < 2e-2 and es < 2e-2
 
 
+def test_prefill_config3_across_segment_boundaries(config3):
+    """The plain 1,048,576-token call runs as a scan over 8 segments of 131,072
+    tokens.  For 4 sampled heads the oracle runs from token 0 over the first
+    two segments and 2,048 tokens of the third; the outputs just after the
+    first and the second segment boundary -- which depend on the scanned start
+    states of segments 1 and 2 -- are compared with the plain call's."""
+    x = config3
+    Tseg, W, heads = 131072, 2048, [0, 9, 22, 31]
+    assert kda.kda_chunk_prefill_segments(1, 1048576, 32, 128, 128, torch.bfloat16) == 8
+    o, _ = run_prefill(x, want_state=False)
+    P = 2 * Tseg + W
+    hs = torch.as_tensor(heads, device=x["q"].device)
+    g = {kk: x[kk][:, :P][:, :, hs].contiguous() for kk in ("q", "k", "v", "z", "beta")}
+    o_ref, _ = oracle.prefill(g["q"], g["k"], g["v"], g["z"], g["beta"], x["A"][hs], x["g_min"],
+                              None, want_state=False)
+    for r in (1, 2):
+        t0 = r * Tseg
+        for i, h in enumerate(heads):
+            e = rel_err(o[:, t0:t0 + W, h], o_ref[:, t0:t0 + W, i])
+            say(f"config 3 after segment boundary {r} (tokens {t0}..{t0 + W - 1}), head {h}: "
+                f"o {e:.2e}")
+            assert e < TOL[torch.bfloat16]
+    # and the last tokens before the first boundary, inside segment 0
+    e0 = rel_err(o[:, Tseg - W:Tseg][:, :, hs], o_ref[:, Tseg - W:Tseg])
+    say(f"config 3 before boundary 1: o {e0:.2e}")
+    assert e0 < TOL[torch.bfloat16]
+
+
 def test_prefill_config3_decay_bound(config3):
     """Every one of the 65,536 x 32 x 128 chunk-channels keeps its cumulative
     log-decay inside [-80, 0) (the pages' (-80, 0); g = g_min is reachable in fp32)."""
