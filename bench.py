@@ -2,23 +2,23 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-One step = one chunkwise prefill pass (gate + intra-chunk + inter-chunk, all
-in libkda's HIP kernels: for this workload a pair-producer launch and a
-state-chain launch, pair_roles_kernel) over the mid-size synthetic workload: B=1, H=32,
-T=4096, d_k=d_v=128, bf16 q/k/v/z, fp32 beta/A/state, g_min=-5.  Inputs are
-resident in HBM before timing, and cold: the steps cycle through copies of
-the inputs, so a step's inputs were last touched more than 1 GiB of traffic
-ago and each step reads them from HBM (the 256 MB Infinity Cache cannot
-hold them).  The same steps after a 1 GiB write flush, whose dirty lines are
-written back during the step, are reported beside.  Prints ONE JSON line with the prefill tokens/s as
-``value``, a ``roofline`` object for the prefill pass, the fp64 CPU oracle
-timed on the host (``cpu_baseline``), a ``decode`` object with the decode
-steps/s of the B=256 workload (1,000 back-to-back in-place steps), and a
-``verify`` object with the multi-token step (T drafted tokens per sequence
-from the B=256 live state into a separate state buffer) per second, and a
-``decode_paged`` object with the decode step on states addressed through a
-slot table into a pool, and a ``backward`` object with the gradients of the
-same prefill (kda_chunk_backward) per second.
+One step = one chunkwise prefill pass -- gate, intra-chunk and inter-chunk
+stages, all in libkda's HIP kernels -- over the million-token synthetic
+workload: B=1, H=32, T=1,048,576, d_k=d_v=128, bf16 q/k/v/z, fp32
+beta/A/state, g_min=-5.  kda_chunk_prefill runs it as a scan over 8 segments
+(two state-only map passes, the scan, a full pass).  Inputs (34 GiB) are
+resident in HBM before timing and far larger than the last-level cache, so
+every step streams them from HBM.
+
+Prints ONE JSON line: the prefill tokens/s as ``value`` with a ``roofline``
+object for the pass; ``mid`` (B1 H32 T4096) and ``batched`` (B8 H32 T32768,
+carried state) prefill objects with their own rooflines (cold inputs:
+the steps cycle through copies); ``decode`` (B=256, 1,000 back-to-back
+in-place steps), ``decode_paged`` (states in a slot-addressed pool),
+``verify`` (T drafted tokens per sequence from a live state) and
+``backward`` (gradients of the mid prefill) objects; and the fp64 CPU oracle
+timed on the host's cores on the first 16,384 tokens of the million-token
+sequence (``cpu_baseline``).
 """
 from __future__ import annotations
 
@@ -85,6 +85,146 @@ def measured_traffic(key):
         return None
 
 
+def measured_record(key):
+    """A figure recorded under profiles/traffic.json (e.g. an MFMA-busy
+    fraction from counters), or None if it is missing or the kernel sources
+    it was taken on have changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["records"][key]
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read()
+                                    for s in rec["sources"])).hexdigest()[:16]
+        return rec["value"] if h == rec["sha256_16"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_prefill(kda, torch, workload, stream, dev, steps, warmup, segments=1, rotate=False,
+                 flush=False):
+    """Times `steps` prefill passes of one workload (after `warmup` untimed
+    ones) with HIP events on `stream`.  Returns (result dict, inputs)."""
+    from linear_attention_recurrence_05_amd.inputs import PREFILL_CONFIGS, config_inputs
+    cfg_index = WORKLOADS[workload]
+    cfg = PREFILL_CONFIGS[cfg_index]
+    B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.dk
+    x = config_inputs(cfg_index, dev)
+    o = torch.empty(B, T, H, d, dtype=cfg.dtype, device=dev)
+    ST = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    if segments > 1:
+        nb = kda.kda_chunk_prefill_segmented_workspace_bytes(B, T, H, d, d, segments, cfg.dtype)
+    else:
+        nb = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, cfg.dtype)
+    # segments the plain prefill entry point chooses by itself (1: direct plan)
+    auto_seg = 1 if segments > 1 else kda.kda_chunk_prefill_segments(B, T, H, d, d, cfg.dtype)
+    n_seg = segments if segments > 1 else auto_seg
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    # Cold inputs.  A workload much larger than the 256 MB last-level cache
+    # streams from HBM by itself; a small one cycles through copies of its
+    # inputs so that a step's inputs were last touched more than 1 GiB of
+    # other traffic ago.
+    in_bytes = sum(t.numel() * t.element_size() for t in x.values() if torch.is_tensor(t))
+    n_rot = min(8, 1 + -(-(1 << 30) // in_bytes)) if rotate else 1
+    xs = [x] + [{kk: (vv.clone() if torch.is_tensor(vv) else vv) for kk, vv in x.items()}
+                for _ in range(n_rot - 1)]
+
+    def step(i):
+        xi = xs[i % n_rot]
+        if segments > 1:
+            kda.kda_chunk_prefill_segmented(xi["q"], xi["k"], xi["v"], xi["z"], xi["beta"],
+                                            xi["A"], xi["g_min"], xi["S0"], o, ST, segments,
+                                            ws, stream)
+        else:
+            kda.kda_chunk_prefill(xi["q"], xi["k"], xi["v"], xi["z"], xi["beta"], xi["A"],
+                                  xi["g_min"], xi["S0"], o, ST, ws, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        step(warmup + i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    ms = sum(times_ms) / len(times_ms)
+    res = {"ms_per_step": ms, "ms_per_step_median": times_ms[len(times_ms) // 2],
+           "wall_s_timed_region": wall}
+    if rotate:
+        res["cold_inputs"] = (f"steps cycle through {n_rot} copies of the inputs "
+                              f"({in_bytes / 2**20:.0f} MiB each)")
+    else:
+        res["cold_inputs"] = (f"inputs of {in_bytes / 2**30:.1f} GiB, far beyond the 256 MB "
+                              "last-level cache: every step streams them from HBM")
+    if flush:
+        # the same steps, each after a 1 GiB write flush, and back to back
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        fl_ms = []
+        for i in range(steps):
+            buf.zero_()
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record(stream)
+            step(0)
+            f1.record(stream)
+            torch.cuda.synchronize()
+            fl_ms.append(f0.elapsed_time(f1))
+        del buf
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for _ in range(steps):
+            step(0)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        res["ms_per_step_after_write_flush"] = sum(fl_ms) / len(fl_ms)
+        res["ms_per_step_warm"] = w0.elapsed_time(w1) / steps
+
+    plan = (f"segment scan over {segments} segments" if segments > 1
+            else f"segment scan over {auto_seg} segments (chosen by kda_chunk_prefill)"
+            if auto_seg > 1 else ("split" if nb else "fused"))
+    alg_b = prefill_alg_bytes(B, T, H, d, with_s0=x["S0"] is not None)
+    alg_f = prefill_alg_flops(B, T, H, d)
+    gbs = alg_b / (ms * 1e-3) / 1e9
+    tflops = alg_f / (ms * 1e-3) / 1e12
+    key = f"prefill_{workload}_pass"
+    kernel = ("segment-scan prefill pass (identity_kernel, two state-only fused_kernel map "
+              "passes, segscan_kernel, one full fused_kernel pass)" if n_seg > 1
+              else "prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
+              else "prefill pass (fused_kernel)")
+    tkey = f"{key}_bytes_{'segscan' if n_seg > 1 else 'split' if nb else 'fused'}"
+    res.update({
+        "value": B * T / (ms * 1e-3), "unit": "tokens/s",
+        "config": {"workload": f"{cfg.name}_prefill_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T,
+                   "H": H, "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": -5.0,
+                   "S0": "zeros" if x["S0"] is None else "N(0, 0.01)",
+                   "parallelism": "single GPU", "plan": plan, "workspace_bytes": nb},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(tkey),
+                     "traffic_unit": "bytes per pass", "kernel": kernel,
+                     "alg_bytes_per_step": alg_b,
+                     "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+                     "alg_flops_per_step": alg_f,
+                     "mfma_busy": measured_record(f"{key}_mfma_busy")},
+    })
+    del o, ST, ws, xs
+    return res, x
+
+
+WORKLOADS = {"mid": 1, "batched": 2, "long": 3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,19 +233,24 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="time only the headline workload (no mid/batched sub-objects)")
     ap.add_argument("--verify-tokens", type=int, default=4,
                     help="drafted tokens per sequence in the verify-step measurement (1..16)")
-    ap.add_argument("--workload", choices=["mid", "batched", "long"], default="mid",
-                    help="prefill workload: mid = B1 H32 T4096 (the headline), "
-                         "batched = B8 H32 T32768 with a carried state, "
-                         "long = B1 H32 T1048576 (one million-token sequence)")
+    ap.add_argument("--workload", choices=list(WORKLOADS), default="long",
+                    help="headline prefill workload: long = B1 H32 T1048576 (one million-token "
+                         "sequence, the default), mid = B1 H32 T4096, batched = B8 H32 T32768 "
+                         "with a carried state")
     ap.add_argument("--segments", type=int, default=1,
                     help="prefill by a scan over this many segments of each sequence "
-                         "(kda_chunk_prefill_segmented); 1 = the direct chunkwise prefill")
+                         "(kda_chunk_prefill_segmented); 1 = the plan kda_chunk_prefill chooses")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--plan", default=None,
                     help="force the prefill plan (sets KDA_PREFILL_PLAN: split | fused:<ncol>)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 1 GiB device-to-device copies (the reference kernel that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.plan:
         os.environ["KDA_PREFILL_PLAN"] = args.plan
@@ -118,130 +263,67 @@ def main():
 
     import linear_attention_recurrence_05_amd as kda
     from linear_attention_recurrence_05_amd.inputs import (DECODE_CONFIG, PREFILL_CONFIGS,
-                                                            config_inputs, decode_state,
-                                                            decode_step_inputs, prefill_inputs)
+                                                            decode_state, decode_step_inputs,
+                                                            prefill_inputs)
 
     dev = torch.device("cuda:0")
-    kda.lib()
-    cfg_index = {"mid": 1, "batched": 2, "long": 3}[args.workload]
-    cfg = PREFILL_CONFIGS[cfg_index]
-    B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.dk
-    x = config_inputs(cfg_index, dev)
-    o = torch.empty(B, T, H, d, dtype=cfg.dtype, device=dev)
-    ST = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
-    if args.segments > 1:
-        nb = kda.kda_chunk_prefill_segmented_workspace_bytes(B, T, H, d, d, args.segments,
-                                                             cfg.dtype)
-    else:
-        nb = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, cfg.dtype)
-    # segments the plain prefill entry point chooses by itself (1: direct plan)
-    auto_seg = 1 if args.segments > 1 else kda.kda_chunk_prefill_segments(B, T, H, d, d, cfg.dtype)
-    n_seg = args.segments if args.segments > 1 else auto_seg
-    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-    stream = torch.cuda.current_stream()
-    # Cold inputs without a flush kernel: the steps cycle through n_rot copies
-    # of the inputs, so a step's inputs were last touched more than 1 GiB of
-    # other traffic ago (the last-level cache is 256 MB).  A flush by writing
-    # a large buffer leaves that cache full of dirty lines whose write-back
-    # then runs inside the next timed step; its figure is reported beside.
-    in_bytes = sum(t.numel() * t.element_size() for t in x.values() if torch.is_tensor(t))
-    n_rot = min(8, 1 + -(-(1 << 30) // in_bytes))
-    xs = [x] + [{kk: (vv.clone() if torch.is_tensor(vv) else vv) for kk, vv in x.items()}
-                for _ in range(n_rot - 1)]
-
-    def step(i):
-        xi = xs[i % n_rot]
-        if args.segments > 1:
-            kda.kda_chunk_prefill_segmented(xi["q"], xi["k"], xi["v"], xi["z"], xi["beta"],
-                                            xi["A"], xi["g_min"], xi["S0"], o, ST, args.segments,
-                                            ws, stream)
-        else:
-            kda.kda_chunk_prefill(xi["q"], xi["k"], xi["v"], xi["z"], xi["beta"], xi["A"],
-                                  xi["g_min"], xi["S0"], o, ST, ws, stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i, (e0, e1) in enumerate(evs):
-        e0.record(stream)
-        step(args.warmup + i)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    times_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-    ms = sum(times_ms) / len(times_ms)
-    # the same steps, each after a 1 GiB write flush (for reference)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    fl_ms = []
-    for i in range(args.steps):
-        flush.zero_()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        step(0)
-        f1.record(stream)
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
         torch.cuda.synchronize()
-        fl_ms.append(f0.elapsed_time(f1))
-    del flush
-    write_flush_ms = sum(fl_ms) / len(fl_ms)
-    # back-to-back (cache-warm) for reference
-    torch.cuda.synchronize()
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record(stream)
-    for _ in range(args.steps):
-        step(0)
-    w1.record(stream)
-    torch.cuda.synchronize()
-    warm_ms = w0.elapsed_time(w1) / args.steps
-
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "copies": 3}), flush=True)
+        return
+    kda.lib()
+    stream = torch.cuda.current_stream()
+    small = args.workload != "long"
+    head, x = time_prefill(kda, torch, args.workload, stream, dev, args.steps, args.warmup,
+                           segments=args.segments, rotate=small, flush=small)
+    cfg = PREFILL_CONFIGS[WORKLOADS[args.workload]]
+    B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.dk
     tokens = B * T
-    alg_b = prefill_alg_bytes(B, T, H, d, with_s0=x["S0"] is not None)
-    alg_f = prefill_alg_flops(B, T, H, d)
-    gbs = alg_b / (ms * 1e-3) / 1e9
-    tflops = alg_f / (ms * 1e-3) / 1e12
+    ms = head["ms_per_step"]
     line = {
         "metric": "KDA prefill tokens/s (decode steps/s in 'decode'); % of MFMA/HBM roofline",
-        "value": tokens / (ms * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
-        "ms_per_step_median": times_ms[len(times_ms) // 2],
-        "ms_per_step_warm": warm_ms,
-        "ms_per_step_after_write_flush": write_flush_ms,
-        "cold_inputs": f"steps cycle through {n_rot} copies of the inputs ({in_bytes / 2**20:.0f} MiB each)",
-        "wall_s_timed_region": wall,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1); v,z N(0,1); beta=sigmoid(N(0,1)); A~U(-1,1))",
-        "config": {"workload": f"{args.workload}_prefill_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T,
-                   "H": H, "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": -5.0,
-                   "S0": "zeros" if x["S0"] is None else "N(0, 0.01)",
-                   "parallelism": "single GPU",
-                   "plan": (f"segment scan over {args.segments} segments" if args.segments > 1
-                            else f"segment scan over {auto_seg} segments (chosen by "
-                                 "kda_chunk_prefill)" if auto_seg > 1
-                            else ("split" if nb else "fused")),
-                   "workspace_bytes": nb},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": (None if n_seg > 1 else measured_traffic(
-                         f"prefill_{args.workload}_pass_bytes_{'split' if nb else 'fused'}")),
-                     "traffic_unit": "bytes per pass",
-                     "kernel": ("segment-scan prefill (two map passes, segscan_kernel, one "
-                                "full prefill pass)"
-                                if n_seg > 1 else
-                                "prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
-                                else "prefill pass (fused_kernel)"),
-                     "alg_bytes_per_step": alg_b,
-                     "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
-                     "alg_flops_per_step": alg_f},
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
+    for kk in ("ms_per_step_median", "ms_per_step_warm", "ms_per_step_after_write_flush",
+               "cold_inputs", "wall_s_timed_region"):
+        if kk in head:
+            line[kk] = head[kk]
+    cpu_x = None
+    if args.workload == "long" and not args.no_cpu_baseline:
+        # the oracle's sample: the first 16,384 tokens of the same sequence
+        P = 16384
+        cpu_x = {kk: (vv[:, :P].cpu() if kk in ("q", "k", "v", "z", "beta") else
+                      vv.cpu() if hasattr(vv, "cpu") else vv) for kk, vv in x.items()}
+    del x
+    torch.cuda.empty_cache()
+
+    if not args.no_sub:
+        for wl in ("mid", "batched"):
+            if wl == args.workload:
+                continue
+            r, xw = time_prefill(kda, torch, wl, stream, dev, max(5, min(args.steps, 20)),
+                                 args.warmup, rotate=True)
+            del xw
+            torch.cuda.empty_cache()
+            r["metric"] = "KDA prefill tokens/s"
+            line[wl] = r
 
     if not args.no_decode:
         c = DECODE_CONFIG
@@ -380,20 +462,24 @@ def main():
         }
         del S, S_out, xv
 
-    if not args.no_backward and args.workload == "mid":
-        # gradients of the same prefill (dO ~ N(0, 1), dS_T ~ N(0, 1))
-        from linear_attention_recurrence_05_amd.inputs import backward_grads
-        gr = backward_grads(B, T, H, d, d, cfg.dtype, seed=cfg_index, device=dev)
-        gq = [torch.empty_like(x[n]) for n in ("q", "k", "v", "z")]
-        gb = torch.empty(B, T, H, dtype=torch.float32, device=dev)
-        gA = torch.empty(H, dtype=torch.float32, device=dev)
-        gS0 = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
-        nbw = kda.kda_chunk_backward_workspace_bytes(B, T, H, d, d, cfg.dtype)
+    if not args.no_backward:
+        # gradients of the mid workload's prefill (dO ~ N(0, 1), dS_T ~ N(0, 1))
+        from linear_attention_recurrence_05_amd.inputs import backward_grads, config_inputs
+        cm = PREFILL_CONFIGS[1]
+        Bm, Tm, Hm, dm = cm.B, cm.T, cm.H, cm.dk
+        xm = config_inputs(1, dev)
+        gr = backward_grads(Bm, Tm, Hm, dm, dm, cm.dtype, seed=1, device=dev)
+        gq = [torch.empty_like(xm[n]) for n in ("q", "k", "v", "z")]
+        gb = torch.empty(Bm, Tm, Hm, dtype=torch.float32, device=dev)
+        gA = torch.empty(Hm, dtype=torch.float32, device=dev)
+        gS0 = torch.empty(Bm, Hm, dm, dm, dtype=torch.float32, device=dev)
+        nbw = kda.kda_chunk_backward_workspace_bytes(Bm, Tm, Hm, dm, dm, cm.dtype)
         wsb = torch.empty(nbw, dtype=torch.uint8, device=dev)
 
         def run_bwd():
-            kda.kda_chunk_backward(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
-                                   x["S0"], gr["dO"], gr["dST"], *gq, gb, gA, gS0, wsb, stream)
+            kda.kda_chunk_backward(xm["q"], xm["k"], xm["v"], xm["z"], xm["beta"], xm["A"],
+                                   xm["g_min"], xm["S0"], gr["dO"], gr["dST"], *gq, gb, gA, gS0,
+                                   wsb, stream)
 
         run_bwd()
         reps = []
@@ -406,42 +492,51 @@ def main():
             torch.cuda.synchronize()
             reps.append(e0.elapsed_time(e1))
         bms = sorted(reps)[len(reps) // 2]
-        bb = backward_alg_bytes(B, T, H, d)
+        bb = backward_alg_bytes(Bm, Tm, Hm, dm)
         bgbs = bb / (bms * 1e-3) / 1e9
         line["backward"] = {
             "metric": "KDA prefill-backward tokens/s",
-            "value": tokens / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms,
+            "value": Bm * Tm / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms,
             "repetitions": args.backward_steps,
-            "config": {"workload": f"backward_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T, "H": H,
-                       "d_k": d, "d_v": d, "workspace_bytes": nbw},
+            "config": {"workload": f"backward_B{Bm}_H{Hm}_T{Tm}_d{dm}_bf16", "B": Bm, "T": Tm,
+                       "H": Hm, "d_k": dm, "d_v": dm, "workspace_bytes": nbw},
             "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": bgbs / HBM_PEAK_GBS,
                          "traffic": measured_traffic("backward_mid_pass_bytes"),
                          "traffic_unit": "bytes per pass",
-                         "kernel": "backward pass (bwd_ckpt_kernel + bwd_seg_kernel + "
-                                   "bwd_finalize_kernel + bwd_dA_kernel)",
-                         "alg_bytes_per_step": bb},
+                         "kernel": "backward pass (all its launches)",
+                         "alg_bytes_per_step": bb,
+                         "mfma_busy": measured_record("backward_mid_pass_mfma_busy")},
         }
-        del wsb, gq, gS0
+        del wsb, gq, gS0, xm, gr
 
-    if not args.no_cpu_baseline and args.workload == "mid":
+    if not args.no_cpu_baseline:
         import oracle
         threads = len(os.sched_getaffinity(0))
-        xc = {kk: (vv.cpu() if hasattr(vv, "cpu") else vv) for kk, vv in x.items()}
+        if cpu_x is not None:
+            xc, what = cpu_x, (f"the first {cpu_x['q'].shape[1]:,} tokens of the same "
+                               f"{T:,}-token sequence, all {H} heads")
+        else:
+            from linear_attention_recurrence_05_amd.inputs import config_inputs
+            xc = {kk: (vv.cpu() if hasattr(vv, "cpu") else vv)
+                  for kk, vv in config_inputs(WORKLOADS[args.workload], "cpu").items()}
+            what = f"the whole workload (B={B}, T={T}, H={H}, d={d})"
+        n_tok = xc["q"].shape[0] * xc["q"].shape[1]
         reps, t0 = 0, time.perf_counter()
-        while True:   # the whole workload, repeated until about 10 s of CPU work
+        while True:   # repeated until about 10 s of CPU work
             oracle.prefill(xc["q"], xc["k"], xc["v"], xc["z"], xc["beta"], xc["A"], xc["g_min"],
                            xc["S0"], nthreads=threads)
             reps += 1
             dt = time.perf_counter() - t0
             if dt >= 10.0 or reps >= 200:
                 break
+        units = xc["q"].shape[0] * xc["q"].shape[2]
         line["cpu_baseline"] = {
-            "value": reps * tokens / dt, "unit": "tokens/s", "cores": min(threads, B * H),
+            "value": reps * n_tok / dt, "unit": "tokens/s", "cores": min(threads, units),
             "kind": "oracle",
-            "sample": f"the whole workload (B={B}, T={T}, H={H}, d={d}) {reps} times, fp64 "
-                      f"token-by-token recurrence, OpenMP over the {B * H} heads, "
-                      f"{threads} threads available",
+            "sample": f"{what}, {reps} times: fp64 token-by-token recurrence, OpenMP over the "
+                      f"{units} heads, {threads} threads available",
+            "cpu_model": cpu_model(),
             "seconds": dt,
         }
     print(json.dumps(line), flush=True)
