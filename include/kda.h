@@ -146,6 +146,30 @@ kda_status kda_chunk_prefill(const void *q, const void *k, const void *v,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Bytes of the static scratch that kda_chunk_prefill_noalloc uses in place of
+ * a workspace (one copy per GPU the library runs on, held until the process
+ * ends). */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* kda_chunk_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same arguments, results and plan choice as kda_chunk_prefill, but no
+ * workspace argument: the workspace kda_chunk_prefill_workspace_bytes(...)
+ * names is taken from a static device array of KDA_NOALLOC_SCRATCH_BYTES on
+ * the GPU that `stream` runs on.  Sizes needing more than that return
+ * KDA_ERR_WORKSPACE_TOO_SMALL (on the host, before any HIP call).  The call
+ * allocates nothing; its first call on a device looks up that device's copy
+ * of the array (hipGetSymbolAddress).  Every call on one GPU shares that GPU's
+ * scratch, so calls that overlap in time on one GPU (different streams, or
+ * different host threads without ordering) race and must not be issued; calls
+ * in one stream are ordered and safe.  Nothing is expected to be zero in the
+ * scratch between calls: every call writes what it reads. */
+kda_status kda_chunk_prefill_noalloc(const void *q, const void *k, const void *v,
+                                     const void *z, const float *beta, const float *A,
+                                     float g_min, const float *S0, void *o, float *S_T,
+                                     int B, int T, int H, int d_k, int d_v, kda_dtype dt,
+                                     void *stream);
+
 /* Bytes of device workspace kda_chunk_prefill_segmented needs (0 for
  * arguments it would reject): the inner prefill's workspace for B * n_seg
  * rows of T / n_seg tokens, four state tensors [B * n_seg, H, d_k, d_v] fp32,

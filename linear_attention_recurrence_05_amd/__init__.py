@@ -36,7 +36,7 @@ from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KDA_MAX_DECODE_TOKENS, KdaError
                    chunk_prefill_segmented, decode_step, decode_tokens, kda_chunk_backward,
                    kda_chunk_backward_workspace_bytes, kda_chunk_prefill_segmented,
                    kda_chunk_prefill_segmented_workspace_bytes,
-                   kda_chunk_prefill, kda_chunk_prefill_paged,
+                   kda_chunk_prefill, kda_chunk_prefill_noalloc, kda_chunk_prefill_paged,
                    kda_chunk_prefill_paged_workspace_bytes, kda_chunk_prefill_segments,
                    kda_chunk_prefill_workspace_bytes,
                    kda_decode_step, kda_decode_step_paged, kda_decode_tokens,
@@ -47,7 +47,7 @@ __all__ = ["KDA_BF16", "KDA_CHUNK", "KDA_F32", "KDA_MAX_DECODE_TOKENS", "KdaErro
            "KdaLibraryMissing", "abi_version", "chunk_backward", "chunk_prefill",
            "chunk_prefill_segmented", "kda_chunk_backward", "kda_chunk_backward_workspace_bytes",
            "kda_chunk_prefill_segmented", "kda_chunk_prefill_segmented_workspace_bytes", "decode_step", "decode_tokens",
-           "kda_chunk_prefill", "kda_chunk_prefill_paged", "kda_chunk_prefill_paged_workspace_bytes",
+           "kda_chunk_prefill", "kda_chunk_prefill_noalloc", "kda_chunk_prefill_paged", "kda_chunk_prefill_paged_workspace_bytes",
            "kda_chunk_prefill_segments",
            "kda_chunk_prefill_workspace_bytes",
            "kda_decode_step", "kda_decode_step_paged", "kda_decode_tokens",

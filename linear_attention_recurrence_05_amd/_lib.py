@@ -41,6 +41,8 @@ _SIGNATURES = {
     "kda_chunk_prefill_segments": ([_i, _i, _i, _i, _i, _i], _i),
     "kda_chunk_prefill": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6
                           + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "kda_chunk_prefill_noalloc": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6
+                                  + [_vp], ctypes.c_int),
     "kda_decode_step": ([_vp] * 6 + [ctypes.c_float, _vp, _vp] + [_i] * 5 + [_vp], ctypes.c_int),
     "kda_decode_tokens": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6 + [_vp],
                           ctypes.c_int),
@@ -208,6 +210,20 @@ def kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace=None, st
                                  float(g_min), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
                                  _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "kda_chunk_prefill")
+
+
+def kda_chunk_prefill_noalloc(q, k, v, z, beta, A, g_min, S0, o, S_T, stream=None):
+    """C entry point kda_chunk_prefill_noalloc (no workspace: the library's
+    static per-GPU scratch)."""
+    c = _Args("kda_chunk_prefill_noalloc", q)
+    (B, T, H), dk, dv = _tokens(c, q, k, v, z, beta, A)
+    c("S0", S0, torch.float32, (B, H, dk, dv), required=False)
+    c("o", o, c.dt, (B, T, H, dv))
+    c("S_T", S_T, torch.float32, (B, H, dk, dv), required=False)
+    st = lib().kda_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta),
+                                         _ptr(A), float(g_min), _ptr(S0), _ptr(o), _ptr(S_T),
+                                         B, T, H, dk, dv, _dtype_code(q), _stream(stream))
+    _check(st, "kda_chunk_prefill_noalloc")
 
 
 def kda_decode_step(q, k, v, z, beta, A, g_min, S, o, stream=None):

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/kda.h"
@@ -165,10 +166,57 @@ int kda_chunk_prefill_segments(int B, int T, int H, int d_k, int d_v, kda_dtype 
     return kda::auto_segments(B, T, H, d_k, dt == KDA_BF16);
 }
 
-kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* z,
-                             const float* beta, const float* A, float g_min, const float* S0,
-                             void* o, float* S_T, int B, int T, int H, int d_k, int d_v,
-                             kda_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Static scratch of kda_chunk_prefill_noalloc: one copy per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in; the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device (with that device current) and kept in g_scratch.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the scratch on the device `stream` runs on.
+kda_status scratch_for(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KDA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return fail(KDA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(KDA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess)
+            return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        if (e2 != hipSuccess)
+            return fail(KDA_ERR_HIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(e2));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return KDA_OK;
+}
+
+// kda_chunk_prefill and kda_chunk_prefill_noalloc: validation (host only,
+// before any HIP call), then the launch.  With use_scratch the workspace is
+// the device's static scratch (the caller's workspace arguments are unused).
+kda_status prefill_entry(const char* name, const void* q, const void* k, const void* v,
+                         const void* z, const float* beta, const float* A, float g_min,
+                         const float* S0, void* o, float* S_T, int B, int T, int H, int d_k,
+                         int d_v, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         void* stream, bool use_scratch) {
     kda_status s = check_common(d_k, d_v, dt, g_min);
     if (s != KDA_OK) return s;
     size_t nel, ntok;
@@ -178,14 +226,23 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     const bool bf = dt == KDA_BF16;
     const int nseg = kda::auto_segments(B, T, H, d_k, bf);
     const size_t need = prefill_ws_bytes(B, T, H, d_k, bf, nseg);
+    if (use_scratch) {
+        workspace = nullptr;   // the scratch overlaps no caller buffer
+        if (need > KDA_NOALLOC_SCRATCH_BYTES)
+            return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                        "%s: these sizes need %zu bytes of scratch, the static scratch holds %zu "
+                        "(call kda_chunk_prefill with a workspace instead)",
+                        name, need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+    }
     const Range r[] = {{"q", q, nel * es, 16},          {"k", k, nel * es, 16},
                        {"v", v, nel * es, 16},          {"z", z, nel * es, 16},
                        {"beta", beta, ntok * 4, 4},     {"A", A, (size_t)H * 4, 4},
                        {"S0", S0, st_bytes, 4},         {"o", o, nel * es, 16},
                        {"S_T", S_T, st_bytes, 4},       {"workspace", workspace, need, 16}};
-    const bool req[] = {true, true, true, true, true, true, false, true, false, need > 0};
+    const bool req[] = {true, true, true, true, true, true, false, true, false,
+                        need > 0 && !use_scratch};
     if ((s = check_ptrs(r, 10, req)) != KDA_OK) return s;
-    if (workspace_bytes < need)
+    if (!use_scratch && workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     need);
     // outputs (o, S_T, workspace) against every other range; S_T == S0 exactly is allowed
@@ -197,6 +254,8 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                 return fail(KDA_ERR_ALIASING, "%s overlaps %s", r[out].name, r[i].name);
         }
     }
+    if (use_scratch && need > 0 && (s = scratch_for((hipStream_t)stream, &workspace)) != KDA_OK)
+        return s;
     kda::PrefillArgs a{q, k, v, z, beta, A, g_min, kda::dense_state(S0, S_T), o, B, T, H, d_k,
                        dt == KDA_BF16};
     if (nseg > 1)
@@ -204,6 +263,26 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                           "kda_chunk_prefill launch (segment scan)");
     const kda::PlanInfo plan = kda::choose_plan(B, T, H, d_k, bf);
     return hip_status(kda::launch_prefill(a, plan, workspace, (hipStream_t)stream), "kda_chunk_prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* z,
+                             const float* beta, const float* A, float g_min, const float* S0,
+                             void* o, float* S_T, int B, int T, int H, int d_k, int d_v,
+                             kda_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_entry("kda_chunk_prefill", q, k, v, z, beta, A, g_min, S0, o, S_T, B, T, H,
+                         d_k, d_v, dt, workspace, workspace_bytes, stream, false);
+}
+
+kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const void* z,
+                                     const float* beta, const float* A, float g_min,
+                                     const float* S0, void* o, float* S_T, int B, int T, int H,
+                                     int d_k, int d_v, kda_dtype dt, void* stream) {
+    return prefill_entry("kda_chunk_prefill_noalloc", q, k, v, z, beta, A, g_min, S0, o, S_T, B,
+                         T, H, d_k, d_v, dt, nullptr, 0, stream, true);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* z,

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk",
               "kda_chunk_backward_workspace_bytes", "kda_chunk_backward",
               "kda_chunk_prefill_segmented_workspace_bytes", "kda_chunk_prefill_segmented",
-              "kda_chunk_prefill_paged_workspace_bytes"]:
+              "kda_chunk_prefill_paged_workspace_bytes", "kda_chunk_prefill_noalloc"]:
         assert n in names
 
 
@@ -234,6 +234,32 @@ def test_paged_prefill_and_tokens_reject():
                                    fake(6), 4, fake(7), fake(7), fake(8), 2, 17, 2, 32, 32,
                                    kda.KDA_F32, None)
     assert st == E["KDA_ERR_INVALID_SHAPE"]
+
+
+def test_noalloc_prefill_rejects_on_the_host():
+    """kda_chunk_prefill_noalloc checks its arguments like kda_chunk_prefill,
+    and rejects sizes whose workspace exceeds its static scratch, before any
+    HIP call."""
+    L = kda.lib()
+
+    def call(**over):
+        a = dict(q=fake(0), k=fake(1), v=fake(2), z=fake(3), beta=fake(4), A=fake(5), g_min=-5.0,
+                 S0=None, o=fake(7), S_T=fake(8), B=1, T=64, H=2, d_k=32, d_v=32, dt=kda.KDA_F32)
+        a.update(over)
+        st = L.kda_chunk_prefill_noalloc(*(a[n] for n in ("q", "k", "v", "z", "beta", "A",
+                                                          "g_min", "S0", "o", "S_T", "B", "T",
+                                                          "H", "d_k", "d_v", "dt")), None)
+        return st, L.kda_last_error().decode()
+
+    assert call(q=None)[0] == E["KDA_ERR_NULL_POINTER"]
+    assert call(g_min=1.0)[0] == E["KDA_ERR_INVALID_VALUE"]
+    assert call(o=fake(0))[0] == E["KDA_ERR_ALIASING"]
+    B, T, H, d = 1, 16384, 32, 128
+    need = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, kda.KDA_BF16)
+    assert need > 256 << 20
+    st, detail = call(B=B, T=T, H=H, d_k=d, d_v=d, dt=kda.KDA_BF16)
+    assert st == E["KDA_ERR_WORKSPACE_TOO_SMALL"], detail
+    assert f"need {need} bytes" in detail and str(256 << 20) in detail
 
 
 def test_paged_prefill_workspace_query_is_its_own():
