@@ -34,9 +34,10 @@
  * - `dt` gives the element type of q, k, v, z and o (KDA_F32 or KDA_BF16);
  *   beta, A, g_min and the state are always fp32.  Accumulation is fp32.
  * - Supported head sizes: (d_k, d_v) in {(32, 32), (128, 128)}.
- * - Size limits (KDA_ERR_INVALID_SHAPE beyond them): B * H <= 2^26,
- *   B * T * H <= 2^40, H * d_k <= 2^24 (the kernels address 32 consecutive
- *   tokens of one head with 32-bit byte offsets).
+ * - Size limits (KDA_ERR_INVALID_SHAPE beyond them): T <= 2^30,
+ *   B * H <= 2^26, B * T * H <= 2^40, H * d_k <= 2^24 (the kernels address 32
+ *   consecutive tokens of one head with 32-bit byte offsets and count chunks
+ *   in 32-bit integers).
  * - beta is used as given (expected in (0, 1)); q and k are used as given
  *   (no normalisation inside).  g_min must lie in [-5, 0]: the chunked form
  *   rescales 16-token tiles by factors up to exp(-16 g_min), which must stay
@@ -67,7 +68,11 @@ extern "C" {
 /* Largest token count of one kda_decode_tokens call. */
 #define KDA_MAX_DECODE_TOKENS 16
 
-typedef enum kda_status {
+/* Status codes and element types are plain ints in the ABI (any value a
+ * caller passes in is well defined; unknown ones are rejected or named
+ * "KDA_ERR_UNKNOWN"). */
+typedef int kda_status;
+enum {
     KDA_OK = 0,
     KDA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL            */
     KDA_ERR_INVALID_SHAPE = 2,       /* B, T or H < 1, or a size limit broken */
@@ -77,9 +82,10 @@ typedef enum kda_status {
     KDA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace below the queried size      */
     KDA_ERR_ALIASING = 7,            /* an output overlaps an input illegally */
     KDA_ERR_HIP = 8                  /* the HIP runtime reported an error     */
-} kda_status;
+};
 
-typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+typedef int kda_dtype;
+enum { KDA_F32 = 0, KDA_BF16 = 1 };
 
 /* KDA_ABI_VERSION of the built library. */
 int kda_abi_version(void);

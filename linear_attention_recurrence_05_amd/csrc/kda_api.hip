@@ -43,6 +43,9 @@ bool overlap(const Range& a, const Range& b) {
     return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
 }
 
+// Longest sequence: chunk counts and token offsets are formed in 32-bit ints.
+constexpr int kMaxT = 1 << 30;
+
 bool aligned(const void* p, unsigned a) { return ((uintptr_t)p & (uintptr_t)(a - 1)) == 0; }
 
 kda_status check_common(int d_k, int d_v, kda_dtype dt, float g_min) {
@@ -75,6 +78,7 @@ kda_status hip_status(hipError_t e, const char* what) {
 // Shape check shared by prefill-style calls; returns element counts.
 kda_status check_shape(int B, int T, int H, int d, size_t& n_tok_el, size_t& n_tok) {
     if (B < 1 || T < 1 || H < 1) return fail(KDA_ERR_INVALID_SHAPE, "B=%d T=%d H=%d must all be >= 1", B, T, H);
+    if (T > kMaxT) return fail(KDA_ERR_INVALID_SHAPE, "T=%d is too large (limit 2^30)", T);
     const unsigned long long tok = (unsigned long long)B * (unsigned long long)T * (unsigned long long)H;
     if ((long long)B * H > (1LL << 26) || tok > (1ULL << 40))
         return fail(KDA_ERR_INVALID_SHAPE, "B*T*H = %llu is too large", tok);
@@ -403,7 +407,7 @@ size_t kda_chunk_prefill_segmented_workspace_bytes(int B, int T, int H, int d_k,
                                                    int n_seg, kda_dtype dt) {
     if (dt != KDA_F32 && dt != KDA_BF16) return 0;
     if (!(d_k == d_v && (d_k == 32 || d_k == 128))) return 0;
-    if (B < 1 || T < 1 || H < 1 || n_seg < 1 || T % n_seg != 0 ||
+    if (B < 1 || T < 1 || H < 1 || T > kMaxT || n_seg < 1 || T % n_seg != 0 ||
         (long long)B * n_seg * H > (1LL << 26) || (unsigned long long)B * T * H > (1ULL << 40) ||
         (long long)H * d_k > (1LL << 24))
         return 0;
@@ -452,7 +456,7 @@ kda_status kda_chunk_prefill_segmented(const void* q, const void* k, const void*
 size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v, kda_dtype dt) {
     if (dt != KDA_F32 && dt != KDA_BF16) return 0;
     if (!(d_k == d_v && (d_k == 32 || d_k == 128))) return 0;
-    if (B < 1 || T < 1 || H < 1 || (long long)B * H > (1LL << 26) ||
+    if (B < 1 || T < 1 || H < 1 || T > kMaxT || (long long)B * H > (1LL << 26) ||
         (unsigned long long)B * T * H > (1ULL << 40) || (long long)H * d_k > (1LL << 24))
         return 0;
     return kda::bwd_layout(B, T, H, d_k, dt == KDA_BF16).total;

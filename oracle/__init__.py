@@ -51,7 +51,9 @@ class Oracle:
     """ctypes wrapper around one build of ``kda_oracle.c``."""
 
     def __init__(self, path: str | None = None):
-        path = path or library_path()
+        # KDA_ORACLE_LIB: another build of the same source (the sanitizer
+        # test runs the pins against one)
+        path = path or os.environ.get("KDA_ORACLE_LIB") or library_path()
         if not os.path.exists(path):
             build()
         lib = ctypes.CDLL(path)

@@ -92,6 +92,8 @@ E = {n: i for i, n in enumerate(_lib._STATUS)}
     (dict(T=0), "KDA_ERR_INVALID_SHAPE"),
     (dict(H=-1), "KDA_ERR_INVALID_SHAPE"),
     (dict(B=1, T=16, H=(1 << 19) + 1), "KDA_ERR_INVALID_SHAPE"),   # H * d_k above 2^24 (d_k 32)
+    (dict(B=1, T=(1 << 30) + 1, H=1), "KDA_ERR_INVALID_SHAPE"),    # T above 2^30
+    (dict(B=1, T=2**31 - 1, H=1), "KDA_ERR_INVALID_SHAPE"),
     (dict(g_min=-5.5), "KDA_ERR_INVALID_VALUE"),
     (dict(g_min=0.25), "KDA_ERR_INVALID_VALUE"),
     (dict(g_min=float("nan")), "KDA_ERR_INVALID_VALUE"),
