@@ -211,16 +211,24 @@ kda_status kda_chunk_prefill_segmented(const void *q, const void *k,
 
 /* Bytes of device workspace kda_chunk_backward needs for these sizes (0 for
  * arguments it would reject).  It holds the state at the start of every
- * 16-token chunk (B * H * ceil(T / 16) * d_k * d_v * 4 bytes), the delta-rule
- * correction v - S'^T k of every token (B * T * H * d_v * 4 bytes), one state
- * per (b, h) carried between launches, partial sums of one segment of the
- * sequence (about 256 MiB, or 128 tokens' worth if that is more) and, when T
- * splits into segments of 256 or more tokens, a segment scan's buffers. */
+ * 16-token chunk (B * H * ceil(T / 16) * d_k * d_v * 4 bytes) and, when T
+ * splits into segments of 256 or more tokens, a segment scan's buffers; for
+ * bf16 at d = 128 also the gradient of every chunk's end state (as much
+ * again) and the chain's operands (13,824 bytes per chunk and head);
+ * otherwise the delta-rule correction v - S'^T k of every token
+ * (B * T * H * d_v * 4 bytes), one state per (b, h) carried between launches
+ * and partial sums of one segment of the sequence (about 256 MiB, or 128
+ * tokens' worth if that is more). */
 size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
                                           kda_dtype dt);
 
 /* Gradients of kda_chunk_prefill (the pages give no backward pass; this is
- * the exact gradient of the recurrence above, for training).  With dO the
+ * the exact gradient of the recurrence above, for training; dev.to "Kimi K3
+ * Architecture ...", section "The Sequence Bottleneck": chunkwise parallel
+ * execution, which training relies on).  For bf16 at d = 128 it runs the
+ * chunk equations differentiated: a chain of chunk-end state gradients from
+ * dS_T back to dS0, then every chunk's gradients at once, all products on
+ * MFMA; other sizes run a token-level reverse sweep.  With dO the
  * gradient of o [B, T, H, d_v] (element type dt) and dS_T that of the final
  * state [B, H, d_k, d_v] fp32 (NULL: zero), it writes the gradients of
  * L = sum(dO * o) + sum(dS_T * S_T):
@@ -238,7 +246,8 @@ size_t kda_chunk_backward_workspace_bytes(int B, int T, int H, int d_k, int d_v,
  * The sweep runs in fp32 whatever dt is.  dA and dbeta are summed over
  * value-column blocks and tokens in a fixed order (deterministic).
  * Test and tuning hook only (production callers leave it unset): the
- * environment variable KDA_BACKWARD_PLAN=chain selects the chunk-level plan (a chain of per-chunk state gradients, then
+ * environment variable KDA_BACKWARD_PLAN=sweep forces the token-level sweep
+ * for bf16 at d = 128 too, and KDA_BACKWARD_PLAN=chain selects the chunk-level plan (a chain of per-chunk state gradients, then
  * every chunk's reverse sweep at once) instead of the default sweep over the
  * whole sequence; the workspace query honours the same variable. */
 kda_status kda_chunk_backward(const void *q, const void *k, const void *v,

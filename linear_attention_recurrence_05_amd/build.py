@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_pair.hip", "kda_backward.hip",
-           "kda_segscan.hip"]
+           "kda_bwd_chunk.hip", "kda_segscan.hip"]
 ARCH = "gfx950"
 
 

@@ -271,7 +271,7 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_ckpt_kernel(
             for (int j = 0; j < N; ++j) S[i][j] = 0.f;
     }
     float* ck = ckpt + (u * G::NCB + cb) * (size_t)NC * (D * N) + (R * l) * N;
-    float* uc = ucor + (u * G::NCB + cb) * (size_t)T * N;
+    float* uc = ucor ? ucor + (u * G::NCB + cb) * (size_t)T * N : nullptr;
     const size_t vstride = (size_t)H * D;     // elements between tokens of a head
     const E* vb = v + ((size_t)b * T * H + h) * D + cb * N;
     Stage<E, R, false> st;
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(BwdGeom<D>::W) void bwd_ckpt_kernel(
             float uu[N];
 #pragma unroll
             for (int j = 0; j < N; ++j) uu[j] = sl.x[buf][r][j] - p[j];
-            if (l == 0) store8f(uc + (size_t)(n * kChunk + r) * N, uu);
+            if (l == 0 && uc) store8f(uc + (size_t)(n * kChunk + r) * N, uu);
 #pragma unroll
             for (int i = 0; i < R; ++i)
 #pragma unroll
@@ -739,6 +739,13 @@ bool bwd_plan_chain(int T) {
     return env && std::strcmp(env, "chain") == 0 && T > kChunk;
 }
 
+// The chunkwise MFMA plan (kda_bwd_chunk.hip) for bf16 at d = 128 unless a
+// token-level plan is forced (KDA_BACKWARD_PLAN = "sweep" or "chain").
+bool bwd_plan_chunk(int d, bool is_bf16) {
+    const char* env = std::getenv("KDA_BACKWARD_PLAN");
+    return bwd_chunk_ok(d, is_bf16) && !env;
+}
+
 BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     BwdLayout L;
     // The forward sweep runs as R segments side by side, each from its start
@@ -754,6 +761,7 @@ BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
     const size_t units = (size_t)B * H;
     const int NCB = d / kBwdCols;
     L.NC = (T + kChunk - 1) / kChunk;
+    L.chunk = bwd_plan_chunk(d, is_bf16);
     L.ntb = (T + kBwdTokBlock - 1) / kBwdTokBlock;
     // segment length: a multiple of the finalize token block, with the
     // partials of one segment within kBwdPartialBudget bytes
@@ -774,24 +782,36 @@ BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16) {
         return o;
     };
     L.ckpt = take(units * L.NC * (size_t)d * d * sizeof(float));
-    L.carry = take(units * (size_t)d * d * sizeof(float));
-    L.ucor = take(units * (size_t)T * d * sizeof(float));
-    const size_t pel = (size_t)NCB * units * seg;   // partial rows
-    L.pq = take(pel * d * sizeof(float));
-    L.pk = take(pel * d * sizeof(float));
-    L.pg = take(pel * d * sizeof(float));
-    L.pb = take(pel * sizeof(float));
-    L.dA_part = take(units * L.ntb * sizeof(float));
-    // chain plan: the gate and intra-chunk exports, and the end-state
-    // gradient of every chunk
-    L.chain = bwd_plan_chain(T);
-    L.Gc = L.Tm = L.Aqk = L.gam = L.dSend = 0;
-    if (L.chain) {
-        L.Gc = take(units * (size_t)T * d * sizeof(float));
-        L.Tm = take(units * L.NC * (size_t)256 * sizeof(float));
-        L.Aqk = take(units * L.NC * (size_t)256 * sizeof(float));
-        L.gam = take(units * L.NC * (size_t)d * sizeof(float));
+    L.fac = L.dSend = 0;
+    if (L.chunk) {
+        // chunkwise plan: checkpoints, the chain's operand blocks, every
+        // chunk's end-state gradient and a dA term per chunk
+        L.fac = take(units * L.NC * bwd_chunk_fac_bytes());
         L.dSend = take(units * L.NC * (size_t)d * d * sizeof(float));
+        L.dA_part = take(units * L.NC * sizeof(float));
+        L.carry = L.ucor = L.pq = L.pk = L.pg = L.pb = 0;
+        L.chain = false;
+        L.Gc = L.Tm = L.Aqk = L.gam = 0;
+    } else {
+        L.carry = take(units * (size_t)d * d * sizeof(float));
+        L.ucor = take(units * (size_t)T * d * sizeof(float));
+        const size_t pel = (size_t)NCB * units * seg;   // partial rows
+        L.pq = take(pel * d * sizeof(float));
+        L.pk = take(pel * d * sizeof(float));
+        L.pg = take(pel * d * sizeof(float));
+        L.pb = take(pel * sizeof(float));
+        L.dA_part = take(units * L.ntb * sizeof(float));
+        // chain plan: the gate and intra-chunk exports, and the end-state
+        // gradient of every chunk
+        L.chain = bwd_plan_chain(T);
+        L.Gc = L.Tm = L.Aqk = L.gam = L.dSend = 0;
+        if (L.chain) {
+            L.Gc = take(units * (size_t)T * d * sizeof(float));
+            L.Tm = take(units * L.NC * (size_t)256 * sizeof(float));
+            L.Aqk = take(units * L.NC * (size_t)256 * sizeof(float));
+            L.gam = take(units * L.NC * (size_t)d * sizeof(float));
+            L.dSend = take(units * L.NC * (size_t)d * d * sizeof(float));
+        }
     }
     L.segws = L.oscr = 0;
     if (L.R > 1) {
@@ -835,9 +855,17 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
         Sseg = (const float*)(ws + L.segws + SL.Sin);
     }
     hipLaunchKernelGGL((bwd_ckpt_kernel<E, D>), dim3((unsigned)(units * L.R * G::NCB)), block, 0,
-                       stream, k, v, z, a.beta, a.A, a.g_min, a.S0, Sseg, L.R, ckpt, ucor, a.B,
-                       a.T, a.H);
+                       stream, k, v, z, a.beta, a.A, a.g_min, a.S0, Sseg, L.R, ckpt,
+                       L.chunk ? nullptr : ucor, a.B, a.T, a.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (L.chunk) {
+        if ((e = launch_bwd_chunk(a, ckpt, ws + L.fac, (float*)(ws + L.dSend), dA_part, stream)) !=
+            hipSuccess)
+            return e;
+        hipLaunchKernelGGL(bwd_dA_kernel, dim3(a.H), dim3(256), 0, stream, dA_part, a.dA, a.B, a.H,
+                           L.NC);
+        return hipGetLastError();
+    }
     const float* dSend = nullptr;
     if (L.chain) {
         // chunk factors (the intra-chunk stage's exports) and the chain

@@ -1,0 +1,685 @@
+// kda_bwd_chunk.hip -- gradients of the KDA prefill in the chunkwise form, on
+// MFMA, for bf16 inputs at d_k = d_v = 128.
+//
+// The pages describe no backward pass (the dev.to page "Kimi K3 Architecture
+// ...", section "The Sequence Bottleneck", says chunkwise parallel execution
+// runs the within-chunk and state products as dense matrix products, which
+// training relies on).  This is the exact gradient of the chunk equations of
+// the forward (kda_chunk.hpp), differentiated step by step.  For a chunk with
+// start state S, end-state gradient dS (of S' = Diag(gam) S + Kd^T U) and
+// output gradient dO:
+//   dU  = Kd dS + Aqk^T dO            dW = Tm^T dU         (dv = dW)
+//   dS_start = Diag(gam) dS + Qt^T dO - Kt^T dW           (the chain)
+//   W   = V - Kt S,   U = Tm W
+//   dQt = dO S^T + dAqk Kh            dAqk = tril_0(dO U^T)
+//   dKt = -dW S^T + dP Kh             dKh  = dAqk^T Qt + dP^T Kt
+//   dKd = U dS^T                      dgam = rowsum(dS o S)
+//   dTm = dU W^T,  dbeta_j += sum_r dTm[r][j] Ninv[r][j],  dN = dTm Diag(beta)
+//   dM  = -Ninv^T dN Ninv^T,  dA = tril_{-1}(dM),  dbeta_r += sum_j dA[r][j] P[r][j]
+//   dP  = Diag(beta) dA                (P = Kt Kh^T, Ninv = (I + Akk)^{-1})
+//   dk  = dKt e^G + dKh e^{-G} + dKd gam e^{-G},   dq = dQt e^G
+//   dG  = dKt o Kt - dKh o Kh + dQt o Qt - dKd o Kd, plus at the chunk's last
+//         row sum_r dKd o Kd + dgam o gam;  dg = reverse cumsum of dG
+// and through the gate dz = dg g_min s (1 - s) e^{A_h}, dA_h += dg g_min s (1 - s) x.
+//
+// Launches (after the forward checkpoints S at every chunk start, which
+// kda_backward.hip's bwd_ckpt_kernel writes):
+//   bwd_fac_kernel    one workgroup per (b, h, chunk): the chunk's factors,
+//                     written as the chain's MFMA operands (13,824 bytes).
+//   bwd_dchain_kernel one wave per (b, h, 16 value columns): dS from dS_T back
+//                     to dS0 over the chunks, last first (14 MFMAs per chunk),
+//                     storing each chunk's end-state gradient.
+//   bwd_grad_kernel   one workgroup per (b, h, chunk), all chunks at once:
+//                     recomputes the factors and forms every gradient from S
+//                     and dS by MFMA products over the 128 key or value
+//                     channels; writes dq, dk, dv, dz, dbeta and a dA term.
+// Precision: the gradient kernel forms every product from fp32 values split
+// into two bf16 parts, x = hi + lo, as hi*hi + hi*lo + lo*hi (three MFMAs;
+// inputs that are bf16 already need two), which keeps about 16 bits of each
+// operand -- the gate gradient dA sums many terms that largely cancel.  The
+// chain uses the factors' leading bf16 part against fp32 state gradients, as
+// the forward's state chain does.  Accumulation and the triangular algebra
+// are fp32.
+#include "kda_chunk.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRS = kD + 8;      // bf16 row stride of [16][128] tiles in LDS (16 B of padding)
+constexpr int kRF = kD + 4;      // fp32 row stride of [16][128] tiles in LDS (16 B of padding)
+
+// Chain operand block of one chunk (lane-major, 16-byte pieces): the layout
+// bwd_fac_kernel writes and bwd_dchain_kernel reads.
+struct CBlk {
+    static constexpr int KD = 0;            // Kd, A-row order: 4 slots x 64 lanes x 16 B
+    static constexpr int QK = KD + 4096;    // [Qt^T | -Kt^T] K = 32 A operands: 8 tiles x 64 x 16 B
+    static constexpr int AQT = QK + 8192;   // Aqk^T, K = 16 A operand: 64 x 8 B
+    static constexpr int TMT = AQT + 512;   // Tm^T, K = 16 A operand: 64 x 8 B
+    static constexpr int GAM = TMT + 512;   // gam, fp32 x 128
+    static constexpr int BYTES = GAM + 512;
+};
+static_assert(CBlk::BYTES == 13824, "chain block size");
+
+// Factors of one chunk in LDS, natural layouts (row r = the chunk's token).
+struct Fac {
+    float G[16][kD];                       // chunk-local cumulative log-decay
+    float gam[kD];                         // e^{G_15}
+    float beta[16];                        // 0 on padded rows
+    float P[16][16];                       // Kt Kh^T
+    float Aqk[16][16];                     // tril_0(Qt Kh^T)
+    float Akk[16][16];                     // tril_{-1}(Diag(beta) P)
+    float Ninv[16][16];                    // (I + Akk)^{-1}
+    float Kt[16][kRF], Kh[16][kRF], Qt[16][kRF], Kd[16][kRF];
+};
+
+// The chunk's raw rows (the finals need k, q, z in fp32) and dO.
+struct Raw {
+    bf16 k[16][kRS], q[16][kRS], z[16][kRS], dO[16][kRS];
+};
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+// 8 consecutive bf16 of an LDS row as one MFMA operand.
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// An fp32 operand as two bf16 parts, x = hi + lo (lo = the rounding error of hi).
+struct B8 {
+    bf16x8 hi, lo;
+};
+struct B4 {
+    bf16x4 hi, lo;
+};
+__device__ __forceinline__ B8 split8(f32x4 a, f32x4 b) {
+    B8 r;
+    r.hi = pack8(a, b);
+    f32x4 ra, rb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ra[e] = a[e] - (float)r.hi[e];
+        rb[e] = b[e] - (float)r.hi[4 + e];
+    }
+    r.lo = pack8(ra, rb);
+    return r;
+}
+__device__ __forceinline__ B4 split4(f32x4 a) {
+    B4 r;
+    r.hi = pack4(a);
+    f32x4 ra;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ra[e] = a[e] - (float)r.hi[e];
+    r.lo = pack4(ra);
+    return r;
+}
+// 8 consecutive fp32 of an LDS row (16-byte aligned), split.
+__device__ __forceinline__ B8 ld8s(const float* p) {
+    return split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4));
+}
+// acc + a b to about 16 bits of both operands (the lo*lo term is dropped).
+__device__ __forceinline__ f32x4 mma3(const B8& a, const B8& b, f32x4 acc) {
+    acc = mma_bf16_k32(a.hi, b.hi, acc);
+    acc = mma_bf16_k32(a.hi, b.lo, acc);
+    return mma_bf16_k32(a.lo, b.hi, acc);
+}
+// ... with an exact bf16 left operand.
+__device__ __forceinline__ f32x4 mma2(bf16x8 a, const B8& b, f32x4 acc) {
+    acc = mma_bf16_k32(a, b.hi, acc);
+    return mma_bf16_k32(a, b.lo, acc);
+}
+__device__ __forceinline__ f32x4 mma3(const B4& a, const B4& b, f32x4 acc) {
+    acc = mma_bf16_k16(a.hi, b.hi, acc);
+    acc = mma_bf16_k16(a.hi, b.lo, acc);
+    return mma_bf16_k16(a.lo, b.hi, acc);
+}
+
+// Factors of chunk n of (b, h) into F (and, with raw, the raw rows and dO).
+// 256 threads; ends with a workgroup barrier after which F is complete.
+template <bool RAW>
+__device__ __forceinline__ void bwd_factors(Fac& F, Raw* raw, const bf16* __restrict__ q,
+                                            const bf16* __restrict__ k,
+                                            const bf16* __restrict__ z,
+                                            const float* __restrict__ beta,
+                                            const bf16* __restrict__ dO, const GateConsts& gc,
+                                            int b, int h, int n, int T, int H) {
+    const int tid = (int)threadIdx.x;
+    const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
+    const int L = cp.L;
+    const int rowb = (int)(cp.rstride * 2);
+    if (tid < kD) {
+        // one key channel per thread, all 16 rows (rows past L read 0 and
+        // get retention 1, so G stays at its last value)
+        const int c = tid;
+        const Rsrc rk = chunk_rsrc<kD>(k, cp, 2), rq = chunk_rsrc<kD>(q, cp, 2),
+                   rz = chunk_rsrc<kD>(z, cp, 2);
+        float kh[16];
+        float Gacc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int off = r * rowb + c * 2;
+            const uint32_t kb = buf_load<unsigned short>(rk, off);
+            const uint32_t qb = buf_load<unsigned short>(rq, off);
+            const uint32_t zb = buf_load<unsigned short>(rz, off);
+            const float kf = bf16_bits_to_f32(kb), qf = bf16_bits_to_f32(qb);
+            const float zf = bf16_bits_to_f32(zb);
+            const float keep = r < L ? 1.f : 0.f;
+            Gacc += keep * gc.gmin * gate_sigmoid(gc, zf);
+            F.G[r][c] = Gacc;
+            const float ex = fast_exp2(Gacc * kLog2e), rex = fast_rcp(ex);
+            F.Kt[r][c] = kf * ex;
+            F.Qt[r][c] = qf * ex;
+            kh[r] = kf * rex;
+            F.Kh[r][c] = kh[r];
+            if constexpr (RAW) {
+                raw->k[r][c] = __builtin_bit_cast(bf16, (unsigned short)kb);
+                raw->q[r][c] = __builtin_bit_cast(bf16, (unsigned short)qb);
+                raw->z[r][c] = __builtin_bit_cast(bf16, (unsigned short)zb);
+            }
+        }
+        const float gam = fast_exp2(Gacc * kLog2e);
+        F.gam[c] = gam;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) F.Kd[r][c] = kh[r] * gam;
+    } else {
+        const int t = tid - kD;
+        if (t < 16) {
+            const Rsrc rb = make_rsrc(beta + cp.brow0, L > 0 ? (uint32_t)(((L - 1) * cp.bstride + 1) * 4) : 0u);
+            F.beta[t] = __builtin_bit_cast(float, buf_load<uint32_t>(rb, t * cp.bstride * 4));
+        }
+        if constexpr (RAW) {
+            // dO rows: 128 threads x 16 elements
+            const Rsrc rd = chunk_rsrc<kD>(dO, cp, 2);
+            const int r = t >> 3, c0 = (t & 7) * 16;
+            const u32x4 a = buf_load<u32x4>(rd, r * rowb + c0 * 2);
+            const u32x4 bq = buf_load<u32x4>(rd, r * rowb + (c0 + 8) * 2);
+            *reinterpret_cast<u32x4*>(&raw->dO[r][c0]) = a;
+            *reinterpret_cast<u32x4*>(&raw->dO[r][c0 + 8]) = bq;
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        // P = Kt Kh^T and Qt Kh^T (K = 128), then Ninv by forward substitution
+        const int i = tid & 15, g = tid >> 4;
+        f32x4 p = zero4(), a = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const B8 kh = ld8s(&F.Kh[i][32 * s + 8 * g]);
+            p = mma3(ld8s(&F.Kt[i][32 * s + 8 * g]), kh, p);
+            a = mma3(ld8s(&F.Qt[i][32 * s + 8 * g]), kh, a);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;   // row r, column i
+            F.P[r][i] = p[e];
+            F.Aqk[r][i] = r >= i ? a[e] : 0.f;
+            F.Akk[r][i] = r > i ? F.beta[r] * p[e] : 0.f;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (tid < 16) {
+            const int j = tid;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+                for (int c = 0; c < r; ++c) acc -= F.Akk[r][c] * x[c];
+                x[r] = acc;
+                F.Ninv[r][j] = acc;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ kernels
+
+// Chain operands of every chunk: block (u, n) at fac + (u * NC + n) * 13824.
+__global__ __launch_bounds__(256) void bwd_fac_kernel(const bf16* __restrict__ q,
+                                                      const bf16* __restrict__ k,
+                                                      const bf16* __restrict__ z,
+                                                      const float* __restrict__ beta,
+                                                      const float* __restrict__ A, float g_min,
+                                                      char* __restrict__ fac, int B, int T,
+                                                      int H) {
+    __shared__ Fac F;
+    const int NC = (T + kChunk - 1) / kChunk;
+    const size_t id = blockIdx.x;
+    const int n = (int)(id % NC);
+    const size_t u = id / NC;
+    const int b = (int)(u / H), h = (int)(u % H);
+    bwd_factors<false>(F, nullptr, q, k, z, beta, nullptr, make_gate(A[h], g_min), b, h, n, T, H);
+    char* out = fac + id * (size_t)CBlk::BYTES;
+    const int tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    if (w == 0) {
+        // Kd in the A-row order of the chain's Kd dS product: slot s, lane
+        // (i, g), element e <-> key channel 32 s + 16 (e / 4) + 4 g + e % 4,
+        // which pairs with dS in its accumulator layout
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(&F.Kd[i][32 * s + 4 * g]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(&F.Kd[i][32 * s + 16 + 4 * g]);
+            *reinterpret_cast<bf16x8*>(out + CBlk::KD + s * 1024 + lane * 16) = pack8(lo, hi);
+        }
+    } else if (w <= 2) {
+        // tile m of [Qt^T | -Kt^T]: lane (i, g) holds Qt[4g + e][16m + i] and
+        // -Kt[4g + e][16m + i], e = 0..3
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            const int m = 4 * (w - 1) + mm;
+            bf16x8 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = (bf16)F.Qt[4 * g + e][16 * m + i];
+                x[4 + e] = (bf16)(-F.Kt[4 * g + e][16 * m + i]);
+            }
+            *reinterpret_cast<bf16x8*>(out + CBlk::QK + m * 1024 + lane * 16) = x;
+        }
+    } else {
+        // Aqk^T and Tm^T = (Ninv Diag(beta))^T as K = 16 A operands: lane
+        // (i, g) holds row i, columns 4g .. 4g + 3
+        bf16x4 aq, tm;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            aq[e] = (bf16)F.Aqk[4 * g + e][i];
+            tm[e] = (bf16)(F.Ninv[4 * g + e][i] * F.beta[i]);
+        }
+        *reinterpret_cast<bf16x4*>(out + CBlk::AQT + lane * 8) = aq;
+        *reinterpret_cast<bf16x4*>(out + CBlk::TMT + lane * 8) = tm;
+        reinterpret_cast<float*>(out + CBlk::GAM)[lane] = F.gam[lane];
+        reinterpret_cast<float*>(out + CBlk::GAM)[64 + lane] = F.gam[64 + lane];
+    }
+}
+
+// The state-gradient chain: one wave per (b, h, 16 value columns), chunks
+// last to first.  dSend[(u NC + n)][k][j] receives the gradient of chunk n's
+// end state (natural [D][D] layout); dS0 (if given) the gradient of S0.  The
+// next chunk's operands load while a chunk computes.
+__global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__ fac,
+                                                        const bf16* __restrict__ dO,
+                                                        const float* __restrict__ dST,
+                                                        float* __restrict__ dSend,
+                                                        float* __restrict__ dS0, int B, int T,
+                                                        int H) {
+    constexpr int NCB = kD / 16;
+    const int NC = (T + kChunk - 1) / kChunk;
+    // (b, h) of a workgroup id: the 8 column blocks of a head share an XCD
+    int u, jb;
+    if (!map_unit(NCB, B * H, u, jb)) return;
+    const int b = u / H, h = u % H;
+    const int lane = lane_id(), i = lane & 15, g = lane >> 4;
+    const int j0 = 16 * jb;
+    struct Ops {
+        bf16x8 kd[4], qk[8];
+        bf16x4 aqt, tmt;
+        f32x4 gam[8];
+        u32x4 dO;
+    };
+    auto load = [&](Ops& o, int n) {
+        const Rsrc rf = make_rsrc(fac + ((size_t)u * NC + n) * CBlk::BYTES, CBlk::BYTES);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            o.kd[s] = __builtin_bit_cast(bf16x8, buf_load<u32x4>(rf, CBlk::KD + s * 1024 + lane * 16));
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            o.qk[m] = __builtin_bit_cast(bf16x8, buf_load<u32x4>(rf, CBlk::QK + m * 1024 + lane * 16));
+        o.aqt = __builtin_bit_cast(bf16x4, buf_load<u32x2>(rf, CBlk::AQT + lane * 8));
+        o.tmt = __builtin_bit_cast(bf16x4, buf_load<u32x2>(rf, CBlk::TMT + lane * 8));
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            o.gam[m] = __builtin_bit_cast(f32x4, buf_load<u32x4>(rf, CBlk::GAM + (16 * m + 4 * g) * 4));
+        // dO rows 4g .. 4g+3 of column j0 + i (rows past T read 0)
+        const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
+        const Rsrc rd = chunk_rsrc<kD>(dO, cp, 2);
+        const int rowb = (int)(cp.rstride * 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o.dO[e] = buf_load<unsigned short>(rd, (4 * g + e) * rowb + (j0 + i) * 2);
+    };
+    // dS in the accumulator layout: lane (i, g) holds rows 16m + 4g + e of column j0 + i
+    f32x4 dS[8];
+    const float* st = dST ? dST + (size_t)u * kD * kD : nullptr;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dS[m][e] = st ? st[(size_t)(16 * m + 4 * g + e) * kD + j0 + i] : 0.f;
+    Ops cur, nxt;
+    load(cur, NC - 1);
+    for (int n = NC - 1; n >= 0; --n) {
+        if (n > 0) load(nxt, n - 1);
+        // the gradient of this chunk's end state, for the gradient kernel
+        float* out = dSend + ((size_t)u * NC + n) * kD * kD + j0 + i;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(size_t)(16 * m + 4 * g + e) * kD] = dS[m][e];
+        // dU = Kd dS + Aqk^T dO (separate accumulators: no 16x16x32 result
+        // feeds a 16x16x16 MFMA as its accumulator input)
+        f32x4 x = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x = mma_bf16_k32(cur.kd[s], pack8(dS[2 * s], dS[2 * s + 1]), x);
+        const f32x4 dOf = __builtin_bit_cast(f32x4, cur.dO << 16);
+        const bf16x4 dOb = pack4(dOf);
+        const f32x4 y = mma_bf16_k16(cur.aqt, dOb, zero4());
+        const f32x4 dU = x + y;
+        const f32x4 dW = mma_bf16_k16(cur.tmt, pack4(dU), zero4());
+        // dS <- Diag(gam) dS + [Qt^T | -Kt^T] [dO; dW]
+        const bf16x4 dWb = pack4(dW);
+        bf16x8 b2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            b2[e] = dOb[e];
+            b2[4 + e] = dWb[e];
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dS[m] = mma_bf16_k32(cur.qk[m], b2, dS[m] * cur.gam[m]);
+        if (n > 0) cur = nxt;
+    }
+    if (dS0) {
+        float* out = dS0 + (size_t)u * kD * kD + j0 + i;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(size_t)(16 * m + 4 * g + e) * kD] = dS[m][e];
+    }
+}
+
+namespace {
+
+// Scratch of the gradient kernel: the 16 x 128 products of the value side and
+// the 16 x 16 gradients of the triangular algebra.
+struct GradLds {
+    Fac F;
+    Raw R;
+    float W[16][kRF], U[16][kRF], dU[16][kRF], dW[16][kRF];
+    float dAqk[16][16], dTm[16][16], dP[16][16], T1[16][16];
+    float db1[4][16], db2[16];
+    float dAred[4];
+};
+
+}  // namespace
+
+// Every gradient of chunk n of (b, h), from the chunk's start state (ckpt, the
+// layout of bwd_ckpt_kernel: 8-column slices) and the gradient of its end
+// state (dSend).  One workgroup of four waves; wave w owns value columns and
+// key channels 32w .. 32w + 31.
+__global__ __launch_bounds__(256) void bwd_grad_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
+    float g_min, const bf16* __restrict__ dO, const float* __restrict__ ckpt,
+    const float* __restrict__ dSend, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    bf16* __restrict__ dv, bf16* __restrict__ dz, float* __restrict__ dbeta,
+    float* __restrict__ dA_part, int B, int T, int H) {
+    constexpr int NCB8 = kD / 8;   // 8-column slices of a checkpoint
+    __shared__ GradLds sm;
+    Fac& F = sm.F;
+    const int NC = (T + kChunk - 1) / kChunk;
+    const size_t id = blockIdx.x;
+    const int n = (int)(id % NC);
+    const size_t u = id / NC;
+    const int b = (int)(u / H), h = (int)(u % H);
+    const GateConsts gc = make_gate(A[h], g_min);
+    bwd_factors<true>(F, &sm.R, q, k, z, beta, dO, gc, b, h, n, T, H);
+    const int tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
+    const int L = cp.L;
+    const int rowb = (int)(cp.rstride * 2);
+    // start state slice (u, cb) of chunk n: D rows of 8 columns
+    auto ck = [&](int cb) { return ckpt + ((u * NCB8 + cb) * NC + n) * (size_t)(kD * 8); };
+    const float* dse = dSend + (u * NC + n) * (size_t)kD * kD;
+
+    // ---- value side, two 16-column blocks per wave
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j0 = 32 * w + 16 * jj, jc = j0 + i;
+        // B operands of the products over key channels: S and dS columns,
+        // lane (i, g), step s: rows 32 s + 8 g + e
+        B8 sB[4], dsB[4];
+        {
+            const float* sc = ck(jc >> 3) + (jc & 7);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                f32x4 lo, hi, dlo, dhi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo[e] = sc[(32 * s + 8 * g + e) * 8];
+                    hi[e] = sc[(32 * s + 8 * g + 4 + e) * 8];
+                    dlo[e] = dse[(size_t)(32 * s + 8 * g + e) * kD + jc];
+                    dhi[e] = dse[(size_t)(32 * s + 8 * g + 4 + e) * kD + jc];
+                }
+                sB[s] = split8(lo, hi);
+                dsB[s] = split8(dlo, dhi);
+            }
+        }
+        f32x4 X = zero4(), Y = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            X = mma3(ld8s(&F.Kt[i][32 * s + 8 * g]), sB[s], X);   // Kt S
+            Y = mma3(ld8s(&F.Kd[i][32 * s + 8 * g]), dsB[s], Y);  // Kd dS
+        }
+        // V and dO in the accumulator layout (rows 4g + e, column jc)
+        const Rsrc rv = chunk_rsrc<kD>(v, cp, 2);
+        f32x4 Vf, dOf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Vf[e] = bf16_bits_to_f32(buf_load<unsigned short>(rv, (4 * g + e) * rowb + jc * 2));
+            dOf[e] = bf2f(sm.R.dO[4 * g + e][jc]);
+        }
+        // Tm = Ninv Diag(beta) and its transpose, Aqk^T, as K = 16 A operands
+        f32x4 tmf, tmtf, aqtf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tmf[e] = F.Ninv[i][4 * g + e] * F.beta[4 * g + e];
+            tmtf[e] = F.Ninv[4 * g + e][i] * F.beta[i];
+            aqtf[e] = F.Aqk[4 * g + e][i];
+        }
+        const B4 tm = split4(tmf), tmt = split4(tmtf), aqt = split4(aqtf);
+        const f32x4 Wv = Vf - X;
+        const f32x4 Uv = mma3(tm, split4(Wv), zero4());
+        const B4 dOs = {pack4(dOf), pack4(zero4())};   // dO is bf16 already
+        const f32x4 dUv = Y + mma3(aqt, dOs, zero4());
+        const f32x4 dWv = mma3(tmt, split4(dUv), zero4());
+        // dv = dW (rows past the chunk's end are dropped)
+        const Rsrc rdv = chunk_rsrc<kD>(dv, cp, 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            buf_store_u16(rdv, r * rowb + jc * 2, __builtin_bit_cast(unsigned short, (bf16)dWv[e]));
+            sm.W[r][jc] = Wv[e];
+            sm.U[r][jc] = Uv[e];
+            sm.dU[r][jc] = dUv[e];
+            sm.dW[r][jc] = dWv[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- dAqk = tril_0(dO U^T) (wave 0) and dTm = dU W^T (wave 1), K = 128
+    if (w < 2) {
+        f32x4 c = zero4();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (w == 0)
+                c = mma2(ld8(&sm.R.dO[i][32 * t + 8 * g]), ld8s(&sm.U[i][32 * t + 8 * g]), c);
+            else
+                c = mma3(ld8s(&sm.dU[i][32 * t + 8 * g]), ld8s(&sm.W[i][32 * t + 8 * g]), c);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            if (w == 0) sm.dAqk[r][i] = r >= i ? c[e] : 0.f;
+            else sm.dTm[r][i] = c[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- the triangular algebra (wave 0, fp32): lane (j = i, rows 4g .. 4g+3)
+    if (w == 0) {
+        const int j = i;
+        float db1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            db1 += sm.dTm[r][j] * F.Ninv[r][j];
+            // T1 = dN Ninv^T with dN = dTm Diag(beta)
+            float t1 = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) t1 += sm.dTm[r][s] * F.beta[s] * F.Ninv[j][s];
+            sm.T1[r][j] = t1;
+        }
+        sm.db1[g][j] = db1;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            // dM = -Ninv^T T1; dA = tril_{-1}(dM); dP = Diag(beta) dA
+            float dm = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) dm -= F.Ninv[s][r] * sm.T1[s][j];
+            const float da = r > j ? dm : 0.f;
+            sm.dP[r][j] = F.beta[r] * da;
+            // dbeta_r += sum_j dA[r][j] P[r][j]: reduce over the 16 lanes of the row group
+            float t = da * F.P[r][j];
+            t += __shfl_xor(t, 1);
+            t += __shfl_xor(t, 2);
+            t += __shfl_xor(t, 4);
+            t += __shfl_xor(t, 8);
+            if (j == 0) sm.db2[r] = t;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < 16 && lane < L) {
+            const float dbv = sm.db1[0][lane] + sm.db1[1][lane] + sm.db1[2][lane] + sm.db1[3][lane] +
+                              sm.db2[lane];
+            dbeta[cp.brow0 + (size_t)lane * cp.bstride] = dbv;
+        }
+    }
+    __syncthreads();
+
+    // ---- key side, two 16-channel blocks per wave
+    float dA_acc = 0.f;
+    const float eA = __expf(A[h]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int k0 = 32 * w + 16 * kk, kc = k0 + i;
+        f32x4 cQ = zero4(), cK = zero4(), cD = zero4();
+        float dgam = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            // S and dS rows kc, value columns 32 t + 8 g .. + 7 (fp32)
+            const float* sr = ck(4 * t + g) + (size_t)kc * 8;
+            const float* dr = dse + (size_t)kc * kD + 32 * t + 8 * g;
+            const f32x4 s_lo = *reinterpret_cast<const f32x4*>(sr);
+            const f32x4 s_hi = *reinterpret_cast<const f32x4*>(sr + 4);
+            const f32x4 d_lo = *reinterpret_cast<const f32x4*>(dr);
+            const f32x4 d_hi = *reinterpret_cast<const f32x4*>(dr + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dgam += s_lo[e] * d_lo[e] + s_hi[e] * d_hi[e];
+            const B8 sb = split8(s_lo, s_hi), db = split8(d_lo, d_hi);
+            cQ = mma2(ld8(&sm.R.dO[i][32 * t + 8 * g]), sb, cQ);    // dO S^T
+            cK = mma3(ld8s(&sm.dW[i][32 * t + 8 * g]), sb, cK);     // dW S^T
+            cD = mma3(ld8s(&sm.U[i][32 * t + 8 * g]), db, cD);      // U dS^T
+        }
+        dgam += __shfl_xor(dgam, 16);
+        dgam += __shfl_xor(dgam, 32);
+        // K = 16 products with Kh, Qt, Kt tiles of channels k0 .. k0+15 as B
+        f32x4 khf, qtf, ktf, dAqf, dAqTf, dPf, dPTf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            khf[e] = F.Kh[4 * g + e][kc];
+            qtf[e] = F.Qt[4 * g + e][kc];
+            ktf[e] = F.Kt[4 * g + e][kc];
+            dAqf[e] = sm.dAqk[i][4 * g + e];
+            dAqTf[e] = sm.dAqk[4 * g + e][i];
+            dPf[e] = sm.dP[i][4 * g + e];
+            dPTf[e] = sm.dP[4 * g + e][i];
+        }
+        const B4 khB = split4(khf), qtB = split4(qtf), ktB = split4(ktf);
+        const f32x4 dQt = cQ + mma3(split4(dAqf), khB, zero4());
+        const f32x4 dKt = mma3(split4(dPf), khB, zero4()) - cK;
+        const f32x4 dKh = mma3(split4(dPTf), ktB, mma3(split4(dAqTf), qtB, zero4()));
+        const f32x4 dKd = cD;
+        // finals: lane (i, g) holds rows 4g + e of channel kc
+        const float gam = F.gam[kc];
+        float dG[4], dkv[4], dqv[4], cs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float ex = fast_exp2(F.G[r][kc] * kLog2e), rex = fast_rcp(ex);
+            const float kv = bf2f(sm.R.k[r][kc]), qv = bf2f(sm.R.q[r][kc]);
+            const float kdv = kv * gam * rex;          // Kd
+            dkv[e] = dKt[e] * ex + dKh[e] * rex + dKd[e] * gam * rex;
+            dqv[e] = dQt[e] * ex;
+            dG[e] = dKt[e] * kv * ex - dKh[e] * kv * rex + dQt[e] * qv * ex - dKd[e] * kdv;
+            cs += dKd[e] * kdv;
+        }
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+        // dg_r = sum of dG over rows r .. 15, plus the last row's extra terms
+        float suf[4];
+        suf[3] = dG[3];
+        suf[2] = dG[2] + suf[3];
+        suf[1] = dG[1] + suf[2];
+        suf[0] = dG[0] + suf[1];
+        const float t1 = __shfl(suf[0], 16 + i), t2 = __shfl(suf[0], 32 + i),
+                    t3 = __shfl(suf[0], 48 + i);
+        const float after = (g < 1 ? t1 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 3 ? t3 : 0.f);
+        const float extra = cs + dgam * gam;
+        const Rsrc rdq = chunk_rsrc<kD>(dq, cp, 2), rdk = chunk_rsrc<kD>(dk, cp, 2),
+                   rdz = chunk_rsrc<kD>(dz, cp, 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float dg = suf[e] + after + extra;
+            const float zv = bf2f(sm.R.z[r][kc]);
+            const float s = gate_sigmoid(gc, zv);
+            const float dx = r < L ? dg * gc.gmin * s * (1.f - s) : 0.f;
+            dA_acc += dx * eA * zv;
+            const int off = r * rowb + kc * 2;
+            buf_store_u16(rdq, off, __builtin_bit_cast(unsigned short, (bf16)dqv[e]));
+            buf_store_u16(rdk, off, __builtin_bit_cast(unsigned short, (bf16)dkv[e]));
+            buf_store_u16(rdz, off, __builtin_bit_cast(unsigned short, (bf16)(dx * eA)));
+        }
+    }
+    // the chunk's dA term: wave sums, then the four waves in order
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) dA_acc += __shfl_xor(dA_acc, x);
+    if (lane == 0) sm.dAred[w] = dA_acc;
+    __syncthreads();
+    if (tid == 0) dA_part[id] = ((sm.dAred[0] + sm.dAred[1]) + sm.dAred[2]) + sm.dAred[3];
+}
+
+// ------------------------------------------------------------------ host
+
+bool bwd_chunk_ok(int d, bool is_bf16) { return d == kD && is_bf16; }
+
+size_t bwd_chunk_fac_bytes() { return CBlk::BYTES; }
+
+hipError_t launch_bwd_chunk(const BackwardArgs& a, const float* ckpt, char* fac, float* dSend,
+                            float* dA_part, hipStream_t stream) {
+    const int NC = (a.T + kChunk - 1) / kChunk;
+    const size_t units = (size_t)a.B * a.H;
+    const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v,
+               *z = (const bf16*)a.z, *dO = (const bf16*)a.dO;
+    hipLaunchKernelGGL(bwd_fac_kernel, dim3((unsigned)(units * NC)), dim3(256), 0, stream, q, k, z,
+                       a.beta, a.A, a.g_min, fac, a.B, a.T, a.H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned chains = (unsigned)(((units + 7) / 8) * 8 * (kD / 16));
+    hipLaunchKernelGGL(bwd_dchain_kernel, dim3(chains), dim3(64), 0, stream, fac, dO, a.dST, dSend,
+                       a.dS0, a.B, a.T, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(units * NC)), dim3(256), 0, stream, q, k, v,
+                       z, a.beta, a.A, a.g_min, dO, ckpt, dSend, (bf16*)a.dq, (bf16*)a.dk,
+                       (bf16*)a.dv, (bf16*)a.dz, a.dbeta, dA_part, a.B, a.T, a.H);
+    return hipGetLastError();
+}
+
+}  // namespace kda

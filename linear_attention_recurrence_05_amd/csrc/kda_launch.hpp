@@ -105,15 +105,26 @@ constexpr int kBwdSegMin = 256;
 
 // Byte offsets of the backward workspace regions (each 256-byte aligned).
 struct BwdLayout {
-    size_t ckpt, carry, ucor, pq, pk, pg, pb, dA_part, segws, oscr, Gc, Tm, Aqk, gam, dSend, total;
+    size_t ckpt, carry, ucor, pq, pk, pg, pb, dA_part, segws, oscr, Gc, Tm, Aqk, gam, dSend, fac,
+        total;
     int R;       // segments of the forward sweep run side by side (1: one sweep)
     bool chain;  // reverse sweep by the chunk-level chain, chunks in parallel
+    bool chunk;  // the chunkwise MFMA plan (kda_bwd_chunk.hip)
     int seg;     // tokens per reverse-sweep launch (multiple of kBwdTokBlock)
     int NC;      // chunks (checkpoints) per sequence
     int ntb;     // finalize token blocks per sequence
 };
 BwdLayout bwd_layout(int B, int T, int H, int d, bool is_bf16);
 bool bwd_plan_chain(int T);
+bool bwd_plan_chunk(int d, bool is_bf16);
+// The chunkwise MFMA backward (bf16, d = 128): whether it applies, the bytes
+// of one chunk's chain operand block, and its launches after the forward
+// checkpoints (ckpt: bwd_ckpt_kernel's layout); fac, dSend and dA_part are
+// workspace regions of units * NC blocks, states and floats.
+bool bwd_chunk_ok(int d, bool is_bf16);
+size_t bwd_chunk_fac_bytes();
+hipError_t launch_bwd_chunk(const BackwardArgs& a, const float* ckpt, char* fac, float* dSend,
+                            float* dA_part, hipStream_t stream);
 
 // How a prefill is executed.
 enum class Plan {

@@ -60,7 +60,7 @@ def test_scanner_flags_a_planted_chain():
     assert mixed_shape_chains(same) == []
 
 
-@pytest.mark.parametrize("source", ["kda_prefill.hip", "kda_pair.hip"])
+@pytest.mark.parametrize("source", ["kda_prefill.hip", "kda_pair.hip", "kda_bwd_chunk.hip"])
 def test_prefill_kernels_have_no_mixed_shape_srcc_chain(tmp_path, source):
     cmd = kbuild.hipcc_command(str(tmp_path / "unused.so"))
     # same flags, device-only assembly of one prefill translation unit
