@@ -437,24 +437,36 @@ def test_backward_workspace_query():
     n = kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_BF16)
     # at least the chunk-start states: 32 heads x 256 chunks x 128 x 128 fp32
     assert n >= 32 * 256 * 128 * 128 * 4
-    # the partial sums stay bounded as T grows (segments); the chunk-start
-    # states and the per-token corrections grow with T
+    # the chunkwise plan (bf16, d = 128): per extra chunk of every head, a
+    # start state, an end-state gradient, the chain's operand block and a
+    # dA term; the segment scan behind the segment-parallel forward sweep
+    # runs state-only passes here (no zero v, no scratch o)
     n2 = kda.kda_chunk_backward_workspace_bytes(1, 8192, 32, 128, 128, kda.KDA_BF16)
-    # chunk-start states + corrections u for the 4096 extra tokens (256
-    # chunks) of 32 heads; the segment scan behind the segment-parallel
-    # forward sweep runs state-only passes here (no zero v, no scratch o)
-    extra = 32 * 256 * 128 * 128 * 4 + 32 * 4096 * 128 * 4
+    extra = 32 * 256 * (2 * 128 * 128 * 4 + 13824 + 4)
     assert extra <= n2 - n <= extra + (1 << 20)
+    # the token-level sweep (forced) holds the per-token corrections and
+    # bounded partial sums instead
+    os.environ["KDA_BACKWARD_PLAN"] = "sweep"
+    try:
+        ns = kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_BF16)
+        ns2 = kda.kda_chunk_backward_workspace_bytes(1, 8192, 32, 128, 128, kda.KDA_BF16)
+        nc = kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_F32)
+    finally:
+        del os.environ["KDA_BACKWARD_PLAN"]
+    extra = 32 * 256 * 128 * 128 * 4 + 32 * 4096 * 128 * 4
+    assert extra <= ns2 - ns <= extra + (1 << 20)
+    # fp32 takes the token-level sweep without any setting
+    assert kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_F32) == nc
     # the chain plan adds the cumulative log-decay, Tm, Aqk, gamma and the
-    # end-state gradient of every chunk
+    # end-state gradient of every chunk to the sweep's
     os.environ["KDA_BACKWARD_PLAN"] = "chain"
     try:
-        nc = kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_BF16)
+        nch = kda.kda_chunk_backward_workspace_bytes(1, 4096, 32, 128, 128, kda.KDA_BF16)
     finally:
         del os.environ["KDA_BACKWARD_PLAN"]
     chain = (32 * 4096 * 128 * 4 + 2 * 32 * 256 * 256 * 4 + 32 * 256 * 128 * 4
              + 32 * 256 * 128 * 128 * 4)
-    assert chain <= nc - n <= chain + (1 << 20)
+    assert chain <= nch - ns <= chain + (1 << 20)
     assert kda.kda_chunk_backward_workspace_bytes(0, 64, 2, 32, 32, kda.KDA_F32) == 0
     assert kda.kda_chunk_backward_workspace_bytes(1, 64, 2, 64, 64, kda.KDA_F32) == 0
 
