@@ -854,11 +854,13 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
         if ((e = seg_start_states(fa, L.R, SL, ws + L.segws, stream)) != hipSuccess) return e;
         Sseg = (const float*)(ws + L.segws + SL.Sin);
     }
-    hipLaunchKernelGGL((bwd_ckpt_kernel<E, D>), dim3((unsigned)(units * L.R * G::NCB)), block, 0,
-                       stream, k, v, z, a.beta, a.A, a.g_min, a.S0, Sseg, L.R, ckpt,
-                       L.chunk ? nullptr : ucor, a.B, a.T, a.H);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (L.chunk) {
+        // chunk-start states by a chunkwise state-only pass, the R segments
+        // side by side from their scanned start states
+        const PrefillArgs ca{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min,
+                             dense_state(L.R > 1 ? Sseg : a.S0, nullptr), nullptr, a.B * L.R,
+                             a.T / L.R, a.H, D, true};
+        if ((e = launch_ckpt_pass(ca, CkOut{ckpt, L.R, L.NC}, stream)) != hipSuccess) return e;
         if ((e = launch_bwd_chunk(a, ckpt, ws + L.fac, (float*)(ws + L.dSend), dA_part, stream)) !=
             hipSuccess)
             return e;
@@ -866,6 +868,10 @@ static hipError_t launch_backward_t(const BackwardArgs& a, char* ws, hipStream_t
                            L.NC);
         return hipGetLastError();
     }
+    hipLaunchKernelGGL((bwd_ckpt_kernel<E, D>), dim3((unsigned)(units * L.R * G::NCB)), block, 0,
+                       stream, k, v, z, a.beta, a.A, a.g_min, a.S0, Sseg, L.R, ckpt, ucor, a.B,
+                       a.T, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const float* dSend = nullptr;
     if (L.chain) {
         // chunk factors (the intra-chunk stage's exports) and the chain

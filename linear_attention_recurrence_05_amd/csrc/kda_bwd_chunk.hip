@@ -22,8 +22,8 @@
 //         row sum_r dKd o Kd + dgam o gam;  dg = reverse cumsum of dG
 // and through the gate dz = dg g_min s (1 - s) e^{A_h}, dA_h += dg g_min s (1 - s) x.
 //
-// Launches (after the forward checkpoints S at every chunk start, which
-// kda_backward.hip's bwd_ckpt_kernel writes):
+// Launches (after the forward checkpoints S at every chunk start, natural
+// [D][D] layout, which a state-only fused prefill pass writes):
 //   bwd_fac_kernel    one workgroup per (b, h, chunk): the chunk's factors,
 //                     written as the chain's MFMA operands (13,824 bytes).
 //   bwd_dchain_kernel one wave per (b, h, 16 value columns): dS from dS_T back
@@ -404,9 +404,8 @@ struct GradLds {
 
 }  // namespace
 
-// Every gradient of chunk n of (b, h), from the chunk's start state (ckpt, the
-// layout of bwd_ckpt_kernel: 8-column slices) and the gradient of its end
-// state (dSend).  One workgroup of four waves; wave w owns value columns and
+// Every gradient of chunk n of (b, h), from the chunk's start state (ckpt)
+// and the gradient of its end state (dSend), both [D][D] per (b, h, chunk).  One workgroup of four waves; wave w owns value columns and
 // key channels 32w .. 32w + 31.
 __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -415,7 +414,6 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const float* __restrict__ dSend, bf16* __restrict__ dq, bf16* __restrict__ dk,
     bf16* __restrict__ dv, bf16* __restrict__ dz, float* __restrict__ dbeta,
     float* __restrict__ dA_part, int B, int T, int H) {
-    constexpr int NCB8 = kD / 8;   // 8-column slices of a checkpoint
     __shared__ GradLds sm;
     Fac& F = sm.F;
     const int NC = (T + kChunk - 1) / kChunk;
@@ -429,8 +427,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
     const int L = cp.L;
     const int rowb = (int)(cp.rstride * 2);
-    // start state slice (u, cb) of chunk n: D rows of 8 columns
-    auto ck = [&](int cb) { return ckpt + ((u * NCB8 + cb) * NC + n) * (size_t)(kD * 8); };
+    const float* sst = ckpt + (u * NC + n) * (size_t)kD * kD;
     const float* dse = dSend + (u * NC + n) * (size_t)kD * kD;
 
     // ---- value side, two 16-column blocks per wave
@@ -441,14 +438,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         // lane (i, g), step s: rows 32 s + 8 g + e
         B8 sB[4], dsB[4];
         {
-            const float* sc = ck(jc >> 3) + (jc & 7);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 f32x4 lo, hi, dlo, dhi;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    lo[e] = sc[(32 * s + 8 * g + e) * 8];
-                    hi[e] = sc[(32 * s + 8 * g + 4 + e) * 8];
+                    lo[e] = sst[(size_t)(32 * s + 8 * g + e) * kD + jc];
+                    hi[e] = sst[(size_t)(32 * s + 8 * g + 4 + e) * kD + jc];
                     dlo[e] = dse[(size_t)(32 * s + 8 * g + e) * kD + jc];
                     dhi[e] = dse[(size_t)(32 * s + 8 * g + 4 + e) * kD + jc];
                 }
@@ -574,7 +570,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             // S and dS rows kc, value columns 32 t + 8 g .. + 7 (fp32)
-            const float* sr = ck(4 * t + g) + (size_t)kc * 8;
+            const float* sr = sst + (size_t)kc * kD + 32 * t + 8 * g;
             const float* dr = dse + (size_t)kc * kD + 32 * t + 8 * g;
             const f32x4 s_lo = *reinterpret_cast<const f32x4*>(sr);
             const f32x4 s_hi = *reinterpret_cast<const f32x4*>(sr + 4);

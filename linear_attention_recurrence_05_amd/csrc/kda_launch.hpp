@@ -43,6 +43,21 @@ inline StateIO dense_state(const float* in, float* out) {
     return StateIO{in, nullptr, out, nullptr, nullptr, nullptr, 0};
 }
 
+// Where a checkpointing pass stores the state entering every chunk: for the
+// pass's row b' (= b R + r: segment r of sequence b when R segments run side
+// by side) and head h, chunk n' of the row is chunk r NCs + n' of the
+// sequence, whose state goes to base + ((b H + h) NC + r NCs + n') D D in
+// the natural [D][D] layout; NC = R NCs chunks per sequence.
+struct CkOut {
+    float* base;
+    int R, NC;
+    template <int D>
+    __device__ float* at(int bp, int h, int n, int H) const {
+        const int b = bp / R, r = bp % R;
+        return base + (((size_t)b * H + h) * NC + (size_t)r * (NC / R) + n) * (size_t)D * D;
+    }
+};
+
 struct DecodeArgs {
     const void *q, *k, *v, *z;
     const float *beta, *A;
@@ -150,6 +165,10 @@ PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16);
 // Whether launch_prefill runs this plan as a state-only pass: a null o (no
 // outputs; q is not read) and optionally a null v (v taken as zero).
 bool prefill_state_only_ok(const PlanInfo& p, int d);
+// A state-only pass of the fused kernel (bf16, d = 128, 128 columns per
+// workgroup) over a.B rows of a.T tokens from a.S.in that stores the state
+// entering every chunk into ck (a.o, a.v unused beyond v's reads).
+hipError_t launch_ckpt_pass(const PrefillArgs& a, const CkOut& ck, hipStream_t stream);
 // Bytes of one two-chunk factor block of the split plan.
 size_t pair_block_bytes(int d, bool is_bf16);
 // Whether the split plan compiles an inter kernel with ncol value columns per

@@ -113,14 +113,16 @@ struct FusedCfg {
 // while the consumers run the state chain over half m&1.  Each role runs its
 // own loop (so neither keeps the other's registers live); both execute
 // 1 + NM barriers.  WQ = false: only the end state (q and o are not
-// touched); VZ: v is taken as zero (v is not read).
-template <typename E, int D, int NB, int NCW, bool WQ = true, bool VZ = false>
+// touched); VZ: v is taken as zero (v is not read); CK: the state at the
+// start of every chunk is stored too (ck, the checkpoints of a backward).
+template <typename E, int D, int NB, int NCW, bool WQ = true, bool VZ = false, bool CK = false>
 __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ v, const E* __restrict__ z,
                                                     const float* __restrict__ beta,
                                                     const float* __restrict__ A, float g_min,
                                                     StateIO io, E* __restrict__ o,
-                                                    int B, int T, int H, int nct) {
+                                                    int B, int T, int H, int nct,
+                                                    CkOut ck = CkOut{}) {
     using Bk = Blk<E, D>;
     using Cfg = FusedCfg<E, D>;
     constexpr int NPROD = Cfg::NPROD;
@@ -198,6 +200,19 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
                 f32x4 Vf[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) Vf[nb] = VZ ? zero4() : v_widen<E>(Vc[cc][nb]);
+                if constexpr (CK) {
+                    // the state entering chunk n, natural [D][D] layout
+                    float* cp = ck.at<D>(b, h, n, H);
+                    const int lane = lane_id(), j = lane & 15, g = lane >> 4;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+                            for (int p = 0; p < 4; ++p)
+                                cp[(size_t)(16 * mm + 4 * g + p) * D + col0 + 16 * nb + j] =
+                                    S[nb][mm][p];
+                }
                 chunk_step<E, D, NB, WQ>(c, S, Vf, O);
                 if constexpr (WQ) o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n, T, H), col0);
             }
@@ -338,6 +353,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PlanInfo& p, void
     }
     (void)ws;
     return hipErrorInvalidValue;   // the split plan runs through launch_split
+}
+
+hipError_t launch_ckpt_pass(const PrefillArgs& a, const CkOut& ck, hipStream_t stream) {
+    if (!a.is_bf16 || a.d != 128) return hipErrorInvalidValue;
+    const int units = a.B * a.H;
+    hipLaunchKernelGGL((fused_kernel<bf16, 128, 2, 4, false, false, true>),
+                       dim3(grid_units(units, 1)), dim3(512), 0, stream, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.z, a.beta, a.A, a.g_min,
+                       a.S, (bf16*)nullptr, a.B, a.T, a.H, 1, ck);
+    return hipGetLastError();
 }
 
 bool prefill_state_only_ok(const PlanInfo& p, int d) {
