@@ -70,14 +70,13 @@ struct Fac {
     float beta[16];                        // 0 on padded rows
     float P[16][16];                       // Kt Kh^T
     float Aqk[16][16];                     // tril_0(Qt Kh^T)
-    float Akk[16][16];                     // tril_{-1}(Diag(beta) P)
-    float Ninv[16][16];                    // (I + Akk)^{-1}
-    float Kt[16][kRF], Kh[16][kRF], Qt[16][kRF], Kd[16][kRF];
+    float Ninv[16][16];                    // (I + Akk)^{-1}, Akk = tril_{-1}(Diag(beta) P)
+    float Kt[16][kRF], Kh[16][kRF], Qt[16][kRF];   // (Kd = Kh Diag(gam))
 };
 
-// The chunk's raw rows (the finals need k, q, z in fp32) and dO.
+// The chunk's raw gate inputs z (the finals need the gate's derivative).
 struct Raw {
-    bf16 k[16][kRS], q[16][kRS], z[16][kRS], dO[16][kRS];
+    bf16 z[16][kRS];
 };
 
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
@@ -134,15 +133,18 @@ __device__ __forceinline__ f32x4 mma3(const B4& a, const B4& b, f32x4 acc) {
     return mma_bf16_k16(a.lo, b.hi, acc);
 }
 
-// Factors of chunk n of (b, h) into F (and, with raw, the raw rows and dO).
-// 256 threads; ends with a workgroup barrier after which F is complete.
+// Factors of chunk n of (b, h) into F (and, with raw, the raw gate inputs).
+// 256 threads; ends with a workgroup barrier after which F is complete.  The
+// 16 x 16 matrices P, Aqk and Ninv are computed here (tri == null, with akk as
+// scratch) or read from tri (768 floats, as bwd_fac_kernel stores them).
 template <bool RAW>
 __device__ __forceinline__ void bwd_factors(Fac& F, Raw* raw, const bf16* __restrict__ q,
                                             const bf16* __restrict__ k,
                                             const bf16* __restrict__ z,
                                             const float* __restrict__ beta,
-                                            const bf16* __restrict__ dO, const GateConsts& gc,
-                                            int b, int h, int n, int T, int H) {
+                                            const GateConsts& gc, int b, int h, int n, int T,
+                                            int H, const float* __restrict__ tri,
+                                            float (*akk)[16]) {
     const int tid = (int)threadIdx.x;
     const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
     const int L = cp.L;
@@ -153,7 +155,6 @@ __device__ __forceinline__ void bwd_factors(Fac& F, Raw* raw, const bf16* __rest
         const int c = tid;
         const Rsrc rk = chunk_rsrc<kD>(k, cp, 2), rq = chunk_rsrc<kD>(q, cp, 2),
                    rz = chunk_rsrc<kD>(z, cp, 2);
-        float kh[16];
         float Gacc = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -169,35 +170,28 @@ __device__ __forceinline__ void bwd_factors(Fac& F, Raw* raw, const bf16* __rest
             const float ex = fast_exp2(Gacc * kLog2e), rex = fast_rcp(ex);
             F.Kt[r][c] = kf * ex;
             F.Qt[r][c] = qf * ex;
-            kh[r] = kf * rex;
-            F.Kh[r][c] = kh[r];
-            if constexpr (RAW) {
-                raw->k[r][c] = __builtin_bit_cast(bf16, (unsigned short)kb);
-                raw->q[r][c] = __builtin_bit_cast(bf16, (unsigned short)qb);
-                raw->z[r][c] = __builtin_bit_cast(bf16, (unsigned short)zb);
-            }
+            F.Kh[r][c] = kf * rex;
+            if constexpr (RAW) raw->z[r][c] = __builtin_bit_cast(bf16, (unsigned short)zb);
         }
-        const float gam = fast_exp2(Gacc * kLog2e);
-        F.gam[c] = gam;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) F.Kd[r][c] = kh[r] * gam;
+        F.gam[c] = fast_exp2(Gacc * kLog2e);
     } else {
         const int t = tid - kD;
+        if (tri) {
+            // P, Aqk, Ninv: 6 floats per thread
+#pragma unroll
+            for (int x = 0; x < 6; ++x) {
+                const int e = t + 128 * x, which = e >> 8, rc = e & 255;
+                const float val = tri[e];
+                (which == 0 ? &F.P[0][0] : which == 1 ? &F.Aqk[0][0] : &F.Ninv[0][0])[rc] = val;
+            }
+        }
         if (t < 16) {
             const Rsrc rb = make_rsrc(beta + cp.brow0, L > 0 ? (uint32_t)(((L - 1) * cp.bstride + 1) * 4) : 0u);
             F.beta[t] = __builtin_bit_cast(float, buf_load<uint32_t>(rb, t * cp.bstride * 4));
         }
-        if constexpr (RAW) {
-            // dO rows: 128 threads x 16 elements
-            const Rsrc rd = chunk_rsrc<kD>(dO, cp, 2);
-            const int r = t >> 3, c0 = (t & 7) * 16;
-            const u32x4 a = buf_load<u32x4>(rd, r * rowb + c0 * 2);
-            const u32x4 bq = buf_load<u32x4>(rd, r * rowb + (c0 + 8) * 2);
-            *reinterpret_cast<u32x4*>(&raw->dO[r][c0]) = a;
-            *reinterpret_cast<u32x4*>(&raw->dO[r][c0 + 8]) = bq;
-        }
     }
     __syncthreads();
+    if (tri) return;
     if (tid < kWave) {
         // P = Kt Kh^T and Qt Kh^T (K = 128), then Ninv by forward substitution
         const int i = tid & 15, g = tid >> 4;
@@ -213,7 +207,7 @@ __device__ __forceinline__ void bwd_factors(Fac& F, Raw* raw, const bf16* __rest
             const int r = 4 * g + e;   // row r, column i
             F.P[r][i] = p[e];
             F.Aqk[r][i] = r >= i ? a[e] : 0.f;
-            F.Akk[r][i] = r > i ? F.beta[r] * p[e] : 0.f;
+            akk[r][i] = r > i ? F.beta[r] * p[e] : 0.f;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -225,7 +219,7 @@ __device__ __forceinline__ void bwd_factors(Fac& F, Raw* raw, const bf16* __rest
             for (int r = 0; r < 16; ++r) {
                 float acc = r == j ? 1.f : 0.f;
 #pragma unroll
-                for (int c = 0; c < r; ++c) acc -= F.Akk[r][c] * x[c];
+                for (int c = 0; c < r; ++c) acc -= akk[r][c] * x[c];
                 x[r] = acc;
                 F.Ninv[r][j] = acc;
             }
@@ -239,30 +233,44 @@ __device__ __forceinline__ void bwd_factors(Fac& F, Raw* raw, const bf16* __rest
 // ------------------------------------------------------------------ kernels
 
 // Chain operands of every chunk: block (u, n) at fac + (u * NC + n) * 13824.
+// P, Aqk and Ninv of every chunk, fp32, at tri + (u * NC + n) * 768 (the
+// gradient kernel reads them instead of solving again).
 __global__ __launch_bounds__(256) void bwd_fac_kernel(const bf16* __restrict__ q,
                                                       const bf16* __restrict__ k,
                                                       const bf16* __restrict__ z,
                                                       const float* __restrict__ beta,
                                                       const float* __restrict__ A, float g_min,
-                                                      char* __restrict__ fac, int B, int T,
+                                                      char* __restrict__ fac,
+                                                      float* __restrict__ tri, int B, int T,
                                                       int H) {
     __shared__ Fac F;
+    __shared__ float akk[16][16];
     const int NC = (T + kChunk - 1) / kChunk;
     const size_t id = blockIdx.x;
     const int n = (int)(id % NC);
     const size_t u = id / NC;
     const int b = (int)(u / H), h = (int)(u % H);
-    bwd_factors<false>(F, nullptr, q, k, z, beta, nullptr, make_gate(A[h], g_min), b, h, n, T, H);
+    bwd_factors<false>(F, nullptr, q, k, z, beta, make_gate(A[h], g_min), b, h, n, T, H, nullptr,
+                       akk);
     char* out = fac + id * (size_t)CBlk::BYTES;
     const int tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    {
+        float* tr = tri + id * 768;
+        tr[tid] = (&F.P[0][0])[tid];
+        tr[256 + tid] = (&F.Aqk[0][0])[tid];
+        tr[512 + tid] = (&F.Ninv[0][0])[tid];
+    }
     if (w == 0) {
         // Kd in the A-row order of the chain's Kd dS product: slot s, lane
         // (i, g), element e <-> key channel 32 s + 16 (e / 4) + 4 g + e % 4,
         // which pairs with dS in its accumulator layout
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(&F.Kd[i][32 * s + 4 * g]);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(&F.Kd[i][32 * s + 16 + 4 * g]);
+            const int c0 = 32 * s + 4 * g, c1 = c0 + 16;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(&F.Kh[i][c0]) *
+                             *reinterpret_cast<const f32x4*>(&F.gam[c0]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(&F.Kh[i][c1]) *
+                             *reinterpret_cast<const f32x4*>(&F.gam[c1]);
             *reinterpret_cast<bf16x8*>(out + CBlk::KD + s * 1024 + lane * 16) = pack8(lo, hi);
         }
     } else if (w <= 2) {
@@ -398,7 +406,7 @@ struct GradLds {
     Raw R;
     float W[16][kRF], U[16][kRF], dU[16][kRF], dW[16][kRF];
     float dAqk[16][16], dTm[16][16], dP[16][16], T1[16][16];
-    float db1[4][16], db2[16];
+    float db2[16];
     float dAred[4];
 };
 
@@ -411,7 +419,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
     float g_min, const bf16* __restrict__ dO, const float* __restrict__ ckpt,
-    const float* __restrict__ dSend, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    const float* __restrict__ dSend, const float* __restrict__ tri, bf16* __restrict__ dq,
+    bf16* __restrict__ dk,
     bf16* __restrict__ dv, bf16* __restrict__ dz, float* __restrict__ dbeta,
     float* __restrict__ dA_part, int B, int T, int H) {
     __shared__ GradLds sm;
@@ -422,41 +431,57 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const size_t u = id / NC;
     const int b = (int)(u / H), h = (int)(u % H);
     const GateConsts gc = make_gate(A[h], g_min);
-    bwd_factors<true>(F, &sm.R, q, k, z, beta, dO, gc, b, h, n, T, H);
     const int tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
+    const float* sst = ckpt + (u * NC + n) * (size_t)kD * kD;
+    const float* dse = dSend + (u * NC + n) * (size_t)kD * kD;
+    // the first column block's S and dS columns load while the factors are
+    // formed: lane (i, g), step s holds rows 32 s + 8 g + e of column jc
+    f32x4 colS[2][4][2], colD[2][4][2];
+    auto col_load = [&](int jj) {
+        const int jc = 32 * w + 16 * jj + i;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    colS[jj][s][hh][e] = sst[(size_t)(32 * s + 8 * g + 4 * hh + e) * kD + jc];
+                    colD[jj][s][hh][e] = dse[(size_t)(32 * s + 8 * g + 4 * hh + e) * kD + jc];
+                }
+    };
+    col_load(0);
+    bwd_factors<true>(F, &sm.R, q, k, z, beta, gc, b, h, n, T, H, tri + id * 768, nullptr);
+    col_load(1);
     const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
     const int L = cp.L;
     const int rowb = (int)(cp.rstride * 2);
-    const float* sst = ckpt + (u * NC + n) * (size_t)kD * kD;
-    const float* dse = dSend + (u * NC + n) * (size_t)kD * kD;
+    const Rsrc rdo = chunk_rsrc<kD>(dO, cp, 2);
+    // dO row i, columns 32 t + 8 g .. + 7, as an exact bf16 A operand
+    auto dO_row = [&](int t) {
+        return __builtin_bit_cast(bf16x8, buf_load<u32x4>(rdo, i * rowb + (32 * t + 8 * g) * 2));
+    };
 
     // ---- value side, two 16-column blocks per wave
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
         const int j0 = 32 * w + 16 * jj, jc = j0 + i;
-        // B operands of the products over key channels: S and dS columns,
-        // lane (i, g), step s: rows 32 s + 8 g + e
+        // B operands of the products over key channels: S and dS columns
         B8 sB[4], dsB[4];
-        {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                f32x4 lo, hi, dlo, dhi;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lo[e] = sst[(size_t)(32 * s + 8 * g + e) * kD + jc];
-                    hi[e] = sst[(size_t)(32 * s + 8 * g + 4 + e) * kD + jc];
-                    dlo[e] = dse[(size_t)(32 * s + 8 * g + e) * kD + jc];
-                    dhi[e] = dse[(size_t)(32 * s + 8 * g + 4 + e) * kD + jc];
-                }
-                sB[s] = split8(lo, hi);
-                dsB[s] = split8(dlo, dhi);
-            }
+        for (int s = 0; s < 4; ++s) {
+            sB[s] = split8(colS[jj][s][0], colS[jj][s][1]);
+            dsB[s] = split8(colD[jj][s][0], colD[jj][s][1]);
         }
         f32x4 X = zero4(), Y = zero4();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            X = mma3(ld8s(&F.Kt[i][32 * s + 8 * g]), sB[s], X);   // Kt S
-            Y = mma3(ld8s(&F.Kd[i][32 * s + 8 * g]), dsB[s], Y);  // Kd dS
+            const int c0 = 32 * s + 8 * g;
+            const f32x4 kd0 = *reinterpret_cast<const f32x4*>(&F.Kh[i][c0]) *
+                              *reinterpret_cast<const f32x4*>(&F.gam[c0]);
+            const f32x4 kd1 = *reinterpret_cast<const f32x4*>(&F.Kh[i][c0 + 4]) *
+                              *reinterpret_cast<const f32x4*>(&F.gam[c0 + 4]);
+            X = mma3(ld8s(&F.Kt[i][c0]), sB[s], X);   // Kt S
+            Y = mma3(split8(kd0, kd1), dsB[s], Y);     // Kd dS
         }
         // V and dO in the accumulator layout (rows 4g + e, column jc)
         const Rsrc rv = chunk_rsrc<kD>(v, cp, 2);
@@ -464,7 +489,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             Vf[e] = bf16_bits_to_f32(buf_load<unsigned short>(rv, (4 * g + e) * rowb + jc * 2));
-            dOf[e] = bf2f(sm.R.dO[4 * g + e][jc]);
+            dOf[e] = bf16_bits_to_f32(buf_load<unsigned short>(rdo, (4 * g + e) * rowb + jc * 2));
         }
         // Tm = Ninv Diag(beta) and its transpose, Aqk^T, as K = 16 A operands
         f32x4 tmf, tmtf, aqtf;
@@ -500,7 +525,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             if (w == 0)
-                c = mma2(ld8(&sm.R.dO[i][32 * t + 8 * g]), ld8s(&sm.U[i][32 * t + 8 * g]), c);
+                c = mma2(dO_row(t), ld8s(&sm.U[i][32 * t + 8 * g]), c);
             else
                 c = mma3(ld8s(&sm.dU[i][32 * t + 8 * g]), ld8s(&sm.W[i][32 * t + 8 * g]), c);
         }
@@ -513,48 +538,36 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     }
     __syncthreads();
 
-    // ---- the triangular algebra (wave 0, fp32): lane (j = i, rows 4g .. 4g+3)
-    if (w == 0) {
-        const int j = i;
-        float db1 = 0.f;
+    // ---- the triangular algebra, fp32, one (row r, column j) per thread
+    {
+        const int r = tid >> 4, j = tid & 15;
+        // T1 = dN Ninv^T with dN = dTm Diag(beta)
+        float t1 = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            db1 += sm.dTm[r][j] * F.Ninv[r][j];
-            // T1 = dN Ninv^T with dN = dTm Diag(beta)
-            float t1 = 0.f;
+        for (int s2 = 0; s2 < 16; ++s2) t1 += sm.dTm[r][s2] * F.beta[s2] * F.Ninv[j][s2];
+        sm.T1[r][j] = t1;
+        __syncthreads();
+        // dM = -Ninv^T T1; dA = tril_{-1}(dM); dP = Diag(beta) dA
+        float dm = 0.f;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) t1 += sm.dTm[r][s] * F.beta[s] * F.Ninv[j][s];
-            sm.T1[r][j] = t1;
-        }
-        sm.db1[g][j] = db1;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int s2 = 0; s2 < 16; ++s2) dm -= F.Ninv[s2][r] * sm.T1[s2][j];
+        const float da = r > j ? dm : 0.f;
+        sm.dP[r][j] = F.beta[r] * da;
+        // dbeta_r += sum_j dA[r][j] P[r][j]: the 16 threads of row r are 16
+        // consecutive lanes of one wave
+        float t = da * F.P[r][j];
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 8);
+        if (j == 0) sm.db2[r] = t;
+        __syncthreads();
+        if (tid < 16 && tid < L) {
+            // plus dbeta_j += sum_r dTm[r][j] Ninv[r][j]
+            float dbv = sm.db2[tid];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            // dM = -Ninv^T T1; dA = tril_{-1}(dM); dP = Diag(beta) dA
-            float dm = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) dm -= F.Ninv[s][r] * sm.T1[s][j];
-            const float da = r > j ? dm : 0.f;
-            sm.dP[r][j] = F.beta[r] * da;
-            // dbeta_r += sum_j dA[r][j] P[r][j]: reduce over the 16 lanes of the row group
-            float t = da * F.P[r][j];
-            t += __shfl_xor(t, 1);
-            t += __shfl_xor(t, 2);
-            t += __shfl_xor(t, 4);
-            t += __shfl_xor(t, 8);
-            if (j == 0) sm.db2[r] = t;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < 16 && lane < L) {
-            const float dbv = sm.db1[0][lane] + sm.db1[1][lane] + sm.db1[2][lane] + sm.db1[3][lane] +
-                              sm.db2[lane];
-            dbeta[cp.brow0 + (size_t)lane * cp.bstride] = dbv;
+            for (int rr = 0; rr < 16; ++rr) dbv += sm.dTm[rr][tid] * F.Ninv[rr][tid];
+            dbeta[cp.brow0 + (size_t)tid * cp.bstride] = dbv;
         }
     }
     __syncthreads();
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) dgam += s_lo[e] * d_lo[e] + s_hi[e] * d_hi[e];
             const B8 sb = split8(s_lo, s_hi), db = split8(d_lo, d_hi);
-            cQ = mma2(ld8(&sm.R.dO[i][32 * t + 8 * g]), sb, cQ);    // dO S^T
+            cQ = mma2(dO_row(t), sb, cQ);                           // dO S^T
             cK = mma3(ld8s(&sm.dW[i][32 * t + 8 * g]), sb, cK);     // dW S^T
             cD = mma3(ld8s(&sm.U[i][32 * t + 8 * g]), db, cD);      // U dS^T
         }
@@ -609,7 +622,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             const float ex = fast_exp2(F.G[r][kc] * kLog2e), rex = fast_rcp(ex);
-            const float kv = bf2f(sm.R.k[r][kc]), qv = bf2f(sm.R.q[r][kc]);
+            const float kv = F.Kt[r][kc] * rex, qv = F.Qt[r][kc] * rex;
             const float kdv = kv * gam * rex;          // Kd
             dkv[e] = dKt[e] * ex + dKh[e] * rex + dKd[e] * gam * rex;
             dqv[e] = dQt[e] * ex;
@@ -656,7 +669,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 
 bool bwd_chunk_ok(int d, bool is_bf16) { return d == kD && is_bf16; }
 
-size_t bwd_chunk_fac_bytes() { return CBlk::BYTES; }
+size_t bwd_chunk_fac_bytes() { return CBlk::BYTES + 768 * sizeof(float); }
 
 hipError_t launch_bwd_chunk(const BackwardArgs& a, const float* ckpt, char* fac, float* dSend,
                             float* dA_part, hipStream_t stream) {
@@ -664,8 +677,9 @@ hipError_t launch_bwd_chunk(const BackwardArgs& a, const float* ckpt, char* fac,
     const size_t units = (size_t)a.B * a.H;
     const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v,
                *z = (const bf16*)a.z, *dO = (const bf16*)a.dO;
+    float* tri = (float*)(fac + units * NC * (size_t)CBlk::BYTES);
     hipLaunchKernelGGL(bwd_fac_kernel, dim3((unsigned)(units * NC)), dim3(256), 0, stream, q, k, z,
-                       a.beta, a.A, a.g_min, fac, a.B, a.T, a.H);
+                       a.beta, a.A, a.g_min, fac, tri, a.B, a.T, a.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned chains = (unsigned)(((units + 7) / 8) * 8 * (kD / 16));
@@ -673,7 +687,7 @@ hipError_t launch_bwd_chunk(const BackwardArgs& a, const float* ckpt, char* fac,
                        a.dS0, a.B, a.T, a.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(units * NC)), dim3(256), 0, stream, q, k, v,
-                       z, a.beta, a.A, a.g_min, dO, ckpt, dSend, (bf16*)a.dq, (bf16*)a.dk,
+                       z, a.beta, a.A, a.g_min, dO, ckpt, dSend, tri, (bf16*)a.dq, (bf16*)a.dk,
                        (bf16*)a.dv, (bf16*)a.dz, a.dbeta, dA_part, a.B, a.T, a.H);
     return hipGetLastError();
 }
