@@ -306,7 +306,8 @@ __global__ __launch_bounds__(256) void bwd_fac_kernel(const bf16* __restrict__ q
 // The state-gradient chain: one wave per (b, h, 16 value columns), chunks
 // last to first.  dSend[(u NC + n)][k][j] receives the gradient of chunk n's
 // end state (natural [D][D] layout); dS0 (if given) the gradient of S0.  The
-// next chunk's operands load while a chunk computes.
+// operands of the next three chunks are in flight while a chunk computes
+// (a ring of three register sets, the loop unrolled three times).
 __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__ fac,
                                                         const bf16* __restrict__ dO,
                                                         const float* __restrict__ dST,
@@ -324,10 +325,11 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
     struct Ops {
         bf16x8 kd[4], qk[8];
         bf16x4 aqt, tmt;
-        f32x4 gam[8];
+        f32x2 gv;      // gam, two values per lane (row_tile)
         u32x4 dO;
     };
     auto load = [&](Ops& o, int n) {
+        if (n < 0) return;
         const Rsrc rf = make_rsrc(fac + ((size_t)u * NC + n) * CBlk::BYTES, CBlk::BYTES);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -337,9 +339,7 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
             o.qk[m] = __builtin_bit_cast(bf16x8, buf_load<u32x4>(rf, CBlk::QK + m * 1024 + lane * 16));
         o.aqt = __builtin_bit_cast(bf16x4, buf_load<u32x2>(rf, CBlk::AQT + lane * 8));
         o.tmt = __builtin_bit_cast(bf16x4, buf_load<u32x2>(rf, CBlk::TMT + lane * 8));
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            o.gam[m] = __builtin_bit_cast(f32x4, buf_load<u32x4>(rf, CBlk::GAM + (16 * m + 4 * g) * 4));
+        o.gv = __builtin_bit_cast(f32x2, buf_load<u32x2>(rf, CBlk::GAM + row_vec_offset<kD>(g, i)));
         // dO rows 4g .. 4g+3 of column j0 + i (rows past T read 0)
         const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
         const Rsrc rd = chunk_rsrc<kD>(dO, cp, 2);
@@ -356,10 +356,9 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             dS[m][e] = st ? st[(size_t)(16 * m + 4 * g + e) * kD + j0 + i] : 0.f;
-    Ops cur, nxt;
-    load(cur, NC - 1);
-    for (int n = NC - 1; n >= 0; --n) {
-        if (n > 0) load(nxt, n - 1);
+    // chunk n with the operands in c; then chunk n - 3's operands load into c
+    auto step = [&](int n, Ops& c) {
+        if (n < 0) return;
         // the gradient of this chunk's end state, for the gradient kernel
         float* out = dSend + ((size_t)u * NC + n) * kD * kD + j0 + i;
 #pragma unroll
@@ -370,12 +369,12 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
         // feeds a 16x16x16 MFMA as its accumulator input)
         f32x4 x = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) x = mma_bf16_k32(cur.kd[s], pack8(dS[2 * s], dS[2 * s + 1]), x);
-        const f32x4 dOf = __builtin_bit_cast(f32x4, cur.dO << 16);
+        for (int s = 0; s < 4; ++s) x = mma_bf16_k32(c.kd[s], pack8(dS[2 * s], dS[2 * s + 1]), x);
+        const f32x4 dOf = __builtin_bit_cast(f32x4, c.dO << 16);
         const bf16x4 dOb = pack4(dOf);
-        const f32x4 y = mma_bf16_k16(cur.aqt, dOb, zero4());
+        const f32x4 y = mma_bf16_k16(c.aqt, dOb, zero4());
         const f32x4 dU = x + y;
-        const f32x4 dW = mma_bf16_k16(cur.tmt, pack4(dU), zero4());
+        const f32x4 dW = mma_bf16_k16(c.tmt, pack4(dU), zero4());
         // dS <- Diag(gam) dS + [Qt^T | -Kt^T] [dO; dW]
         const bf16x4 dWb = pack4(dW);
         bf16x8 b2;
@@ -384,9 +383,20 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
             b2[e] = dOb[e];
             b2[4 + e] = dWb[e];
         }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) dS[m] = mma_bf16_k32(cur.qk[m], b2, dS[m] * cur.gam[m]);
-        if (n > 0) cur = nxt;
+        static_for<0, 8>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            dS[m] = mma_bf16_k32(c.qk[m], b2, dS[m] * row_tile<m>(c.gv));
+        });
+        load(c, n - 3);
+    };
+    Ops o0, o1, o2;
+    load(o0, NC - 1);
+    load(o1, NC - 2);
+    load(o2, NC - 3);
+    for (int n = NC - 1; n >= 0; n -= 3) {
+        step(n, o0);
+        step(n - 1, o1);
+        step(n - 2, o2);
     }
     if (dS0) {
         float* out = dS0 + (size_t)u * kD * kD + j0 + i;

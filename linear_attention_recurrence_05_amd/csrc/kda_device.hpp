@@ -146,6 +146,24 @@ __device__ __forceinline__ float row_bcast(float x) {
                                                                  0x150 + L, 0xF, 0xF, false));
 }
 
+// Values of rows 16 M + 4 g + p (p = 0..3) of a length-D vector for lane
+// (j, g) = 16 g + j, when lane (k, g) holds rows 16 (k/2) + 4 g + 2 (k%2) +
+// {0, 1} (row_vec_offset): DPP row broadcasts deliver them, so a lane reads
+// and holds 8 bytes of the vector instead of 16 per 16-row tile.
+template <int M>
+__device__ __forceinline__ f32x4 row_tile(const f32x2& gv) {
+    return f32x4{row_bcast<2 * M>(gv[0]), row_bcast<2 * M>(gv[1]),
+                 row_bcast<2 * M + 1>(gv[0]), row_bcast<2 * M + 1>(gv[1])};
+}
+
+// Byte offset (from the start of the fp32 vector) of the two values lane
+// (r, g) holds for row_tile; lanes past the last tile read a valid word.
+template <int D>
+__device__ __forceinline__ int row_vec_offset(int g, int r) {
+    const int mm = min(r >> 1, D / 16 - 1);
+    return (16 * mm + 4 * g + 2 * (r & 1)) * 4;
+}
+
 // f(integral_constant<int, I>) for I = B .. E-1, each with a compile-time index
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {

@@ -451,13 +451,10 @@ struct POps {
     f32x2 gv;   // two values of gam_a gam_b per lane (see gab_tile)
 };
 
-// gam_a gam_b of rows 16 M + 4 g + p (p = 0..3) of tile M for lane (j, g).
-// Lane (k, g) holds rows 16 (k/2) + 4 g + 2 (k%2) + {0, 1} of the vector, and
-// row broadcasts deliver them: the lane reads 8 bytes instead of 16 per tile.
+// gam_a gam_b of rows 16 M + 4 g + p of tile M for lane (j, g) (row_tile).
 template <int M>
 __device__ __forceinline__ f32x4 gab_tile(const f32x2& gv) {
-    return f32x4{row_bcast<2 * M>(gv[0]), row_bcast<2 * M>(gv[1]),
-                 row_bcast<2 * M + 1>(gv[0]), row_bcast<2 * M + 1>(gv[1])};
+    return row_tile<M>(gv);
 }
 
 // The operands read first (Kt_a, Kt_b Diag(gam_a)): loaded one pair ahead.
@@ -488,10 +485,7 @@ template <typename E, int D>
 __device__ __forceinline__ void pops_load_supd(POps<E, D>& c, const char* blk) {
     using P = PBlk<E, D>;
     const int lane = lane_id(), g = lane >> 4, r = lane & 15;
-    {
-        const int mm = min(r >> 1, P::MT - 1);   // lanes past the last tile read a valid word
-        c.gv = *reinterpret_cast<const f32x2*>(blk + P::GAB + (16 * mm + 4 * g + 2 * (r & 1)) * 4);
-    }
+    c.gv = *reinterpret_cast<const f32x2*>(blk + P::GAB + row_vec_offset<D>(g, r));
 #pragma unroll
     for (int m = 0; m < P::MT; ++m) {
         c.kd2[m] = *reinterpret_cast<const V8<E>*>(blk + P::kd2_offset(m, g, r));
