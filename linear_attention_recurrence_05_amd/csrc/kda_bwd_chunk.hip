@@ -409,16 +409,28 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
 
 namespace {
 
+// Row stride of the staging tile (64 rows of S or dS, fp32): with 130 floats
+// the column reads of the value side (lanes: 16 columns x rows 8 apart) fall
+// in distinct banks, and rows stay 8-byte aligned for the row writes.
+constexpr int kSS = kD + 2;
+
 // Scratch of the gradient kernel: the 16 x 128 products of the value side and
-// the 16 x 16 gradients of the triangular algebra.
+// the 16 x 16 gradients of the triangular algebra.  Before the products exist
+// their space stages half of S or dS at a time for the value side.
 struct GradLds {
     Fac F;
     Raw R;
-    float W[16][kRF], U[16][kRF], dU[16][kRF], dW[16][kRF];
+    union {
+        struct {
+            float W[16][kRF], U[16][kRF], dU[16][kRF], dW[16][kRF];
+        };
+        float stage[64][kSS];
+    };
     float dAqk[16][16], dTm[16][16], dP[16][16], T1[16][16];
     float db2[16];
     float dAred[4];
 };
+static_assert(sizeof(float) * 64 * kSS <= sizeof(float) * 4 * 16 * kRF, "staging tile fits");
 
 }  // namespace
 
@@ -444,24 +456,28 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const int tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63, i = lane & 15, g = lane >> 4;
     const float* sst = ckpt + (u * NC + n) * (size_t)kD * kD;
     const float* dse = dSend + (u * NC + n) * (size_t)kD * kD;
-    // the first column block's S and dS columns load while the factors are
-    // formed: lane (i, g), step s holds rows 32 s + 8 g + e of column jc
-    f32x4 colS[2][4][2], colD[2][4][2];
-    auto col_load = [&](int jj) {
-        const int jc = 32 * w + 16 * jj + i;
+    // S and dS rows 32 w .. 32 w + 31 (the wave's key channels), loaded once
+    // while the factors are formed: lane (i, g) holds rows 32 w + 16 kk + i,
+    // columns 32 t + 8 g .. + 7 -- the B operands of the key side as they
+    // are, and the wave's share of the staging tile for the value side.
+    f32x4 rowS[2][4][2], rowD[2][4][2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+        for (int t = 0; t < 4; ++t) {
+            const size_t off = (size_t)(32 * w + 16 * kk + i) * kD + 32 * t + 8 * g;
+            rowS[kk][t][0] = *reinterpret_cast<const f32x4*>(sst + off);
+            rowS[kk][t][1] = *reinterpret_cast<const f32x4*>(sst + off + 4);
+        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    colS[jj][s][hh][e] = sst[(size_t)(32 * s + 8 * g + 4 * hh + e) * kD + jc];
-                    colD[jj][s][hh][e] = dse[(size_t)(32 * s + 8 * g + 4 * hh + e) * kD + jc];
-                }
-    };
-    col_load(0);
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const size_t off = (size_t)(32 * w + 16 * kk + i) * kD + 32 * t + 8 * g;
+            rowD[kk][t][0] = *reinterpret_cast<const f32x4*>(dse + off);
+            rowD[kk][t][1] = *reinterpret_cast<const f32x4*>(dse + off + 4);
+        }
     bwd_factors<true>(F, &sm.R, q, k, z, beta, gc, b, h, n, T, H, tri + id * 768, nullptr);
-    col_load(1);
     const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
     const int L = cp.L;
     const int rowb = (int)(cp.rstride * 2);
@@ -471,28 +487,64 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         return __builtin_bit_cast(bf16x8, buf_load<u32x4>(rdo, i * rowb + (32 * t + 8 * g) * 2));
     };
 
-    // ---- value side, two 16-column blocks per wave
+    // ---- value side: X = Kt S and Y = Kd dS over the 128 key channels, for
+    // the wave's two 16-column blocks.  Half of S (or dS) at a time passes
+    // through the staging tile: the two waves that hold rows 64 hf .. 64 hf +
+    // 63 write them, then every wave reads its columns of those rows.
+    f32x4 Xa[2] = {zero4(), zero4()}, Ya[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int arr = 0; arr < 2; ++arr) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            if ((w >> 1) == hf) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const f32x4 x = arr == 0 ? rowS[kk][t][hh] : rowD[kk][t][hh];
+                            float* dst = &sm.stage[32 * (w & 1) + 16 * kk + i][32 * t + 8 * g + 4 * hh];
+                            *reinterpret_cast<f32x2*>(dst) = f32x2{x[0], x[1]};
+                            *reinterpret_cast<f32x2*>(dst + 2) = f32x2{x[2], x[3]};
+                        }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                const int s = 2 * hf + sl, c0 = 32 * s + 8 * g;
+                B8 a;
+                if (arr == 0) {
+                    a = ld8s(&F.Kt[i][c0]);
+                } else {
+                    const f32x4 kd0 = *reinterpret_cast<const f32x4*>(&F.Kh[i][c0]) *
+                                      *reinterpret_cast<const f32x4*>(&F.gam[c0]);
+                    const f32x4 kd1 = *reinterpret_cast<const f32x4*>(&F.Kh[i][c0 + 4]) *
+                                      *reinterpret_cast<const f32x4*>(&F.gam[c0 + 4]);
+                    a = split8(kd0, kd1);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int jc = 32 * w + 16 * jj + i;
+                    f32x4 c_lo, c_hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        c_lo[e] = sm.stage[32 * sl + 8 * g + e][jc];
+                        c_hi[e] = sm.stage[32 * sl + 8 * g + 4 + e][jc];
+                    }
+                    if (arr == 0)
+                        Xa[jj] = mma3(a, split8(c_lo, c_hi), Xa[jj]);   // Kt S
+                    else
+                        Ya[jj] = mma3(a, split8(c_lo, c_hi), Ya[jj]);   // Kd dS
+                }
+            }
+            __syncthreads();
+        }
+    }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
         const int j0 = 32 * w + 16 * jj, jc = j0 + i;
-        // B operands of the products over key channels: S and dS columns
-        B8 sB[4], dsB[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            sB[s] = split8(colS[jj][s][0], colS[jj][s][1]);
-            dsB[s] = split8(colD[jj][s][0], colD[jj][s][1]);
-        }
-        f32x4 X = zero4(), Y = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int c0 = 32 * s + 8 * g;
-            const f32x4 kd0 = *reinterpret_cast<const f32x4*>(&F.Kh[i][c0]) *
-                              *reinterpret_cast<const f32x4*>(&F.gam[c0]);
-            const f32x4 kd1 = *reinterpret_cast<const f32x4*>(&F.Kh[i][c0 + 4]) *
-                              *reinterpret_cast<const f32x4*>(&F.gam[c0 + 4]);
-            X = mma3(ld8s(&F.Kt[i][c0]), sB[s], X);   // Kt S
-            Y = mma3(split8(kd0, kd1), dsB[s], Y);     // Kd dS
-        }
+        const f32x4 X = Xa[jj], Y = Ya[jj];
         // V and dO in the accumulator layout (rows 4g + e, column jc)
         const Rsrc rv = chunk_rsrc<kD>(v, cp, 2);
         f32x4 Vf, dOf;
@@ -593,12 +645,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             // S and dS rows kc, value columns 32 t + 8 g .. + 7 (fp32)
-            const float* sr = sst + (size_t)kc * kD + 32 * t + 8 * g;
-            const float* dr = dse + (size_t)kc * kD + 32 * t + 8 * g;
-            const f32x4 s_lo = *reinterpret_cast<const f32x4*>(sr);
-            const f32x4 s_hi = *reinterpret_cast<const f32x4*>(sr + 4);
-            const f32x4 d_lo = *reinterpret_cast<const f32x4*>(dr);
-            const f32x4 d_hi = *reinterpret_cast<const f32x4*>(dr + 4);
+            const f32x4 s_lo = rowS[kk][t][0], s_hi = rowS[kk][t][1];
+            const f32x4 d_lo = rowD[kk][t][0], d_hi = rowD[kk][t][1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) dgam += s_lo[e] * d_lo[e] + s_hi[e] * d_hi[e];
             const B8 sb = split8(s_lo, s_hi), db = split8(d_lo, d_hi);
