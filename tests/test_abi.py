@@ -438,11 +438,12 @@ def test_backward_workspace_query():
     # at least the chunk-start states: 32 heads x 256 chunks x 128 x 128 fp32
     assert n >= 32 * 256 * 128 * 128 * 4
     # the chunkwise plan (bf16, d = 128): per extra chunk of every head, a
-    # start state, an end-state gradient, the chain's operand block and a
-    # dA term; the segment scan behind the segment-parallel forward sweep
-    # runs state-only passes here (no zero v, no scratch o)
+    # start state, an end-state gradient, the chain's operand block, the fp32
+    # triangular factors (P, Aqk, Ninv) and a dA term; the segment scan behind
+    # the segment-parallel forward sweep runs state-only passes here (no zero
+    # v, no scratch o)
     n2 = kda.kda_chunk_backward_workspace_bytes(1, 8192, 32, 128, 128, kda.KDA_BF16)
-    extra = 32 * 256 * (2 * 128 * 128 * 4 + 13824 + 4)
+    extra = 32 * 256 * (2 * 128 * 128 * 4 + 13824 + 3 * 16 * 16 * 4 + 4)
     assert extra <= n2 - n <= extra + (1 << 20)
     # the token-level sweep (forced) holds the per-token corrections and
     # bounded partial sums instead
