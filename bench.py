@@ -110,14 +110,17 @@ def cpu_model():
 
 
 def time_prefill(kda, torch, workload, stream, dev, steps, warmup, segments=1, rotate=False,
-                 flush=False):
+                 flush=False, g_min=None):
     """Times `steps` prefill passes of one workload (after `warmup` untimed
-    ones) with HIP events on `stream`.  Returns (result dict, inputs)."""
+    ones) with HIP events on `stream`; g_min overrides the workload's.
+    Returns (result dict, inputs)."""
     from linear_attention_recurrence_05_amd.inputs import PREFILL_CONFIGS, config_inputs
     cfg_index = WORKLOADS[workload]
     cfg = PREFILL_CONFIGS[cfg_index]
     B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.dk
     x = config_inputs(cfg_index, dev)
+    if g_min is not None:
+        x["g_min"] = g_min
     o = torch.empty(B, T, H, d, dtype=cfg.dtype, device=dev)
     ST = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
     if segments > 1:
@@ -198,7 +201,7 @@ def time_prefill(kda, torch, workload, stream, dev, steps, warmup, segments=1, r
     alg_f = prefill_alg_flops(B, T, H, d)
     gbs = alg_b / (ms * 1e-3) / 1e9
     tflops = alg_f / (ms * 1e-3) / 1e12
-    key = f"prefill_{workload}_pass"
+    key = f"prefill_{workload}_pass" if g_min is None else f"prefill_{workload}_gmin{g_min:g}_pass"
     kernel = ("segment-scan prefill pass (identity_kernel, two state-only fused_kernel map "
               "passes, segscan_kernel, one full fused_kernel pass)" if n_seg > 1
               else "prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
@@ -207,7 +210,7 @@ def time_prefill(kda, torch, workload, stream, dev, steps, warmup, segments=1, r
     res.update({
         "value": B * T / (ms * 1e-3), "unit": "tokens/s",
         "config": {"workload": f"{cfg.name}_prefill_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T,
-                   "H": H, "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": -5.0,
+                   "H": H, "d_k": d, "d_v": d, "chunk": CHUNK, "g_min": x["g_min"],
                    "S0": "zeros" if x["S0"] is None else "N(0, 0.01)",
                    "parallelism": "single GPU", "plan": plan, "workspace_bytes": nb},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -313,6 +316,16 @@ def main():
                       vv.cpu() if hasattr(vv, "cpu") else vv) for kk, vv in x.items()}
     del x
     torch.cuda.empty_cache()
+
+    if not args.no_sub and args.workload == "long" and args.segments == 1:
+        # the same sequence with slow decay (g_min = -0.05): no segment's map
+        # vanishes, so the segment scan runs its map pass in full and redoes
+        # every segment from its scanned start state
+        r, xw = time_prefill(kda, torch, "long", stream, dev, 3, 1, g_min=-0.05)
+        del xw
+        torch.cuda.empty_cache()
+        r["metric"] = "KDA prefill tokens/s, slow decay (g_min = -0.05)"
+        line["long_slow_decay"] = r
 
     if not args.no_sub:
         for wl in ("mid", "batched"):

@@ -78,6 +78,16 @@ struct TokensArgs {
     bool is_bf16;
 };
 
+// Per-unit chunk counts of a fused-plan pass (unit u = b H + h of the pass):
+// `in` (may be null) limits unit u to its first in[u] chunks; `out` (may be
+// null; only state-only passes with v = 0 take it) makes the pass stop once
+// the unit's state is exactly zero, and receives in out[u] the number of
+// chunks it processed.
+struct ChunkLim {
+    const int* in;
+    int* out;
+};
+
 struct PrefillArgs {
     const void *q, *k, *v, *z;
     const float *beta, *A;
@@ -86,6 +96,7 @@ struct PrefillArgs {
     void* o;
     int B, T, H, d;
     bool is_bf16;
+    ChunkLim lim{};     // fused plan only
 };
 
 // Gradients of a prefill: inputs of the forward call plus dO (and dST, may be
@@ -187,7 +198,7 @@ hipError_t launch_backward(const BackwardArgs& a, void* ws, hipStream_t stream);
 // a scan over segments, and a last pass from the scanned start states.
 struct SegLayout {
     PlanInfo inner;        // plan of the inner prefill calls (B * R rows of T / R)
-    size_t inner_ws, vzero, ident, M, N, Sin, total;   // byte offsets, 256-aligned
+    size_t inner_ws, vzero, ident, M, N, Sin, nch, total;   // byte offsets, 256-aligned
 };
 SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R);
 // a.S: dense S0 (in, may be null) and S_T (out, may be null).

@@ -1271,6 +1271,7 @@ static hipError_t launch_split_t(const PrefillArgs& a, const PlanInfo& p, void* 
 }
 
 hipError_t launch_split(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream) {
+    if (a.lim.in || a.lim.out) return hipErrorInvalidValue;   // per-unit chunk counts: fused plan only
     if (a.is_bf16)
         return a.d == 128 ? launch_split_t<bf16, 128>(a, p, ws, stream)
                           : launch_split_t<bf16, 32>(a, p, ws, stream);

@@ -115,25 +115,43 @@ struct FusedCfg {
 // 1 + NM barriers.  WQ = false: only the end state (q and o are not
 // touched); VZ: v is taken as zero (v is not read); CK: the state at the
 // start of every chunk is stored too (ck, the checkpoints of a backward).
-template <typename E, int D, int NB, int NCW, bool WQ = true, bool VZ = false, bool CK = false>
+// lim.in limits unit u to its first lim.in[u] chunks.  EX (state-only, v =
+// 0): the pass stops after the first step at whose end the state of every
+// consumer is exactly zero -- with v = 0 a zero state stays zero, so the end
+// state is the same -- and lim.out[u] receives the number of chunks
+// processed.
+template <typename E, int D, int NB, int NCW, bool WQ = true, bool VZ = false, bool CK = false,
+          bool EX = false>
 __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ v, const E* __restrict__ z,
                                                     const float* __restrict__ beta,
                                                     const float* __restrict__ A, float g_min,
                                                     StateIO io, E* __restrict__ o,
                                                     int B, int T, int H, int nct,
-                                                    CkOut ck = CkOut{}) {
+                                                    CkOut ck = CkOut{}, ChunkLim lim = ChunkLim{}) {
     using Bk = Blk<E, D>;
     using Cfg = FusedCfg<E, D>;
     constexpr int NPROD = Cfg::NPROD;
+    static_assert(!EX || (VZ && !WQ && NCW <= 4), "early exit: state-only passes with v = 0");
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
+    // EX: per consumer wave, whether its state was zero at the end of step m
+    // (slot m & 1: a slot is rewritten two steps later, after every wave has
+    // passed the barrier between)
+    __shared__ int zflag[2][4];
     int u, ct;
     if (!map_unit(nct, B * H, u, ct)) return;   // uniform over the workgroup
     const int b = u / H, h = u % H;
     if (io.skip(b)) return;                      // uniform over the workgroup
     const int w = wave_id();
-    const int NC = (T + kChunk - 1) / kChunk;
+    const int NCA = (T + kChunk - 1) / kChunk;
+    const int NC = lim.in ? max(0, min(NCA, lim.in[u])) : NCA;   // uniform over the workgroup
     const int NM = (NC + NPROD - 1) / NPROD;
+    auto all_zero = [&](int m) {
+        bool z0 = true;
+#pragma unroll
+        for (int x = 0; x < NCW; ++x) z0 = z0 && zflag[m & 1][x] != 0;
+        return z0;
+    };
 
     if (w < NPROD) {
         // ------------------------------------------------ producer wave
@@ -160,6 +178,9 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
                                               smem + (((m + 1) & 1) * NPROD + w) * Bk::BYTES,
                                               myscr, nullptr, nullptr, nullptr);
             wg_barrier();
+            if constexpr (EX) {
+                if (all_zero(m)) break;
+            }
         }
         return;
     }
@@ -167,7 +188,12 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
     if (cw < 0 || cw >= NCW) {
         // ------------------------------------------------ idle wave
         wg_barrier();
-        for (int m = 0; m < NM; ++m) wg_barrier();
+        for (int m = 0; m < NM; ++m) {
+            wg_barrier();
+            if constexpr (EX) {
+                if (all_zero(m)) break;
+            }
+        }
         return;
     }
     // ---------------------------------------------------- consumer wave
@@ -182,6 +208,7 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
             if (cc < NC) v_load<D, NB>(Vc[cc], v, ES, chunk_pos<D>(b, h, cc, T, H), col0);
     }
     wg_barrier();
+    int done = NC;
     for (int m = 0; m < NM; ++m) {
         if constexpr (!VZ) {
 #pragma unroll
@@ -223,7 +250,29 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) Vc[cc][nb] = Vn[cc][nb];
         }
+        if constexpr (EX) {
+            // exactly zero: every bit but the sign clear (-0 counts as zero)
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        bits |= __builtin_bit_cast(uint32_t, S[nb][mm][p]) & 0x7FFFFFFFu;
+            const bool wz = !__any(bits != 0u);
+            if (lane_id() == 0) zflag[m & 1][cw] = wz ? 1 : 0;
+        }
         wg_barrier();
+        if constexpr (EX) {
+            if (all_zero(m)) {
+                done = min(NC, (m + 1) * NPROD);
+                break;
+            }
+        }
+    }
+    if constexpr (EX) {
+        if (cw == 0 && lane_id() == 0) lim.out[u] = done;
     }
     if (io.out) state_store<D, NB>(S, io.out_at(b, h, H, D), col0);
 }
@@ -310,45 +359,38 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PlanInfo& p, void
     if (p.plan == Plan::kFused) {
         const int nct = D / p.ncol;
         const dim3 grid(grid_units(units, nct)), block(512);
+        const CkOut nock{};
         if (!o || !v) {
             // state-only passes (o null; v null = zero), d = 128 with 128 or
             // 64 columns per workgroup (prefill_state_only_ok); a null v
-            // with outputs is not a pass any caller makes
-            if (D != 128 || o != nullptr || (p.ncol != 128 && p.ncol != 64))
+            // with outputs is not a pass any caller makes; the early exit
+            // (lim.out) only for v = 0
+            if (D != 128 || o != nullptr || (p.ncol != 128 && p.ncol != 64) || (v && a.lim.out))
                 return hipErrorInvalidValue;
+#define KDA_FUSED_SO(NB, VZ, EX)                                                                  \
+    hipLaunchKernelGGL((fused_kernel<E, D, NB, 4, false, VZ, false, EX>), grid, block, 0, stream, q, \
+                       k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct, nock, a.lim)
             if (p.ncol == 128) {
-                if (v)
-                    hipLaunchKernelGGL((fused_kernel<E, D, 2, 4, false, false>), grid, block, 0,
-                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
-                                       a.H, nct);
-                else
-                    hipLaunchKernelGGL((fused_kernel<E, D, 2, 4, false, true>), grid, block, 0,
-                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
-                                       a.H, nct);
+                if (v) KDA_FUSED_SO(2, false, false);
+                else if (a.lim.out) KDA_FUSED_SO(2, true, true);
+                else KDA_FUSED_SO(2, true, false);
             } else {
-                if (v)
-                    hipLaunchKernelGGL((fused_kernel<E, D, 1, 4, false, false>), grid, block, 0,
-                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
-                                       a.H, nct);
-                else
-                    hipLaunchKernelGGL((fused_kernel<E, D, 1, 4, false, true>), grid, block, 0,
-                                       stream, q, k, v, z, a.beta, a.A, a.g_min, a.S, o, a.B, a.T,
-                                       a.H, nct);
+                if (v) KDA_FUSED_SO(1, false, false);
+                else if (a.lim.out) KDA_FUSED_SO(1, true, true);
+                else KDA_FUSED_SO(1, true, false);
             }
+#undef KDA_FUSED_SO
             return hipGetLastError();
         }
-        if (p.ncol == 128 && D == 128)
-            hipLaunchKernelGGL((fused_kernel<E, D, 2, 4>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
-        else if (p.ncol == 64 && D == 128)
-            hipLaunchKernelGGL((fused_kernel<E, D, 1, 4>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
-        else if (p.ncol == 32)
-            hipLaunchKernelGGL((fused_kernel<E, D, 1, 2>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
-        else
-            hipLaunchKernelGGL((fused_kernel<E, D, 1, 1>), grid, block, 0, stream, q, k, v, z, a.beta,
-                               a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct);
+        if (a.lim.out) return hipErrorInvalidValue;
+#define KDA_FUSED(NB, NCW)                                                                        \
+    hipLaunchKernelGGL((fused_kernel<E, D, NB, NCW>), grid, block, 0, stream, q, k, v, z, a.beta,  \
+                       a.A, a.g_min, a.S, o, a.B, a.T, a.H, nct, nock, a.lim)
+        if (p.ncol == 128 && D == 128) KDA_FUSED(2, 4);
+        else if (p.ncol == 64 && D == 128) KDA_FUSED(1, 4);
+        else if (p.ncol == 32) KDA_FUSED(1, 2);
+        else KDA_FUSED(1, 1);
+#undef KDA_FUSED
         return hipGetLastError();
     }
     (void)ws;

@@ -44,6 +44,26 @@ __global__ __launch_bounds__(256) void identity_kernel(float* __restrict__ p, si
     }
 }
 
+// Start states of the two map passes with the segments of every sequence as
+// rows b R + r ([B R, H, d, d] each): the M_r pass from the identity, except
+// segment 0, whose map is taken as zero (it starts from the known S0); the
+// other pass from zero, except segment 0, which starts from S0 (null: zero),
+// so that its end state is already S_in(1).
+__global__ __launch_bounds__(256) void seg_fill_kernel(float* __restrict__ ident,
+                                                       float* __restrict__ nstart,
+                                                       const float* __restrict__ S0, int B, int R,
+                                                       int H, int d) {
+    const size_t per = (size_t)d * d, n = (size_t)B * R * H * per;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+        const size_t st = i / per, e = i % per;
+        const size_t row = st / H, h = st % H;
+        const size_t b = row / R;
+        const bool first = row % R == 0;
+        ident[i] = (!first && e / d == e % d) ? 1.0f : 0.0f;
+        nstart[i] = (first && S0) ? S0[(b * H + h) * per + e] : 0.0f;
+    }
+}
+
 // Scan over the R segments of each (b, h), one workgroup per 16 value
 // columns: S <- M_r S + N_r, with M_r staged in LDS and M_{r+1} loaded into
 // registers while step r computes.  Writes S_in(r) of every segment to
@@ -158,12 +178,22 @@ SegLayout seg_layout(int B, int T, int H, int d, bool is_bf16, int R) {
     L.M = take(states);
     L.N = take(states);
     L.Sin = take(states);
+    L.nch = take((size_t)B * R * H * sizeof(int));
     L.total = off;
     return L;
 }
 
-hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, char* w,
-                            hipStream_t stream) {
+// Fused inner plan (bf16 or fp32 at d = 128, state-only passes):
+//   M_r: from the identity (zero for segment 0) with v = 0, stopping once the
+//        map is exactly zero -- it only contracts, and for fast-decaying
+//        gates it vanishes within a few chunks -- and recording how many
+//        chunks that took (nch: the segment's first nch chunks depend on its
+//        start state; the later ones do not);
+//   N_r: from zero (segment 0 from S0), with the outputs when with_o;
+//   the scan.
+// Other plans: M_r and N_r in full, as ordinary prefills with a zero v.
+static hipError_t start_states(const PrefillArgs& a, int R, const SegLayout& L, char* w,
+                               bool with_o, hipStream_t stream) {
     void* inner = L.inner.ws_bytes ? (void*)(w + L.inner_ws) : nullptr;
     float* ident = (float*)(w + L.ident);
     float* M = (float*)(w + L.M);
@@ -171,11 +201,20 @@ hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, cha
     float* Sin = (float*)(w + L.Sin);
     const int Bs = a.B * R, Ts = a.T / R;
     const size_t n_states = (size_t)Bs * a.H;
-    // Plans that have state-only passes skip q, o and (for M_r) v; the others
-    // run ordinary prefills with a zero v buffer and o as scratch.
     const bool state_only = prefill_state_only_ok(L.inner, a.d);
     hipError_t e;
-    if (!state_only) {
+    const float* s_in0 = a.S.in;
+    if (state_only) {
+        hipLaunchKernelGGL(seg_fill_kernel, dim3(2048), dim3(256), 0, stream, ident, N, a.S.in, a.B,
+                           R, a.H, a.d);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        PrefillArgs pm{a.q, a.k, nullptr, a.z, a.beta, a.A, a.g_min, dense_state(ident, M), nullptr,
+                       Bs, Ts, a.H, a.d, a.is_bf16, ChunkLim{nullptr, (int*)(w + L.nch)}};
+        if ((e = launch_prefill(pm, L.inner, inner, stream)) != hipSuccess) return e;
+        PrefillArgs pn{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state(N, N),
+                       with_o ? a.o : nullptr, Bs, Ts, a.H, a.d, a.is_bf16};
+        if ((e = launch_prefill(pn, L.inner, inner, stream)) != hipSuccess) return e;
+    } else {
         // v has d (a multiple of 32) elements per token-head: whole 16-byte words
         const size_t vwords = (size_t)a.B * a.T * a.H * a.d * (a.is_bf16 ? 2 : 4) / 16;
         size_t zblocks = (vwords + 255) / 256;
@@ -183,35 +222,47 @@ hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, cha
         hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream,
                            (u32x4*)(w + L.vzero), vwords);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(identity_kernel, dim3(2048), dim3(256), 0, stream, ident, n_states, a.d);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        // M_r: v = 0 from the identity; N_r: v from zero; o is scratch.
+        PrefillArgs pm{a.q, a.k, (const void*)(w + L.vzero), a.z, a.beta, a.A, a.g_min,
+                       dense_state(ident, M), a.o, Bs, Ts, a.H, a.d, a.is_bf16};
+        if ((e = launch_prefill(pm, L.inner, inner, stream)) != hipSuccess) return e;
+        PrefillArgs pn{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state(nullptr, N), a.o,
+                       Bs, Ts, a.H, a.d, a.is_bf16};
+        if ((e = launch_prefill(pn, L.inner, inner, stream)) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(identity_kernel, dim3(2048), dim3(256), 0, stream, ident, n_states, a.d);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // M_r: v = 0 from the identity; N_r: v from zero.
-    void* o_scr = state_only ? nullptr : a.o;
-    PrefillArgs pm{a.q, a.k, state_only ? nullptr : (const void*)(w + L.vzero), a.z, a.beta, a.A,
-                   a.g_min, dense_state(ident, M), o_scr, Bs, Ts, a.H, a.d, a.is_bf16};
-    if ((e = launch_prefill(pm, L.inner, inner, stream)) != hipSuccess) return e;
-    PrefillArgs pn{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state(nullptr, N), o_scr,
-                   Bs, Ts, a.H, a.d, a.is_bf16};
-    if ((e = launch_prefill(pn, L.inner, inner, stream)) != hipSuccess) return e;
     const unsigned grid = (unsigned)((size_t)a.B * a.H * (a.d / 16));
     if (a.d == 128)
-        hipLaunchKernelGGL(segscan_kernel<128>, dim3(grid), dim3(256), 0, stream, M, N, a.S.in,
-                           Sin, a.S.out, a.H, R);
+        hipLaunchKernelGGL(segscan_kernel<128>, dim3(grid), dim3(256), 0, stream, M, N, s_in0, Sin,
+                           a.S.out, a.H, R);
     else
-        hipLaunchKernelGGL(segscan_kernel<32>, dim3(grid), dim3(256), 0, stream, M, N, a.S.in,
-                           Sin, a.S.out, a.H, R);
+        hipLaunchKernelGGL(segscan_kernel<32>, dim3(grid), dim3(256), 0, stream, M, N, s_in0, Sin,
+                           a.S.out, a.H, R);
     return hipGetLastError();
 }
 
+hipError_t seg_start_states(const PrefillArgs& a, int R, const SegLayout& L, char* w,
+                            hipStream_t stream) {
+    return start_states(a, R, L, w, false, stream);
+}
+
+// Fused inner plan: the start states with the outputs of every segment from
+// its zero start (exact from each segment's nch-th chunk on, and in segment
+// 0 throughout), then the first nch chunks of every segment again from its
+// scanned start state, overwriting those outputs.  When a map does not
+// vanish, nch is the whole segment and this last pass is a full one.  Other
+// plans: the start states, then every segment in full from its start state.
 hipError_t launch_segmented(const PrefillArgs& a, int R, void* ws, hipStream_t stream) {
     const SegLayout L = seg_layout(a.B, a.T, a.H, a.d, a.is_bf16, R);
     char* w = (char*)ws;
-    hipError_t e = seg_start_states(a, R, L, w, stream);
+    const bool fast = prefill_state_only_ok(L.inner, a.d);
+    hipError_t e = start_states(a, R, L, w, fast, stream);
     if (e != hipSuccess) return e;
     void* inner = L.inner.ws_bytes ? (void*)(w + L.inner_ws) : nullptr;
     PrefillArgs pf{a.q, a.k, a.v, a.z, a.beta, a.A, a.g_min, dense_state((float*)(w + L.Sin), nullptr),
                    a.o, a.B * R, a.T / R, a.H, a.d, a.is_bf16};
+    if (fast) pf.lim = ChunkLim{(const int*)(w + L.nch), nullptr};
     return launch_prefill(pf, L.inner, inner, stream);
 }
 

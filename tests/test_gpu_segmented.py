@@ -134,3 +134,39 @@ def test_prefill_chooses_segment_scan_for_long_sequences_of_few_heads(H, R):
         kda.kda_chunk_prefill(*args, x["g_min"], x["S0"], o3, None, ws)
         torch.cuda.synchronize()
         assert torch.equal(S, ST) and torch.equal(o2, o) and torch.equal(o3, o)
+
+
+@pytest.mark.parametrize("dt,H,decay", [("bf16", 32, "fast"), ("bf16", 32, "slow"),
+                                        ("bf16", 32, "mixed"), ("bf16", 24, "mixed"),
+                                        ("f32", 32, "fast"), ("f32", 32, "mixed")])
+def test_segmented_fused_map_early_exit(dt, H, decay):
+    """Segments of the fused plan (B * R * H >= 128 units at d = 128): the M_r
+    pass stops once a segment's map is exactly zero, the outputs come from a
+    zero-start pass and the first chunks of every segment are redone from its
+    scanned start state.  Fast decay (g_min = -5: every map vanishes within a
+    few chunks), slow decay (g_min = -0.05: no map vanishes, the redo covers
+    whole segments) and a mix (half the heads with z shifted by -12, so that
+    their gate stays near 0 and their maps do not vanish), with S0 given;
+    against the oracle and bit for bit from run to run."""
+    dev = need_gpu()
+    T, R = (2048, 8) if dt == "bf16" else (1024, 8)
+    x = prefill_inputs(1, T, H, 128, 128, DT[dt], seed=1300 + H + len(decay), s0_std=0.1,
+                       device=dev)
+    if decay == "slow":
+        x["g_min"] = -0.05
+    elif decay == "mixed":
+        zf = x["z"].float()
+        zf[:, :, ::2] -= 12.0
+        x["z"] = zf.to(x["z"].dtype)
+    o, ST = seg(x, R)
+    o2, ST2 = seg(x, R)
+    assert torch.equal(o, o2) and torch.equal(ST, ST2)
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"], x["g_min"],
+                                  x["S0"], nthreads=16)
+    eo, es = rel_err(o, o_ref), rel_err(ST, S_ref)
+    Tseg = T // R
+    eb = max(rel_err(o[:, r * Tseg:r * Tseg + 64], o_ref[:, r * Tseg:r * Tseg + 64])
+             for r in range(1, R))
+    say(f"segmented fused {dt} H={H} {decay} decay: o {eo:.2e} S_T {es:.2e}; "
+        f"first 64 tokens after each boundary {eb:.2e}")
+    assert eo < TOL[DT[dt]] and es < TOL[DT[dt]] and eb < TOL[DT[dt]]
