@@ -537,6 +537,78 @@ __device__ __forceinline__ void state_store(const f32x4 (&S)[NB][D / 16], float*
                 ST[(size_t)(16 * m + 4 * g + p) * D + col0 + 16 * nb + j] = S[nb][m][p];
 }
 
+// Interleaved column blocks (fused plan at bf16, two 16-column blocks per
+// wave): in a wave's 32 value columns col0 .. col0 + 31, block nb of lane
+// column j is column col0 + 2 j + nb.  The value columns evolve
+// independently, so any assignment is exact; this one makes the two blocks'
+// elements of a row adjacent, so V and O move as 4-byte pairs (one access per
+// row and lane instead of two) and states as 8-byte pairs.
+template <int D>
+__device__ __forceinline__ void state_load_il(f32x4 (&S)[2][D / 16], const float* __restrict__ S0,
+                                              int col0) {
+    const int lane = lane_id(), j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f32x2 x = S0 ? *reinterpret_cast<const f32x2*>(
+                                     S0 + (size_t)(16 * m + 4 * g + p) * D + col0 + 2 * j)
+                               : f32x2{0.f, 0.f};
+            S[0][m][p] = x[0];
+            S[1][m][p] = x[1];
+        }
+}
+
+template <int D>
+__device__ __forceinline__ void state_store_il(const f32x4 (&S)[2][D / 16], float* __restrict__ ST,
+                                               int col0) {
+    const int lane = lane_id(), j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            *reinterpret_cast<f32x2*>(ST + (size_t)(16 * m + 4 * g + p) * D + col0 + 2 * j) =
+                f32x2{S[0][m][p], S[1][m][p]};
+}
+
+// V of one chunk, rows 4g + p of the lane's column pair (bf16): one word per
+// row, block 0 in the low half.
+struct VPair {
+    uint32_t w[4];
+};
+
+template <int D>
+__device__ __forceinline__ void v_load_il(VPair& V, const bf16* __restrict__ v, const ChunkPos& c,
+                                          int col0) {
+    const int lane = lane_id(), j = lane & 15, g = lane >> 4;
+    const Rsrc rv = chunk_rsrc<D>(v, c, 2);
+    const int rowb = (int)(c.rstride * 2);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) V.w[p] = buf_load<uint32_t>(rv, (4 * g + p) * rowb + (col0 + 2 * j) * 2);
+}
+
+__device__ __forceinline__ void v_widen_il(const VPair& V, f32x4 (&Vf)[2]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        Vf[0][p] = __builtin_bit_cast(float, V.w[p] << 16);
+        Vf[1][p] = __builtin_bit_cast(float, V.w[p] & 0xffff0000u);
+    }
+}
+
+// O of one chunk (both blocks); stores to rows past the chunk's end are dropped.
+template <int D>
+__device__ __forceinline__ void o_store_il(const f32x4 (&O)[2], bf16* __restrict__ o,
+                                           const ChunkPos& c, int col0) {
+    const int lane = lane_id(), j = lane & 15, g = lane >> 4;
+    const Rsrc ro = chunk_rsrc<D>(o, c, 2);
+    const int rowb = (int)(c.rstride * 2);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const bf16x2 x{(bf16)O[0][p], (bf16)O[1][p]};
+        buf_store_u32(ro, (4 * g + p) * rowb + (col0 + 2 * j) * 2, __builtin_bit_cast(uint32_t, x));
+    }
+}
+
 // Workgroup id -> (unit = b*H + h, column tile).  Workgroups are dispatched
 // round-robin over the 8 XCDs; all column tiles of one head get the same
 // id mod 8 so they share an XCD's L2.

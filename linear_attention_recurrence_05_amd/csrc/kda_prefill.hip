@@ -197,24 +197,38 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
         return;
     }
     // ---------------------------------------------------- consumer wave
+    // bf16, NB = 2: the two blocks interleave (block nb, lane column j =
+    // column col0 + 2 j + nb), so V, O and the states move as column pairs.
+    // (fp32 keeps separate blocks: built interleaved, its output stores came
+    // out wrong -- the compiler stored row 4g's value for all four rows.)
+    constexpr bool IL = NB == 2 && std::is_same<E, bf16>::value;
     const int col0 = ct * (NCW * NB * 16) + cw * NB * 16;
     f32x4 S[NB][D / 16];
     constexpr int ES = (int)sizeof(E);
-    u32x4 Vc[NPROD][NB], Vn[NPROD][NB];
-    state_load<D, NB>(S, io.in_at(b, h, H, D), col0);
+    struct VBlocks {
+        u32x4 x[NB];
+    };
+    using VRaw = typename std::conditional<IL, VPair, VBlocks>::type;
+    VRaw Vc[NPROD], Vn[NPROD];
+    auto vload = [&](VRaw& V, int n) {
+        if constexpr (IL) v_load_il<D>(V, (const bf16*)v, chunk_pos<D>(b, h, n, T, H), col0);
+        else v_load<D, NB>(V.x, v, ES, chunk_pos<D>(b, h, n, T, H), col0);
+    };
+    if constexpr (IL) state_load_il<D>(S, io.in_at(b, h, H, D), col0);
+    else state_load<D, NB>(S, io.in_at(b, h, H, D), col0);
     if constexpr (!VZ) {
 #pragma unroll
         for (int cc = 0; cc < NPROD; ++cc)
-            if (cc < NC) v_load<D, NB>(Vc[cc], v, ES, chunk_pos<D>(b, h, cc, T, H), col0);
+            if (cc < NC) vload(Vc[cc], cc);
     }
     wg_barrier();
-    int done = NC;
+    [[maybe_unused]] int done = NC;
     for (int m = 0; m < NM; ++m) {
         if constexpr (!VZ) {
 #pragma unroll
             for (int cc = 0; cc < NPROD; ++cc) {
                 const int nn = (m + 1) * NPROD + cc;
-                if (nn < NC) v_load<D, NB>(Vn[cc], v, ES, chunk_pos<D>(b, h, nn, T, H), col0);
+                if (nn < NC) vload(Vn[cc], nn);
             }
         }
 #pragma unroll
@@ -225,30 +239,42 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
                 cops_load<E, D, LdsSrc, WQ>(c, LdsSrc{smem + ((m & 1) * NPROD + cc) * Bk::BYTES});
                 f32x4 O[NB];
                 f32x4 Vf[NB];
+                if constexpr (VZ) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) Vf[nb] = VZ ? zero4() : v_widen<E>(Vc[cc][nb]);
+                    for (int nb = 0; nb < NB; ++nb) Vf[nb] = zero4();
+                } else if constexpr (IL) {
+                    v_widen_il(Vc[cc], Vf);
+                } else {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) Vf[nb] = v_widen<E>(Vc[cc].x[nb]);
+                }
                 if constexpr (CK) {
                     // the state entering chunk n, natural [D][D] layout
                     float* cp = ck.at<D>(b, h, n, H);
-                    const int lane = lane_id(), j = lane & 15, g = lane >> 4;
+                    if constexpr (IL) {
+                        state_store_il<D>(S, cp, col0);
+                    } else {
+                        const int lane = lane_id(), j = lane & 15, g = lane >> 4;
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
+                        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                        for (int mm = 0; mm < D / 16; ++mm)
+                            for (int mm = 0; mm < D / 16; ++mm)
 #pragma unroll
-                            for (int p = 0; p < 4; ++p)
-                                cp[(size_t)(16 * mm + 4 * g + p) * D + col0 + 16 * nb + j] =
-                                    S[nb][mm][p];
+                                for (int p = 0; p < 4; ++p)
+                                    cp[(size_t)(16 * mm + 4 * g + p) * D + col0 + 16 * nb + j] =
+                                        S[nb][mm][p];
+                    }
                 }
                 chunk_step<E, D, NB, WQ>(c, S, Vf, O);
-                if constexpr (WQ) o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n, T, H), col0);
+                if constexpr (WQ) {
+                    if constexpr (IL) o_store_il<D>(O, (bf16*)o, chunk_pos<D>(b, h, n, T, H), col0);
+                    else o_store<E, D, NB>(O, o, chunk_pos<D>(b, h, n, T, H), col0);
+                }
             }
         }
         if constexpr (!VZ) {
 #pragma unroll
-            for (int cc = 0; cc < NPROD; ++cc)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) Vc[cc][nb] = Vn[cc][nb];
+            for (int cc = 0; cc < NPROD; ++cc) Vc[cc] = Vn[cc];
         }
         if constexpr (EX) {
             // exactly zero: every bit but the sign clear (-0 counts as zero)
@@ -274,7 +300,10 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
     if constexpr (EX) {
         if (cw == 0 && lane_id() == 0) lim.out[u] = done;
     }
-    if (io.out) state_store<D, NB>(S, io.out_at(b, h, H, D), col0);
+    if (io.out) {
+        if constexpr (IL) state_store_il<D>(S, io.out_at(b, h, H, D), col0);
+        else state_store<D, NB>(S, io.out_at(b, h, H, D), col0);
+    }
 }
 
 // --------------------------------------------------------------- plans / launchers

@@ -168,7 +168,7 @@ def plan_ok(p, d, dt):
     if not p.startswith("fused:"):
         return True
     n = int(p.split(":")[1])
-    return n <= d and not (dt == "f32" and d == 128 and n > 64)
+    return n <= d
 
 
 @pytest.mark.parametrize("p", PLANS)
