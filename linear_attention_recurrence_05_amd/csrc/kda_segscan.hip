@@ -69,12 +69,15 @@ __global__ __launch_bounds__(256) void seg_fill_kernel(float* __restrict__ ident
 // registers while step r computes.  Writes S_in(r) of every segment to
 // Sin[(b R + r), h] and the end state to S_T[b, h] (if given).  Reads S0
 // (null: zeros) before any write, and only its own columns, so S_T may alias
-// S0.
+// S0.  nch (may be null): chunks the map pass of unit (b R + r) H + h ran
+// before its map was exactly zero; fewer than ncs (the segment's chunks)
+// means M_r = 0, and the step is S <- N_r without reading M_r.
 template <int D>
 __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ M,
                                                       const float* __restrict__ Nst,
                                                       const float* S0, float* __restrict__ Sin,
-                                                      float* S_T, int H, int R) {
+                                                      float* S_T, int H, int R,
+                                                      const int* __restrict__ nch, int ncs) {
     constexpr int CB = 16;                  // value columns per workgroup
     constexpr int OPT = D * CB / 256;       // outputs per thread
     constexpr int MPT = D * D / 256;        // elements of M per thread
@@ -93,8 +96,10 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
         const int c = e / CB, j = e % CB;
         Ss[c][j] = S0 ? S0[(bh * D + c) * D + col0 + j] : 0.0f;
     }
+    // whether M_r is known to be zero (uniform over the workgroup)
+    auto zero_map = [&](int r) { return nch && nch[(b * R + r) * H + h] < ncs; };
     float mreg[MPT];
-    {
+    if (!zero_map(0)) {
         const float* m = state(M, b * R);
 #pragma unroll
         for (int x = 0; x < MPT; ++x) mreg[x] = m[tid + 256 * x];
@@ -107,13 +112,16 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
             const int c = e / CB, j = e % CB;
             sin[(size_t)c * D + col0 + j] = Ss[c][j];
         }
+        const bool zr = zero_map(r);
+        if (!zr) {
 #pragma unroll
-        for (int x = 0; x < MPT; ++x) {
-            const int e = tid + 256 * x;
-            Ms[e / D][e % D] = mreg[x];
+            for (int x = 0; x < MPT; ++x) {
+                const int e = tid + 256 * x;
+                Ms[e / D][e % D] = mreg[x];
+            }
         }
         __syncthreads();
-        if (r + 1 < R) {   // the next map, in flight while this step computes
+        if (r + 1 < R && !zero_map(r + 1)) {   // the next map, in flight while this step computes
             const float* m = state(M, row + 1);
 #pragma unroll
             for (int x = 0; x < MPT; ++x) mreg[x] = m[tid + 256 * x];
@@ -122,10 +130,12 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
         float acc[OPT];
 #pragma unroll
         for (int x = 0; x < OPT; ++x) acc[x] = nr[(size_t)i * D + col0 + j0 + x];
-        for (int c = 0; c < D; ++c) {
-            const float mic = Ms[i][c];
+        if (!zr) {
+            for (int c = 0; c < D; ++c) {
+                const float mic = Ms[i][c];
 #pragma unroll
-            for (int x = 0; x < OPT; ++x) acc[x] += mic * Ss[c][j0 + x];
+                for (int x = 0; x < OPT; ++x) acc[x] += mic * Ss[c][j0 + x];
+            }
         }
         __syncthreads();   // every thread has read Ss and Ms
 #pragma unroll
@@ -233,12 +243,14 @@ static hipError_t start_states(const PrefillArgs& a, int R, const SegLayout& L, 
         if ((e = launch_prefill(pn, L.inner, inner, stream)) != hipSuccess) return e;
     }
     const unsigned grid = (unsigned)((size_t)a.B * a.H * (a.d / 16));
+    const int* nch = state_only ? (const int*)(w + L.nch) : nullptr;
+    const int ncs = (Ts + kChunk - 1) / kChunk;
     if (a.d == 128)
         hipLaunchKernelGGL(segscan_kernel<128>, dim3(grid), dim3(256), 0, stream, M, N, s_in0, Sin,
-                           a.S.out, a.H, R);
+                           a.S.out, a.H, R, nch, ncs);
     else
         hipLaunchKernelGGL(segscan_kernel<32>, dim3(grid), dim3(256), 0, stream, M, N, s_in0, Sin,
-                           a.S.out, a.H, R);
+                           a.S.out, a.H, R, nch, ncs);
     return hipGetLastError();
 }
 
