@@ -156,6 +156,36 @@ def test_out_of_range_slot_is_skipped(p):
     assert torch.equal(pool[int(s_in[0])], pool1[int(s_in[0])])
 
 
+def test_decode_paged_d128_pairs_with_skipped_units():
+    """At d = 128 one workgroup takes two consecutive (b, h) units. With an
+    odd head count the pairs straddle sequences, so a live unit shares its
+    workgroup with a skipped one (negative or out-of-range slot) and the last
+    workgroup holds a single unit; the live units still match the oracle and
+    the skipped ones leave their outputs and pool rows as they were."""
+    dev = need_gpu()
+    B, H, d, n_slots = 5, 3, 128, 9
+    pool, slots, _ = pool_and_slots(B, H, d, n_slots, dev, seed=31)
+    gen, A, _ = decode_state(B, H, d, d, seed=32, device=dev)
+    x = decode_step_inputs(gen, B, H, d, d, torch.bfloat16, dev)
+    s = slots.clone()
+    s[1] = -1
+    s[3] = n_slots
+    live = [0, 2, 4]
+    pool0 = pool.clone()
+    S_ref = pool[slots[live].long()].double().cpu().numpy().copy()
+    o = torch.full((B, H, d), 7.0, dtype=torch.bfloat16, device=dev)
+    kda.kda_decode_step_paged(x["q"], x["k"], x["v"], x["z"], x["beta"], A, -5.0, pool, s, o)
+    torch.cuda.synchronize()
+    sub = {kk: x[kk][live] for kk in ("q", "k", "v", "z", "beta")}
+    o_ref = oracle.decode(sub["q"], sub["k"], sub["v"], sub["z"], sub["beta"], A, -5.0, S_ref)
+    eo, es = rel_err(o[live], o_ref), rel_err(pool[slots[live].long()], S_ref)
+    say(f"paged decode, d=128, skipped units in shared workgroups: o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[torch.bfloat16] and es < 1e-4
+    assert torch.all(o[1] == 7.0) and torch.all(o[3] == 7.0)
+    untouched = untouched_rows(n_slots, slots[live])
+    assert torch.equal(pool[untouched], pool0[untouched])
+
+
 def test_decode_and_verify_paged_against_oracle():
     """Paged decode (two steps in place) and the paged 5-token verify step
     (snapshot kept) against the fp64 oracle directly, bf16 at d = 128."""
