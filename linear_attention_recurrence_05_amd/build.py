@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_pair.hip", "kda_backward.hip",
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_pair.hip", "kda_ring.hip", "kda_backward.hip",
            "kda_bwd_chunk.hip", "kda_segscan.hip"]
 ARCH = "gfx950"
 

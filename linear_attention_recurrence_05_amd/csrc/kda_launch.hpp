@@ -156,6 +156,7 @@ hipError_t launch_bwd_chunk(const BackwardArgs& a, const float* ckpt, char* fac,
 enum class Plan {
     kFused,   // gate + intra + inter in one launch; one workgroup per (b, h, column tile)
     kSplit,   // intra kernel over all chunk pairs -> workspace, then inter kernel
+    kRing,    // pair producers and state chains in one launch, pairs passed through L2
 };
 
 struct PlanInfo {
@@ -191,6 +192,13 @@ hipError_t launch_tokens(const TokensArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
 // Split plan: pair intra kernel -> workspace -> pair inter kernel, per segment.
 hipError_t launch_split(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream);
+// Ring plan (bf16, d = 128, at most one workgroup per CU: B * H * 8 <= CUs
+// rounded to whole XCD groups): whether it runs on the current device, its
+// workspace (flags and an L2-resident ring of pair blocks per unit), and the
+// launch (a flag fill, then the ring kernel).  Needs o and v; no chunk limits.
+bool ring_ok(int B, int H, int d, bool is_bf16);
+size_t ring_ws_bytes(int B, int H, int d, bool is_bf16);
+hipError_t launch_ring(const PrefillArgs& a, void* ws, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, void* ws, hipStream_t stream);
 
 // Segment-scan prefill: the T tokens of each sequence as R segments of T / R

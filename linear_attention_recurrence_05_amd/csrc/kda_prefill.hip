@@ -310,13 +310,19 @@ __global__ __launch_bounds__(512) void fused_kernel(const E* __restrict__ q, con
 
 
 // Plan override for tests and tuning: KDA_PREFILL_PLAN = "fused:<ncol>"
-// (ncol in {16, 32, 64, 128}, at most d) or "split".  Unset or anything
-// else: chosen from the sizes.
-static bool plan_override(int d, bool is_bf16, PlanInfo& p) {
+// (ncol in {16, 32, 64, 128}, at most d), "split", "split:<ncol>:<nb>" or
+// "ring" (where it runs).  Unset or anything else: chosen from the sizes.
+static bool plan_override(int B, int H, int d, bool is_bf16, PlanInfo& p) {
     const char* env = std::getenv("KDA_PREFILL_PLAN");
     if (!env) return false;
     if (std::strcmp(env, "split") == 0) {
         p.plan = Plan::kSplit;
+        return true;
+    }
+    if (std::strcmp(env, "ring") == 0 && ring_ok(B, H, d, is_bf16)) {
+        p.plan = Plan::kRing;
+        p.ncol = 16;
+        p.ws_bytes = ring_ws_bytes(B, H, d, is_bf16);
         return true;
     }
     if (std::strncmp(env, "split:", 6) == 0) {
@@ -348,8 +354,8 @@ PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16) {
     p.plan = Plan::kSplit;
     p.ncol = 0;
     p.nb = 1;
-    const bool forced = plan_override(d, is_bf16, p);
-    if (forced && p.plan == Plan::kFused) return p;
+    const bool forced = plan_override(B, H, d, is_bf16, p);
+    if (forced && (p.plan == Plan::kFused || p.plan == Plan::kRing)) return p;
     if (!forced && units >= 128) {
         p.plan = Plan::kFused;
         p.ncol = units >= 256 ? d : (d >= 64 ? 64 : d);
@@ -442,6 +448,7 @@ bool prefill_state_only_ok(const PlanInfo& p, int d) {
 
 hipError_t launch_prefill(const PrefillArgs& a, const PlanInfo& p, void* ws, hipStream_t stream) {
     if (p.plan == Plan::kSplit) return launch_split(a, p, ws, stream);
+    if (p.plan == Plan::kRing) return launch_ring(a, ws, stream);
     if (a.is_bf16)
         return a.d == 128 ? launch_prefill_t<bf16, 128>(a, p, ws, stream)
                           : launch_prefill_t<bf16, 32>(a, p, ws, stream);

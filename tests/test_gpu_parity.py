@@ -149,7 +149,7 @@ def test_intra_chunk(d, dt):
 # ------------------------------------------------------------------ prefill, small shapes
 
 PLANS = ["auto", "split", "split:16:1", "split:32:1", "split:64:1", "split:32:2", "split:64:2",
-         "fused:16", "fused:32", "fused:64", "fused:128"]
+         "fused:16", "fused:32", "fused:64", "fused:128", "ring"]
 SHAPES = [(2, 100, 3, True), (1, 1, 2, False), (1, 15, 1, True), (1, 17, 2, False),
           (3, 33, 1, True), (1, 64, 2, False)]
 
@@ -165,6 +165,8 @@ def plan_ok(p, d, dt):
         if nb == 2:
             return d == 128 and dt == "bf16" and ncw in (1, 2)
         return ncw in (1, 2) or (ncw == 4 and d == 128 and dt == "bf16")
+    if p == "ring":
+        return d == 128 and dt == "bf16"
     if not p.startswith("fused:"):
         return True
     n = int(p.split(":")[1])

@@ -10,7 +10,7 @@ from linear_attention_recurrence_05_amd.inputs import decode_step_inputs, prefil
 from gpu_common import TOL, need_gpu, plan, rel_err, say
 
 pytestmark = pytest.mark.gpu
-PLANS = ["split", "fused:16", "fused:64"]
+PLANS = ["split", "fused:16", "fused:64", "ring"]
 
 
 def run(x, S0="keep"):
