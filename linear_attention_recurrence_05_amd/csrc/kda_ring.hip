@@ -14,16 +14,17 @@
 // workgroup checks the XCD it runs on).  The grid is at most one workgroup
 // per CU and every workgroup fits a CU by itself, so the whole grid is
 // resident at once, which the waits between workgroups need.  A workgroup:
-//   waves 0..3  producers: pairs p = tile + 8 (w + 4 j) of the unit, each
+//   waves 0..2  producers: pairs p = tile + 8 (w + 3 j) of the unit, each
 //               built in the wave's LDS as a whole pair block, then copied
 //               to ring slot p mod R of the unit (global memory that stays
 //               in the XCD's L2) once every tile has taken pair p - R;
-//   wave 4      the chain of the tile's 16 columns (x, U, state update);
-//   wave 5      the outputs of those columns, from the state at the pair's
+//   wave 3      the chain of the tile's 16 columns (x, U, state update),
+//               alone on its SIMD;
+//   wave 4      the outputs of those columns, from the state at the pair's
 //               start (bf16, as the chain packs it for its own products)
 //               and [U_a; U_b], both handed over by the chain in LDS;
-//   wave 6      the gate: forwards the ring's ready flags to LDS for waves
-//               4 and 5, publishes their progress, and passes the slowest
+//   wave 5      the gate: forwards the ring's ready flags to LDS for waves
+//               3 and 4, publishes their progress, and passes the slowest
 //               tile's progress to this workgroup's producers (only the gate
 //               polls flags in L2; every other wait is on LDS).
 // The chain and output waves load their operands of a pair from the ring
@@ -47,11 +48,13 @@ struct RingCfg {
     using P = PBlk<E, D>;
     using Sg = PStageFull<E, D>;
     static constexpr int NCT = D / 16;             // 16-column tiles per unit
-    static constexpr int NPW = 4;                  // producer waves
+    // waves go to the four SIMDs in turn: three producers (SIMDs 0-2), the
+    // chain alone on SIMD 3, the output wave and the gate beside producers
+    static constexpr int NPW = 3;                  // producer waves
     static constexpr int WCH = NPW, WOUT = NPW + 1, WGATE = NPW + 2;
     static constexpr int THREADS = (NPW + 3) * kWave;
     static constexpr int R = 16;                   // ring slots per unit
-    static constexpr int NU = 2;                   // entries chain -> output wave
+    static constexpr int NU = 4;                   // entries chain -> output wave
     // an entry: [U_a; U_b] (bf16x8 per lane), then the packed state (NSLOT
     // bf16x8 per lane)
     static constexpr int UBYTES = kWave * 16 * (1 + P::NSLOT);
@@ -159,7 +162,7 @@ __device__ __forceinline__ void ring_load_out(POps<E, D>& c, Rsrc r, int base) {
 // 16x16x16 product (lane (r, g) holds row r, columns 4g .. 4g + 3, of each
 // chunk); rows past T read 0.
 template <int D>
-__device__ __forceinline__ void ring_load_v(const bf16* __restrict__ v, int b, int h, int T, int H,
+__device__ __forceinline__ void ring_load_v(const bf16* v, int b, int h, int T, int H,
                                             int col0, int s, u32x2& va, u32x2& vb) {
     const int t0 = 2 * s * kChunk;
     const int Lr = min(2 * kChunk, T - t0);
@@ -181,12 +184,28 @@ __device__ __forceinline__ bool lds_wait_ge(const int* flag, int target, bool li
     return ok;
 }
 
+// The same with the last value read kept in `seen`: no LDS access while
+// seen >= target (flags only grow).  The workgroup's give-up flag is read
+// with every read of the flag, so a give-up is seen no later than the next
+// wait that has to read.
+__device__ __forceinline__ bool lds_wait_seen(const int* flag, int target, int& seen, bool live,
+                                              const int* bad, bool& poisoned) {
+    if (seen >= target) return live;
+    if (live) live = spin_until_ge(flag, target);
+    seen = live ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0x7fffffff;
+    poisoned = poisoned || !live ||
+               __hip_atomic_load(bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    pin_issued();
+    return live;
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
-    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const E* __restrict__ z, const float* __restrict__ beta, const float* __restrict__ A,
-    float g_min, StateIO io, E* __restrict__ o, char* __restrict__ ring, int* __restrict__ flags,
-    int B, int T, int H) {
+    const E* q, const E* k, const E* v, const E* z, const float* beta, const float* A, float g_min,
+    StateIO io, E* o, char* ring, int* flags, int B, int T, int H) {
+    // (no __restrict__: loads through a restrict pointer may move across the
+    // compiler fences that keep each load group in its place in a step, and
+    // the waits for a pair's operands count on that order)
     using P = PBlk<E, D>;
     using Cfg = RingCfg<E, D>;
     using Sg = PStageFull<E, D>;
@@ -331,24 +350,35 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
 
     if (w == Cfg::WCH) {
         // -------------------------------------------------------- chain
-        // A step issues the next pair's loads while its own products run:
-        // Kt operands and V right after the x products, the rest right
-        // after the state update.  The last step reloads its own pair, so
-        // every path issues the same loads and a wait for this pair's
-        // operands never includes the next pair's.
+        // A step issues all of the next pair's loads first, so they have a
+        // whole step to arrive (an L2 access takes about as long as a step
+        // takes to compute).  The last step reloads its own pair, so every
+        // path issues the same loads in the same order and a wait for this
+        // pair's operands never includes the next pair's.
         POps<E, D> c0, c1;
         u32x2 va0, vb0, va1, vb1;
-        bool live = lds_wait_ge(&lready, 0, true);
+        int seen_ready = -1, seen_udone = -1;
+        bool bad = __hip_atomic_load(&lbad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+        bool live = lds_wait_seen(&lready, 0, seen_ready, true, &lbad, bad);
+        // (the same groups in the same order as a step issues them)
         ring_load_chain_k<E, D>(c0, rring, 0);
         ring_load_v<D>(v, b, h, T, H, col0, 0, va0, vb0);
+        pin_issued();
         ring_load_chain_rest<E, D>(c0, rring, 0);
+        pin_issued();
         auto step = [&](POps<E, D>& c, const u32x2& va, const u32x2& vb, POps<E, D>& cn, u32x2& van,
                         u32x2& vbn, int s) {
             const int sn = s + 1 < NP ? s + 1 : s;
-            live = lds_wait_ge(&lready, sn, live);      // the next pair is in the ring
-            live = lds_wait_ge(&udone, s - NU, live);   // the output wave has read entry s - NU
-            if (!live || __hip_atomic_load(&lbad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
-                poison_state(S[0]);
+            // the next pair is in the ring; the output wave has read entry s - NU
+            live = lds_wait_seen(&lready, sn, seen_ready, live, &lbad, bad);
+            live = lds_wait_seen(&udone, s - NU, seen_udone, live, &lbad, bad);
+            if (bad) poison_state(S[0]);
+            pin_issued();
+            ring_load_chain_k<E, D>(cn, rring, (sn % R) * P::BYTES);
+            ring_load_v<D>(v, b, h, T, H, col0, sn, van, vbn);
+            pin_issued();
+            ring_load_chain_rest<E, D>(cn, rring, (sn % R) * P::BYTES);
+            pin_issued();
             bf16x8* e = reinterpret_cast<bf16x8*>(uring + (s % NU) * Cfg::UBYTES);
             const f32x4 Va = mma_bf16_k16(__builtin_bit_cast(bf16x4, va), ident, zero4());
             const f32x4 Vb = mma_bf16_k16(__builtin_bit_cast(bf16x4, vb), ident, zero4());
@@ -357,39 +387,39 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
             pair_x<E, D, 1>(c, S, sb, xa, xb);
 #pragma unroll
             for (int kk = 0; kk < P::NSLOT; ++kk) e[(1 + kk) * kWave + lane] = sb[0][kk];
-            __builtin_amdgcn_sched_barrier(0);
-            ring_load_chain_k<E, D>(cn, rring, (sn % R) * P::BYTES);
-            ring_load_v<D>(v, b, h, T, H, col0, sn, van, vbn);
-            __builtin_amdgcn_sched_barrier(0);
             const bf16x8 u2 = pair_u<E, D>(c, xa[0], xb[0], Va, Vb);
             e[lane] = u2;
             asm volatile("" ::: "memory");
             __hip_atomic_store(&uready, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             pair_supdate<E, D>(c, S[0], u2);
-            __builtin_amdgcn_sched_barrier(0);
-            ring_load_chain_rest<E, D>(cn, rring, (sn % R) * P::BYTES);
             // the pair's operands are all in registers (their last use
             // waited for them): release the slot
             pin_issued();
             __hip_atomic_store(&ldone[0], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
-        for (int s = 0; s < NP; s += 2) {
+        // whole pairs of steps in the loop, an odd last step after it: every
+        // path into the loop head then has the same loads in flight
+        int s = 0;
+        for (; s + 1 < NP; s += 2) {
             step(c0, va0, vb0, c1, va1, vb1, s);
-            if (s + 1 < NP) step(c1, va1, vb1, c0, va0, vb0, s + 1);
+            step(c1, va1, vb1, c0, va0, vb0, s + 1);
         }
+        if (s < NP) step(c0, va0, vb0, c1, va1, vb1, s);
         if (io.out) state_store<D, 1>(S, io.out_at(b, h, H, D), col0);
         return;
     }
 
     // ------------------------------------------------------------ outputs
     POps<E, D> c0, c1;
-    bool live = lds_wait_ge(&lready, 0, true);
+    int seen_ready = -1, seen_u = -1;
+    bool bad = __hip_atomic_load(&lbad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    bool live = lds_wait_seen(&lready, 0, seen_ready, true, &lbad, bad);
     ring_load_out<E, D>(c0, rring, 0);
     auto step = [&](POps<E, D>& c, POps<E, D>& cn, int s) {
         const int sn = s + 1 < NP ? s + 1 : s;   // as in the chain
-        live = lds_wait_ge(&lready, sn, live);
+        live = lds_wait_seen(&lready, sn, seen_ready, live, &lbad, bad);
         ring_load_out<E, D>(cn, rring, (sn % R) * P::BYTES);
-        live = lds_wait_ge(&uready, s, live);
+        live = lds_wait_seen(&uready, s, seen_u, live, &lbad, bad);
         const bf16x8* e = reinterpret_cast<const bf16x8*>(uring + (s % NU) * Cfg::UBYTES);
         const bf16x8 u2 = e[lane];
         bf16x8 sb[P::NSLOT];
@@ -397,7 +427,7 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
         for (int kk = 0; kk < P::NSLOT; ++kk) sb[kk] = e[(1 + kk) * kWave + lane];
         f32x4 Oa, Ob;
         pair_out<E, D>(c, sb, u2, Oa, Ob);
-        if (!live || __hip_atomic_load(&lbad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
+        if (bad) {
             const float nan = __builtin_bit_cast(float, kNaNWord);
             Oa = Ob = f32x4{nan, nan, nan, nan};
         }
@@ -417,10 +447,12 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
         buf_store_u32x2(ro, off, acc_rows_bf16(Oa));
         buf_store_u32x2(ro, off + (int)(kChunk * rs * 2), acc_rows_bf16(Ob));
     };
-    for (int s = 0; s < NP; s += 2) {
+    int s = 0;
+    for (; s + 1 < NP; s += 2) {   // as in the chain
         step(c0, c1, s);
-        if (s + 1 < NP) step(c1, c0, s + 1);
+        step(c1, c0, s + 1);
     }
+    if (s < NP) step(c0, c1, s);
 }
 
 // Flags of every unit to -1 (nothing published, nothing taken).
