@@ -194,19 +194,23 @@ def time_prefill(kda, torch, workload, stream, dev, steps, warmup, segments=1, r
         res["ms_per_step_after_write_flush"] = sum(fl_ms) / len(fl_ms)
         res["ms_per_step_warm"] = w0.elapsed_time(w1) / steps
 
+    direct = kda.kda_chunk_prefill_plan(B, T, H, d, d, cfg.dtype)
     plan = (f"segment scan over {segments} segments" if segments > 1
             else f"segment scan over {auto_seg} segments (chosen by kda_chunk_prefill)"
-            if auto_seg > 1 else ("split" if nb else "fused"))
+            if auto_seg > 1 else direct)
     alg_b = prefill_alg_bytes(B, T, H, d, with_s0=x["S0"] is not None)
     alg_f = prefill_alg_flops(B, T, H, d)
     gbs = alg_b / (ms * 1e-3) / 1e9
     tflops = alg_f / (ms * 1e-3) / 1e12
     key = f"prefill_{workload}_pass" if g_min is None else f"prefill_{workload}_gmin{g_min:g}_pass"
-    kernel = ("segment-scan prefill pass (identity_kernel, two state-only fused_kernel map "
-              "passes, segscan_kernel, one full fused_kernel pass)" if n_seg > 1
-              else "prefill pass (pair_intra_kernel + pair_roles_kernel)" if nb
+    kernel = ("segment-scan prefill pass (seg_fill_kernel, the state-only fused_kernel map pass, "
+              "the zero-start fused_kernel pass, segscan_kernel, the fused_kernel redo)" if n_seg > 1
+              else "prefill pass (ring_flags_init + pair_ring_kernel)" if direct == "ring"
+              else "prefill pass (pair_intra_kernel + pair_roles_kernel)" if direct == "split"
               else "prefill pass (fused_kernel)")
-    tkey = f"{key}_bytes_{'segscan' if n_seg > 1 else 'split' if nb else 'fused'}"
+    kind = ("segscan" if n_seg > 1 else "ring" if direct == "ring" else "split" if direct == "split"
+            else "fused")
+    tkey = f"{key}_bytes_{kind}"
     res.update({
         "value": B * T / (ms * 1e-3), "unit": "tokens/s",
         "config": {"workload": f"{cfg.name}_prefill_B{B}_H{H}_T{T}_d{d}_bf16", "B": B, "T": T,

@@ -112,6 +112,16 @@ size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v,
  * 0 for arguments kda_chunk_prefill would reject. */
 int kda_chunk_prefill_segments(int B, int T, int H, int d_k, int d_v, kda_dtype dt);
 
+/* The plan kda_chunk_prefill runs for these sizes on the current device, as
+ * a static string: "segment scan" (the segment scan above), "ring" (pair
+ * producers and state chains in one launch, pairs passed through an XCD's L2:
+ * bf16, d = 128, B * H * 8 workgroups fit the device's CUs at one each),
+ * "split" (pair blocks through the workspace) or "fused:<columns>" (one
+ * launch per 16-token chunk chain, no workspace).  "" for arguments
+ * kda_chunk_prefill would reject.  Informational: results do not depend on
+ * the plan beyond rounding. */
+const char *kda_chunk_prefill_plan(int B, int T, int H, int d_k, int d_v, kda_dtype dt);
+
 /* Chunkwise prefill over T tokens (any T >= 1; chunks of KDA_CHUNK tokens
  * start at t = 0 and the last may be short).  Computes o for every token and,
  * if S_T != NULL, the final state.

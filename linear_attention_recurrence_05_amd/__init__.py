@@ -19,6 +19,7 @@ Functions named like the C entry points take torch tensors in the layouts
     kda_intra_chunk(q, k, z, beta, A, g_min, Tm, Aqk, gamma, stream)
     kda_chunk_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype)
     kda_chunk_prefill_segments(B, T, H, d_k, d_v, dtype)
+    kda_chunk_prefill_plan(B, T, H, d_k, d_v, dtype)
     kda_chunk_backward(q, k, v, z, beta, A, g_min, S0, dO, dS_T, dq, dk, dv, dz, dbeta, dA,
                        dS0, workspace, stream)
     kda_chunk_backward_workspace_bytes(B, T, H, d_k, d_v, dtype)
@@ -37,8 +38,8 @@ from ._lib import (KDA_BF16, KDA_CHUNK, KDA_F32, KDA_MAX_DECODE_TOKENS, KdaError
                    kda_chunk_backward_workspace_bytes, kda_chunk_prefill_segmented,
                    kda_chunk_prefill_segmented_workspace_bytes,
                    kda_chunk_prefill, kda_chunk_prefill_noalloc, kda_chunk_prefill_paged,
-                   kda_chunk_prefill_paged_workspace_bytes, kda_chunk_prefill_segments,
-                   kda_chunk_prefill_workspace_bytes,
+                   kda_chunk_prefill_paged_workspace_bytes, kda_chunk_prefill_plan,
+                   kda_chunk_prefill_segments, kda_chunk_prefill_workspace_bytes,
                    kda_decode_step, kda_decode_step_paged, kda_decode_tokens,
                    kda_decode_tokens_paged, kda_gate_chunk_cumsum, kda_intra_chunk, lib,
                    library_path, status_string)
@@ -48,7 +49,7 @@ __all__ = ["KDA_BF16", "KDA_CHUNK", "KDA_F32", "KDA_MAX_DECODE_TOKENS", "KdaErro
            "chunk_prefill_segmented", "kda_chunk_backward", "kda_chunk_backward_workspace_bytes",
            "kda_chunk_prefill_segmented", "kda_chunk_prefill_segmented_workspace_bytes", "decode_step", "decode_tokens",
            "kda_chunk_prefill", "kda_chunk_prefill_noalloc", "kda_chunk_prefill_paged", "kda_chunk_prefill_paged_workspace_bytes",
-           "kda_chunk_prefill_segments",
+           "kda_chunk_prefill_plan", "kda_chunk_prefill_segments",
            "kda_chunk_prefill_workspace_bytes",
            "kda_decode_step", "kda_decode_step_paged", "kda_decode_tokens",
            "kda_decode_tokens_paged", "kda_gate_chunk_cumsum", "kda_intra_chunk", "lib",

@@ -39,6 +39,7 @@ _SIGNATURES = {
     "kda_last_error": ([], ctypes.c_char_p),
     "kda_chunk_prefill_workspace_bytes": ([_i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "kda_chunk_prefill_segments": ([_i, _i, _i, _i, _i, _i], _i),
+    "kda_chunk_prefill_plan": ([_i, _i, _i, _i, _i, _i], ctypes.c_char_p),
     "kda_chunk_prefill": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6
                           + [_vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "kda_chunk_prefill_noalloc": ([_vp] * 6 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 6
@@ -196,6 +197,12 @@ def kda_chunk_prefill_segments(B, T, H, d_k, d_v, dtype) -> int:
     """C entry point kda_chunk_prefill_segments (1: a direct plan)."""
     code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
     return int(lib().kda_chunk_prefill_segments(B, T, H, d_k, d_v, code))
+
+
+def kda_chunk_prefill_plan(B, T, H, d_k, d_v, dtype) -> str:
+    """C entry point kda_chunk_prefill_plan (the plan's name; "" if rejected)."""
+    code = dtype if isinstance(dtype, int) else (KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+    return lib().kda_chunk_prefill_plan(B, T, H, d_k, d_v, code).decode()
 
 
 def kda_chunk_prefill(q, k, v, z, beta, A, g_min, S0, o, S_T, workspace=None, stream=None):

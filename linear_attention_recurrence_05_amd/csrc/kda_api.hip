@@ -170,6 +170,21 @@ int kda_chunk_prefill_segments(int B, int T, int H, int d_k, int d_v, kda_dtype 
     return kda::auto_segments(B, T, H, d_k, dt == KDA_BF16);
 }
 
+const char* kda_chunk_prefill_plan(int B, int T, int H, int d_k, int d_v, kda_dtype dt) {
+    size_t a, b;
+    if (check_common(d_k, d_v, dt, -5.0f) != KDA_OK || check_shape(B, T, H, d_k, a, b) != KDA_OK) return "";
+    if (kda::auto_segments(B, T, H, d_k, dt == KDA_BF16) > 1) return "segment scan";
+    const kda::PlanInfo p = kda::choose_plan(B, T, H, d_k, dt == KDA_BF16);
+    if (p.plan == kda::Plan::kRing) return "ring";
+    if (p.plan == kda::Plan::kSplit) return "split";
+    switch (p.ncol) {
+        case 16: return "fused:16";
+        case 32: return "fused:32";
+        case 64: return "fused:64";
+        default: return "fused:128";
+    }
+}
+
 }  // extern "C"
 
 namespace {

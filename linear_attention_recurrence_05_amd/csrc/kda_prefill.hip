@@ -356,6 +356,14 @@ PlanInfo choose_plan(int B, int T, int H, int d, bool is_bf16) {
     p.nb = 1;
     const bool forced = plan_override(B, H, d, is_bf16, p);
     if (forced && (p.plan == Plan::kFused || p.plan == Plan::kRing)) return p;
+    if (!forced && ring_ok(B, H, d, is_bf16)) {
+        // few sequence-heads: every unit gets a CU per 16-column tile and
+        // its pair blocks pass from producers to chains through L2
+        p.plan = Plan::kRing;
+        p.ncol = 16;
+        p.ws_bytes = ring_ws_bytes(B, H, d, is_bf16);
+        return p;
+    }
     if (!forced && units >= 128) {
         p.plan = Plan::kFused;
         p.ncol = units >= 256 ? d : (d >= 64 ? 64 : d);

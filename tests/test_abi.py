@@ -512,6 +512,21 @@ def test_segmented_workspace_query():
                                                            kda.KDA_BF16) == 0
 
 
+def test_prefill_plan_names():
+    """kda_chunk_prefill_plan names the plan the dense entry point runs (host
+    logic; without a GPU no device reports CUs, so the ring plan is never
+    chosen here)."""
+    f = kda.kda_chunk_prefill_plan
+    bf, f32 = kda.KDA_BF16, kda.KDA_F32
+    assert f(1, 1048576, 32, 128, 128, bf) == "segment scan"
+    assert f(8, 32768, 32, 128, 128, bf) == "fused:128"    # 256 units
+    assert f(1, 4096, 128, 128, 128, bf) == "fused:64"     # 128 units
+    assert f(1, 4096, 32, 128, 128, bf) in ("split", "ring")
+    assert f(1, 4096, 32, 32, 32, f32) == "split"          # the ring plan is bf16 at d = 128
+    assert f(0, 4096, 32, 128, 128, bf) == ""              # rejected sizes
+    assert f(1, 4096, 32, 64, 64, bf) == ""
+
+
 def test_prefill_segment_choice():
     """Which sizes kda_chunk_prefill runs as a segment scan (host logic)."""
     f = kda.kda_chunk_prefill_segments

@@ -1,8 +1,8 @@
 """kda_chunk_prefill_noalloc (the prefill without a workspace argument: its
 scratch is a static per-GPU array) against kda_chunk_prefill with a caller
 workspace, through the C ABI: equal results on consecutive calls of shrinking
-size and of each plan that uses scratch (the segment scan, the split plan), and
-sizes beyond the scratch rejected before any launch."""
+size and of each plan that uses scratch (the segment scan, the ring plan, the
+split plan), and sizes beyond the scratch rejected before any launch."""
 from __future__ import annotations
 
 import pytest
@@ -30,7 +30,8 @@ def _both(x):
 def test_noalloc_equals_workspace_call_on_consecutive_calls():
     dev = need_gpu()
     # (B, T, H, d, dtype, S0 std): the segment scan (67 MB of scratch), the
-    # split plan (115 MB), a smaller split-plan call, a fused-plan call (none)
+    # ring plan (14 MB; the split plan's 115 MB where no ring fits the
+    # device), a smaller split-plan call (fp32), a fused-plan call (none)
     cases = [(1, 65536, 32, 128, torch.bfloat16, 0.1), (1, 4096, 32, 128, torch.bfloat16, None),
              (2, 100, 3, 32, torch.float32, 0.1), (8, 40, 32, 128, torch.bfloat16, 0.1)]
     sizes = []
@@ -48,10 +49,12 @@ def test_noalloc_equals_workspace_call_on_consecutive_calls():
 
 def test_noalloc_rejects_sizes_beyond_the_scratch():
     dev = need_gpu()
+    # fp32 runs the split plan, whose pair blocks of 16,384 tokens x 32 heads
+    # exceed the scratch
     B, T, H, d = 1, 16384, 32, 128
-    need = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, torch.bfloat16)
+    need = kda.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, torch.float32)
     assert need > (256 << 20)
-    x = prefill_inputs(B, T, H, d, d, torch.bfloat16, seed=310, device=dev)
+    x = prefill_inputs(B, T, H, d, d, torch.float32, seed=310, device=dev)
     o = torch.zeros_like(x["v"])
     with pytest.raises(kda.KdaError, match="KDA_ERR_WORKSPACE_TOO_SMALL"):
         kda.kda_chunk_prefill_noalloc(x["q"], x["k"], x["v"], x["z"], x["beta"], x["A"],
