@@ -53,7 +53,12 @@ struct RingCfg {
     static constexpr int NPW = 3;                  // producer waves
     static constexpr int WCH = NPW, WOUT = NPW + 1, WGATE = NPW + 2;
     static constexpr int THREADS = (NPW + 3) * kWave;
-    static constexpr int R = 16;                   // ring slots per unit
+    // ring slots per unit: 8 keep a unit's blocks (4 units per XCD, 0.9 MB)
+    // in the XCD's 4 MB L2 between a slot's refills; with 12 or 16 slots
+    // the streaming inputs and outputs evict most blocks while dirty and
+    // they are written back to HBM (1.7x and 1.9x the algorithmic bytes of
+    // a pass at B1 H32 T4096, against 1.34x with 8, which is 4% slower)
+    static constexpr int R = 8;
     static constexpr int NU = 4;                   // entries chain -> output wave
     // an entry: [U_a; U_b] (bf16x8 per lane), then the packed state (NSLOT
     // bf16x8 per lane)
