@@ -187,7 +187,11 @@ __device__ __forceinline__ void prod_load(ProdIn<E, D>& in, const E* __restrict_
     in.L = c.L;
     // Rows past the chunk's end lie outside the buffers and read as zero.
     const Rsrc rq = chunk_rsrc<D>(q, c, ES), rk = chunk_rsrc<D>(k, c, ES), rz = chunk_rsrc<D>(z, c, ES);
-    const int rowb = (int)(c.rstride * ES);
+    // The row stride passes through an empty asm so that the 16 row offsets
+    // are formed at each call rather than hoisted out of a producer's loop,
+    // where they would hold 16 VGPRs for the whole loop.
+    int rowb = (int)(c.rstride * ES);
+    asm volatile("" : "+s"(rowb));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int off = c0 * ES + r * rowb;

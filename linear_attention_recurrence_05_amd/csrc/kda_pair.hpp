@@ -484,13 +484,20 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// No work between the products of a step (the default of the hooks below).
+struct NoHook {
+    __device__ void operator()(int) const {}
+};
+
 // The first products of a pair (bf16): S packed once, x_a = Kt_a S and
 // x_b = (Kt_b Diag(gam_a)) S.  They need only the operands read one pair
 // ahead, so the wave issues them before waiting for this pair's other reads.
-template <typename E, int D, int NB>
+// hook(s) runs after the products of A-row slot s (of the last column
+// block): a caller can issue other work between them.
+template <typename E, int D, int NB, typename Hook = NoHook>
 __device__ __forceinline__ void pair_x(const POps<E, D>& c, const f32x4 (&S)[NB][D / 16],
                                        bf16x8 (&sb)[NB][PBlk<E, D>::NSLOT], f32x4 (&xa)[NB],
-                                       f32x4 (&xb)[NB]) {
+                                       f32x4 (&xb)[NB], Hook hook = Hook{}) {
     using P = PBlk<E, D>;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -501,6 +508,7 @@ __device__ __forceinline__ void pair_x(const POps<E, D>& c, const f32x4 (&S)[NB]
             sb[nb][s] = pack8(S[nb][2 * s], S[nb][2 * s + 1]);
             xa[nb] = mma_bf16_k32(c.ka[s], sb[nb][s], xa[nb]);
             xb[nb] = mma_bf16_k32(c.kb[s], sb[nb][s], xb[nb]);
+            if (nb == NB - 1) hook(s);
         }
     }
 }
@@ -520,11 +528,14 @@ __device__ __forceinline__ bf16x8 pair_u(const POps<E, D>& c, const f32x4& xa, c
 }
 
 // S <- Diag(gam_a gam_b) S + [Kd_a Diag(gam_b); Kd_b]^T [U_a; U_b] (bf16).
-template <typename E, int D>
-__device__ __forceinline__ void pair_supdate(const POps<E, D>& c, f32x4 (&S)[D / 16], const bf16x8& u2) {
+// hook(m) runs after the product of row tile m.
+template <typename E, int D, typename Hook = NoHook>
+__device__ __forceinline__ void pair_supdate(const POps<E, D>& c, f32x4 (&S)[D / 16], const bf16x8& u2,
+                                             Hook hook = Hook{}) {
     static_for<0, PBlk<E, D>::MT>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         S[m] = mma_bf16_k32(c.kd2[m], u2, S[m] * gab_tile<m>(c.gv));
+        hook(m);
     });
 }
 

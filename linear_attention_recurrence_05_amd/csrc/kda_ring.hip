@@ -136,16 +136,37 @@ __device__ __forceinline__ void ring_load_chain_k(POps<E, D>& c, Rsrc r, int bas
         c.kb[s] = l2_load<V16<E>>(r, base + P::KB + off);
     }
 }
+// A-row slot s of Kt_a and Kt_b Diag(gam_a).
 template <typename E, int D>
-__device__ __forceinline__ void ring_load_chain_rest(POps<E, D>& c, Rsrc r, int base) {
+__device__ __forceinline__ void ring_load_k_slot(POps<E, D>& c, Rsrc r, int base, int s) {
+    using P = PBlk<E, D>;
+    const int lane = lane_id(), g = lane >> 4, rr = lane & 15;
+    const int off = P::B1::arow_chunk(s, g, rr);
+    c.ka[s] = l2_load<V16<E>>(r, base + P::KA + off);
+    c.kb[s] = l2_load<V16<E>>(r, base + P::KB + off);
+}
+// The 16x16 operands of U_a, U_b and the pair decay.
+template <typename E, int D>
+__device__ __forceinline__ void ring_load_small(POps<E, D>& c, Rsrc r, int base) {
     using P = PBlk<E, D>;
     const int lane = lane_id(), g = lane >> 4, rr = lane & 15;
     c.tma = l2_load<V4<E>>(r, base + P::TMA + lane * P::OPB);
     c.mkb = l2_load<V4<E>>(r, base + P::MKB + lane * P::OPB);
     c.tmb = l2_load<V4<E>>(r, base + P::TMB + lane * P::OPB);
     c.gv = l2_load<f32x2>(r, base + P::GAB + row_vec_offset<D>(g, rr));
+}
+// Row tile m of the state-update operand.
+template <typename E, int D>
+__device__ __forceinline__ void ring_load_kd2(POps<E, D>& c, Rsrc r, int base, int m) {
+    using P = PBlk<E, D>;
+    const int lane = lane_id(), g = lane >> 4, rr = lane & 15;
+    c.kd2[m] = l2_load<V8<E>>(r, base + P::kd2_offset(m, g, rr));
+}
+template <typename E, int D>
+__device__ __forceinline__ void ring_load_chain_rest(POps<E, D>& c, Rsrc r, int base) {
+    ring_load_small<E, D>(c, r, base);
 #pragma unroll
-    for (int m = 0; m < P::MT; ++m) c.kd2[m] = l2_load<V8<E>>(r, base + P::kd2_offset(m, g, rr));
+    for (int m = 0; m < PBlk<E, D>::MT; ++m) ring_load_kd2<E, D>(c, r, base, m);
 }
 
 // Output-wave operands.
@@ -189,19 +210,44 @@ __device__ __forceinline__ bool lds_wait_ge(const int* flag, int target, bool li
     return ok;
 }
 
+// Mark the gate stores to lready and lfree when it gives up: above every
+// pair index, so every wait on them ends, and a consumer that reads it
+// poisons its results.
+constexpr int kGaveUp = 1 << 30;
+
 // The same with the last value read kept in `seen`: no LDS access while
-// seen >= target (flags only grow).  The workgroup's give-up flag is read
-// with every read of the flag, so a give-up is seen no later than the next
-// wait that has to read.
+// seen >= target (flags only grow), and one read per poll otherwise (the
+// value that ends the wait is the one kept).  A wait that gives up, or a
+// value at kGaveUp, sets `poisoned`.
 __device__ __forceinline__ bool lds_wait_seen(const int* flag, int target, int& seen, bool live,
-                                              const int* bad, bool& poisoned) {
+                                              bool& poisoned) {
     if (seen >= target) return live;
-    if (live) live = spin_until_ge(flag, target);
-    seen = live ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0x7fffffff;
-    poisoned = poisoned || !live ||
-               __hip_atomic_load(bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    int v = 0x7fffffff;
+    if (live) {
+        live = false;
+        for (int it = 0; it < kSpinLimit; ++it) {
+            v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (v >= target) {
+                live = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (!live) v = 0x7fffffff;
+    }
+    seen = v;
+    poisoned = poisoned || !live || v >= kGaveUp;
+    // later LDS reads stay after the poll that released them
+    asm volatile("" ::: "memory");
     pin_issued();
     return live;
+}
+
+// A flag value read ahead of its wait (the read's latency then overlaps other
+// work): taken into `seen` as a poll would take it.
+__device__ __forceinline__ void lds_note(int v, int& seen, bool& poisoned) {
+    seen = max(seen, v);
+    poisoned = poisoned || v >= kGaveUp;
 }
 
 template <typename E, int D>
@@ -219,8 +265,9 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
     // lready: last pair the gate saw published; lfree: last pair every tile
     // of the unit has taken (its slot may be refilled); ldone[c]: last pair
     // consumer c (0 chain, 1 output) has taken from the ring; uready / udone:
-    // the entries between chain and output wave; lbad: a wave gave up or
-    // the workgroup is not on its unit's XCD
+    // the entries between chain and output wave; lbad: the workgroup is not
+    // on its unit's XCD (a gate that gives up stores kGaveUp to lready and
+    // lfree instead)
     __shared__ int lready, lfree, ldone[2], uready, udone, lbad;
     int u, ct;
     if (!map_unit(NCT, B * H, u, ct)) return;   // uniform over the workgroup
@@ -334,9 +381,8 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
                 // give up: every wait of the workgroup ends and its results
                 // are poisoned
                 if (lane == 0) {
-                    __hip_atomic_store(&lbad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    __hip_atomic_store(&lfree, NP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    __hip_atomic_store(&lready, NP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_store(&lfree, kGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_store(&lready, kGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 break;
             }
@@ -355,48 +401,67 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
 
     if (w == Cfg::WCH) {
         // -------------------------------------------------------- chain
-        // A step issues all of the next pair's loads first, so they have a
-        // whole step to arrive (an L2 access takes about as long as a step
-        // takes to compute).  The last step reloads its own pair, so every
-        // path issues the same loads in the same order and a wait for this
-        // pair's operands never includes the next pair's.
+        // A step issues the next pair's loads between its own products: the
+        // K rows of the next pair between the x products, the small
+        // operands after them, the state-update operand between the
+        // update's products.  A CU's vector memory pipeline takes a load
+        // every ~20 cycles here, so a burst of them at the top of the step
+        // would hold the wave for most of its MFMA time; spread out, they
+        // drain while the products run, and each still arrives a whole step
+        // before its use (an L2 access takes about as long as a step).  V
+        // comes from HBM and goes first.  The last step reloads its own
+        // pair, so every step issues the same loads in the same order and a
+        // wait for this pair's operands never includes the next pair's.
         POps<E, D> c0, c1;
         u32x2 va0, vb0, va1, vb1;
-        int seen_ready = -1, seen_udone = -1;
+        int seen_ready = -1, seen_udone = -1, ahead_ready = -1, ahead_udone = -1;
         bool bad = __hip_atomic_load(&lbad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
-        bool live = lds_wait_seen(&lready, 0, seen_ready, true, &lbad, bad);
-        // (the same groups in the same order as a step issues them)
-        ring_load_chain_k<E, D>(c0, rring, 0);
+        bool live = lds_wait_seen(&lready, 0, seen_ready, true, bad);
+        // (pair 0's loads in the order a step issues them)
         ring_load_v<D>(v, b, h, T, H, col0, 0, va0, vb0);
-        pin_issued();
+        ring_load_chain_k<E, D>(c0, rring, 0);
         ring_load_chain_rest<E, D>(c0, rring, 0);
         pin_issued();
         auto step = [&](POps<E, D>& c, const u32x2& va, const u32x2& vb, POps<E, D>& cn, u32x2& van,
                         u32x2& vbn, int s) {
             const int sn = s + 1 < NP ? s + 1 : s;
+            const int nbase = (sn % R) * P::BYTES;
             // the next pair is in the ring; the output wave has read entry s - NU
-            live = lds_wait_seen(&lready, sn, seen_ready, live, &lbad, bad);
-            live = lds_wait_seen(&udone, s - NU, seen_udone, live, &lbad, bad);
+            lds_note(ahead_ready, seen_ready, bad);
+            lds_note(ahead_udone, seen_udone, bad);
+            live = lds_wait_seen(&lready, sn, seen_ready, live, bad);
+            live = lds_wait_seen(&udone, s - NU, seen_udone, live, bad);
             if (bad) poison_state(S[0]);
             pin_issued();
-            ring_load_chain_k<E, D>(cn, rring, (sn % R) * P::BYTES);
             ring_load_v<D>(v, b, h, T, H, col0, sn, van, vbn);
-            pin_issued();
-            ring_load_chain_rest<E, D>(cn, rring, (sn % R) * P::BYTES);
             pin_issued();
             bf16x8* e = reinterpret_cast<bf16x8*>(uring + (s % NU) * Cfg::UBYTES);
             const f32x4 Va = mma_bf16_k16(__builtin_bit_cast(bf16x4, va), ident, zero4());
             const f32x4 Vb = mma_bf16_k16(__builtin_bit_cast(bf16x4, vb), ident, zero4());
             bf16x8 sb[1][P::NSLOT];
             f32x4 xa[1], xb[1];
-            pair_x<E, D, 1>(c, S, sb, xa, xb);
+            pair_x<E, D, 1>(c, S, sb, xa, xb, [&](int k) {
+                ring_load_k_slot<E, D>(cn, rring, nbase, k);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // the slot's 2 products
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // then its 2 loads
+            });
+            ring_load_small<E, D>(cn, rring, nbase);
 #pragma unroll
             for (int kk = 0; kk < P::NSLOT; ++kk) e[(1 + kk) * kWave + lane] = sb[0][kk];
             const bf16x8 u2 = pair_u<E, D>(c, xa[0], xb[0], Va, Vb);
             e[lane] = u2;
             asm volatile("" ::: "memory");
             __hip_atomic_store(&uready, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            pair_supdate<E, D>(c, S[0], u2);
+            // both flags of the next step's waits, read while the state
+            // update runs
+            ahead_ready = __hip_atomic_load(&lready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            ahead_udone = __hip_atomic_load(&udone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            pin_issued();
+            pair_supdate<E, D>(c, S[0], u2, [&](int m) {
+                ring_load_kd2<E, D>(cn, rring, nbase, m);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // the tile's product
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // then its load
+            });
             // the pair's operands are all in registers (their last use
             // waited for them): release the slot
             pin_issued();
@@ -418,13 +483,18 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
     POps<E, D> c0, c1;
     int seen_ready = -1, seen_u = -1;
     bool bad = __hip_atomic_load(&lbad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
-    bool live = lds_wait_seen(&lready, 0, seen_ready, true, &lbad, bad);
+    bool live = lds_wait_seen(&lready, 0, seen_ready, true, bad);
     ring_load_out<E, D>(c0, rring, 0);
     auto step = [&](POps<E, D>& c, POps<E, D>& cn, int s) {
         const int sn = s + 1 < NP ? s + 1 : s;   // as in the chain
-        live = lds_wait_seen(&lready, sn, seen_ready, live, &lbad, bad);
+        // The next pair's loads go out once the chain has left its own loads
+        // behind, so the two waves' bursts do not meet in the CU's memory
+        // pipeline.  The chain stores uready = s only after its wait for
+        // pair sn, so pair sn is in the ring by then (a chain whose wait
+        // ended in a give-up poisons the state it passes on, and with it
+        // these outputs).
+        live = lds_wait_seen(&uready, s, seen_u, live, bad);
         ring_load_out<E, D>(cn, rring, (sn % R) * P::BYTES);
-        live = lds_wait_seen(&uready, s, seen_u, live, &lbad, bad);
         const bf16x8* e = reinterpret_cast<const bf16x8*>(uring + (s % NU) * Cfg::UBYTES);
         const bf16x8 u2 = e[lane];
         bf16x8 sb[P::NSLOT];

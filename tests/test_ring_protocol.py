@@ -11,9 +11,11 @@ that polls L2: a round publishes done[tile] (the last pair both of its
 consumers took), reads the R ready flags and the NCT done flags, sets its LDS
 flag lfree to the slowest tile's done and forwards the run of published pairs
 to its LDS flag lready.  The chain and the output wave of a tile read each
-pair from its slot (issuing the loads of the next pair a whole step ahead)
-and hand U and the chain's state over NU LDS entries (flags uready and
-udone); each releases a pair (ldone) after its last use.
+pair from its slot (the chain issues the loads of the next pair a whole step
+ahead, once lready shows it; the output wave once uready shows U of the
+current pair, which the chain stores only after that wait) and hand U and the
+chain's state over NU LDS entries (flags uready and udone); each releases a
+pair (ldone) after its last use.
 
 Steps are the kernel's flag loads and stores and its slot and entry accesses
 in program order.  A slot or entry write is two steps (begun, finished): a
@@ -87,7 +89,8 @@ def _explore(init, successors, finished, limit=3_000_000):
 # tile-local LDS flags
 LREADY, LFREE, LDONE0, LDONE1, UREADY, UDONE, ENTRIES = range(7)
 
-PLANTS = ("no_free_wait", "done_from_chain_only", "any_ready", "no_udone_wait", "own_tile_free")
+PLANTS = ("no_free_wait", "done_from_chain_only", "any_ready", "no_udone_wait", "own_tile_free",
+          "out_loads_first")
 
 
 def ring_model(NP, NCT, NPW, R, NU, plant=None, each_read=True):
@@ -221,15 +224,18 @@ def ring_model(NP, NCT, NPW, R, NU, plant=None, each_read=True):
                 yield go(("top", 0, (issue(slot, 0, who),)))
             return
         kind, s, op = pc
-        if kind == "top":             # the next pair published: its loads
+        if kind == "top" and which == 0:   # chain: the next pair published, entry s mod NU read
             sn = nxt_pair(s)
             if lt[LREADY] < sn:
                 return
-            # (the chain also waits for entry s mod NU to be read)
-            if which == 0 and plant != "no_udone_wait" and lt[UDONE] < s - NU:
+            if plant != "no_udone_wait" and lt[UDONE] < s - NU:
                 return
-            op = op + (issue(slot, sn, who),)
-            yield go(("use", s, op) if which == 0 else ("uw", s, op))
+            yield go(("use", s, op + (issue(slot, sn, who),)))
+        elif kind == "top":           # output wave: U of pair s ready, which the chain stores
+            # only after its own wait for pair s + 1; then the next pair's loads
+            if lt[UREADY] < s and plant != "out_loads_first":
+                return
+            yield go(("rd", s, op + (issue(slot, nxt_pair(s), who),)))
         elif kind == "use":           # pair s's operands used: its loads close
             j = op.index(s)
             op = op[:j] + op[j + 1:]
@@ -241,10 +247,9 @@ def ring_model(NP, NCT, NPW, R, NU, plant=None, each_read=True):
             yield go(("ur", s, op), with_entry(s % NU, s))
         elif kind == "ur":
             yield go(("rel", s, op), _set(tiles, t, _set(lt, UREADY, s)))
-        elif kind == "uw":            # output wave: U and the chain's state ready
-            if lt[UREADY] >= s:
-                yield go(("rd", s, op))
         elif kind == "rd":
+            if lt[UREADY] < s:        # (only a planted early load gets here first)
+                return
             got = lt[ENTRIES][s % NU]
             if got != s:
                 raise Violation(f"{who} read entry {s % NU} for pair {s}: it held {got}")
@@ -299,8 +304,9 @@ def test_model_finds_a_planted_mistake(plant):
     """The model is not vacuous: a producer that does not wait for its slot,
     a gate that publishes its tile's done from the chain alone, takes any
     published flag for the pair it waits for, or frees slots by its own
-    tile's progress, and a chain that does not wait for the output wave to
-    read an entry are each caught as a stale read."""
+    tile's progress, a chain that does not wait for the output wave to read
+    an entry, and an output wave that issues the next pair's loads before U
+    of the current pair is ready are each caught as a stale read."""
     NU = 1 if plant == "no_udone_wait" else 2
     with pytest.raises(Violation, match="held"):
         _explore(*ring_model(4, 2, 1, 2, NU, plant))
