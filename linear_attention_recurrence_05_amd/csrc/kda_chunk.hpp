@@ -372,7 +372,7 @@ struct COps {
     V16<E> kt[B::NSLOT], qt[B::NSLOT];
     V4<E> kd[B::MT];
     V4<E> tm, aq;
-    f32x4 gam[B::MT];
+    f32x2 gv;   // two values of gam per lane: row_tile<m>(gv) is gam of row tile m
 };
 
 // Factor-block sources: LDS (fused kernel) or a buffer over a workspace
@@ -406,8 +406,8 @@ __device__ __forceinline__ void cops_load(COps<E, D>& c, const Src& src) {
 #pragma unroll
     for (int m = 0; m < B::MT; ++m) {
         c.kd[m] = src.template ld<V4<E>>(B::kd_offset(m, g, r));
-        c.gam[m] = src.template ld<f32x4>(B::GAM + (16 * m + 4 * g) * 4);
     }
+    c.gv = src.template ld<f32x2>(B::GAM + row_vec_offset<D>(g, r));
     c.tm = src.template ld<V4<E>>(B::TM + lane * B::OPB);
     if constexpr (WQ) c.aq = src.template ld<V4<E>>(B::AQ + lane * B::OPB);
 }
@@ -483,9 +483,12 @@ __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D
             // take as srcC the result of an MFMA of another shape still in
             // flight (16x16x32 -> 16x16x16 chains read stale srcC on gfx950).
             if constexpr (WQ) o += mma_bf16_k16(c.aq, ub, zero4());  // + Aqk U
-#pragma unroll
-            for (int m = 0; m < B::MT; ++m)
-                S[nb][m] = mma_bf16_k16(c.kd[m], ub, S[nb][m] * c.gam[m]);  // Diag(gam) S + Kd^T U
+            static_for<0, B::MT>([&](auto mc) {   // Diag(gam) S + Kd^T U
+                constexpr int m = decltype(mc)::value;
+                // (each column block its own broadcasts: each folds into its multiply)
+                const f32x4 gm = nb == 0 ? row_tile<m>(c.gv) : row_tile_mov<m>(c.gv);
+                S[nb][m] = mma_bf16_k16(c.kd[m], ub, S[nb][m] * gm);
+            });
         } else {
 #pragma unroll
             for (int m = 0; m < B::MT; ++m)
@@ -502,13 +505,13 @@ __device__ __forceinline__ void chunk_step(const COps<E, D>& c, f32x4 (&S)[NB][D
 #pragma unroll
                 for (int p = 0; p < 4; ++p) o = mma_f32_k4(c.aq[p], u[p], o);
             }
-#pragma unroll
-            for (int m = 0; m < B::MT; ++m) {
-                f32x4 s = S[nb][m] * c.gam[m];
+            static_for<0, B::MT>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                f32x4 s = S[nb][m] * row_tile<m>(c.gv);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) s = mma_f32_k4(c.kd[m][p], u[p], s);
                 S[nb][m] = s;
-            }
+            });
         }
         if constexpr (WQ) O[nb] = o;
     }

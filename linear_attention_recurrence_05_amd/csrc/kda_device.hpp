@@ -146,6 +146,16 @@ __device__ __forceinline__ float row_bcast(float x) {
                                                                  0x150 + L, 0xF, 0xF, false));
 }
 
+// The same broadcast written as a DPP move: a second use of one broadcast
+// value then stays a separate instruction that can fold into its own VALU
+// operation (one broadcast with two uses becomes a move plus two operations).
+template <int L>
+__device__ __forceinline__ float row_bcast_mov(float x) {
+    static_assert(L >= 0 && L < 16, "row lane");
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + L,
+                                                              0xF, 0xF, true));
+}
+
 // Values of rows 16 M + 4 g + p (p = 0..3) of a length-D vector for lane
 // (j, g) = 16 g + j, when lane (k, g) holds rows 16 (k/2) + 4 g + 2 (k%2) +
 // {0, 1} (row_vec_offset): DPP row broadcasts deliver them, so a lane reads
@@ -154,6 +164,11 @@ template <int M>
 __device__ __forceinline__ f32x4 row_tile(const f32x2& gv) {
     return f32x4{row_bcast<2 * M>(gv[0]), row_bcast<2 * M>(gv[1]),
                  row_bcast<2 * M + 1>(gv[0]), row_bcast<2 * M + 1>(gv[1])};
+}
+template <int M>
+__device__ __forceinline__ f32x4 row_tile_mov(const f32x2& gv) {
+    return f32x4{row_bcast_mov<2 * M>(gv[0]), row_bcast_mov<2 * M>(gv[1]),
+                 row_bcast_mov<2 * M + 1>(gv[0]), row_bcast_mov<2 * M + 1>(gv[1])};
 }
 
 // Byte offset (from the start of the fp32 vector) of the two values lane
