@@ -53,12 +53,15 @@ struct RingCfg {
     static constexpr int NPW = 3;                  // producer waves
     static constexpr int WCH = NPW, WOUT = NPW + 1, WGATE = NPW + 2;
     static constexpr int THREADS = (NPW + 3) * kWave;
-    // ring slots per unit: 8 keep a unit's blocks (4 units per XCD, 0.9 MB)
-    // in the XCD's 4 MB L2 between a slot's refills; with 12 or 16 slots
-    // the streaming inputs and outputs evict most blocks while dirty and
-    // they are written back to HBM (1.7x and 1.9x the algorithmic bytes of
-    // a pass at B1 H32 T4096, against 1.34x with 8, which is 4% slower)
-    static constexpr int R = 8;
+    // ring slots per unit: a consumer waits for pair s + 1 while it holds
+    // pair s, and a slot is refilled only after every tile of the unit has
+    // released its pair, so the slots beyond two are the slack that hides
+    // the hand-off (release, the gates' rounds, the 28 KB publish).  10 are
+    // 2-3% faster than 8 at B1 H32 (1.34x against 1.19x the algorithmic
+    // bytes at T4096: some blocks are evicted dirty); 12 are slower again,
+    // and 16 move 1.9x, as the streaming inputs and outputs evict most
+    // blocks from the XCD's 4 MB L2 before their slots are refilled
+    static constexpr int R = 10;
     static constexpr int NU = 4;                   // entries chain -> output wave
     // an entry: [U_a; U_b] (bf16x8 per lane), then the packed state (NSLOT
     // bf16x8 per lane)
@@ -241,6 +244,16 @@ __device__ __forceinline__ bool lds_wait_seen(const int* flag, int target, int& 
     asm volatile("" ::: "memory");
     pin_issued();
     return live;
+}
+
+// Ties the registers of loaded operands to this point: the compiler waits
+// here for the loads that fill them (and only those), so a release of their
+// slot after it cannot let a refill overtake them.
+template <typename T>
+__device__ __forceinline__ void regs_arrived(const T& x) {
+    if constexpr (sizeof(T) == 16) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, x)));
+    else if constexpr (sizeof(T) == 8) asm volatile("" ::"v"(__builtin_bit_cast(u32x2, x)));
+    else asm volatile("" ::"v"(__builtin_bit_cast(uint32_t, x)));
 }
 
 // A flag value read ahead of its wait (the read's latency then overlaps other
@@ -456,16 +469,19 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
             // update runs
             ahead_ready = __hip_atomic_load(&lready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             ahead_udone = __hip_atomic_load(&udone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            // the pair's last operands (the update's) have arrived: its slot
+            // is released before the update runs (the others were used above)
+#pragma unroll
+            for (int m = 0; m < P::MT; ++m) regs_arrived(c.kd2[m]);
+            regs_arrived(c.gv);
             pin_issued();
+            __hip_atomic_store(&ldone[0], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             pair_supdate<E, D>(c, S[0], u2, [&](int m) {
                 ring_load_kd2<E, D>(cn, rring, nbase, m);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // the tile's product
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // then its load
             });
-            // the pair's operands are all in registers (their last use
-            // waited for them): release the slot
             pin_issued();
-            __hip_atomic_store(&ldone[0], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
         // whole pairs of steps in the loop, an odd last step after it: every
         // path into the loop head then has the same loads in flight
@@ -495,6 +511,17 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
         // these outputs).
         live = lds_wait_seen(&uready, s, seen_u, live, bad);
         ring_load_out<E, D>(cn, rring, (sn % R) * P::BYTES);
+        // this pair's operands (loaded a step ago) have arrived: its slot is
+        // released now, not after the products
+#pragma unroll
+        for (int kk = 0; kk < P::NSLOT; ++kk) {
+            regs_arrived(c.qa[kk]);
+            regs_arrived(c.qb[kk]);
+        }
+        regs_arrived(c.aqa);
+        regs_arrived(c.ob2);
+        pin_issued();
+        __hip_atomic_store(&ldone[1], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         const bf16x8* e = reinterpret_cast<const bf16x8*>(uring + (s % NU) * Cfg::UBYTES);
         const bf16x8 u2 = e[lane];
         bf16x8 sb[P::NSLOT];
@@ -506,11 +533,9 @@ __global__ __launch_bounds__((RingCfg<E, D>::THREADS)) void pair_ring_kernel(
             const float nan = __builtin_bit_cast(float, kNaNWord);
             Oa = Ob = f32x4{nan, nan, nan, nan};
         }
-        // the entry and the pair's operands are all in registers (their
-        // last use waited for them): release both
+        // the entry is in registers (its last use waited for it): release it
         pin_issued();
         __hip_atomic_store(&udone, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_store(&ldone[1], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         // outputs: rows 4g + (j & 3) of each chunk, columns 4 (j >> 2) .. +3
         // of the tile, 8 bytes per lane and chunk; rows past T are dropped
         const int t0 = 2 * s * kChunk;
