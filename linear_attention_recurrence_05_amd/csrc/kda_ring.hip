@@ -28,7 +28,8 @@
 //               tile's progress to this workgroup's producers (only the gate
 //               polls flags in L2; every other wait is on LDS).
 // The chain and output waves load their operands of a pair from the ring
-// straight into registers, one pair ahead.
+// straight into registers, one pair ahead, and each releases a pair's slot
+// as soon as the operands it still needs have arrived.
 //
 // Handover through L2 (all parties on one XCD, so one L2 serves them):
 //   publish: plain stores of the block, s_waitcnt vmcnt(0) (the stores have

@@ -15,7 +15,8 @@ pair from its slot (the chain issues the loads of the next pair a whole step
 ahead, once lready shows it; the output wave once uready shows U of the
 current pair, which the chain stores only after that wait) and hand U and the
 chain's state over NU LDS entries (flags uready and udone); each releases a
-pair (ldone) after its last use.
+pair (ldone) once the operands it still needs have arrived (the output wave
+before it reads the entry).
 
 Steps are the kernel's flag loads and stores and its slot and entry accesses
 in program order.  A slot or entry write is two steps (begun, finished): a
@@ -235,14 +236,16 @@ def ring_model(NP, NCT, NPW, R, NU, plant=None, each_read=True):
             # only after its own wait for pair s + 1; then the next pair's loads
             if lt[UREADY] < s and plant != "out_loads_first":
                 return
-            yield go(("rd", s, op + (issue(slot, nxt_pair(s), who),)))
-        elif kind == "use":           # pair s's operands used: its loads close
+            yield go(("use", s, op + (issue(slot, nxt_pair(s), who),)))
+        elif kind == "use":           # pair s's operands arrived: its loads close
             j = op.index(s)
             op = op[:j] + op[j + 1:]
             if which == 0:            # the chain's writes of entry s mod NU begin
                 yield go(("wdone", s, op), with_entry(s % NU, ("w", s)))
-            else:
-                yield go(("ud", s, op))
+            else:                     # the output wave releases the slot at once
+                yield go(("orel", s, op))
+        elif kind == "orel":
+            yield go(("rd", s, op), _set(tiles, t, _set(lt, LDONE1, s)))
         elif kind == "wdone":         # chain: the entry written, then uready
             yield go(("ur", s, op), with_entry(s % NU, s))
         elif kind == "ur":
@@ -253,11 +256,12 @@ def ring_model(NP, NCT, NPW, R, NU, plant=None, each_read=True):
             got = lt[ENTRIES][s % NU]
             if got != s:
                 raise Violation(f"{who} read entry {s % NU} for pair {s}: it held {got}")
-            yield go(("use", s, op))
-        elif kind == "ud":
-            yield go(("rel", s, op), _set(tiles, t, _set(lt, UDONE, s)))
-        elif kind == "rel":           # pair s released
-            nt = _set(tiles, t, _set(lt, LDONE0 if which == 0 else LDONE1, s))
+            yield go(("ud", s, op))
+        elif kind == "ud":            # output wave: the entry released, the products follow
+            nt = _set(tiles, t, _set(lt, UDONE, s))
+            yield go(("top", s + 1, op) if s + 1 < NP else ("drain", s, op), nt)
+        elif kind == "rel":           # chain: pair s released (before its state update)
+            nt = _set(tiles, t, _set(lt, LDONE0, s))
             yield go(("top", s + 1, op) if s + 1 < NP else ("drain", s, op), nt)
         elif kind == "drain":         # the last step's reload of its own pair lands
             yield go("end")
