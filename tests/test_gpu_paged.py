@@ -186,6 +186,39 @@ def test_decode_paged_d128_pairs_with_skipped_units():
     assert torch.equal(pool[untouched], pool0[untouched])
 
 
+def test_verify_paged_d128_pairs_with_skipped_units():
+    """The verify step at d = 128 also takes two (b, h) units per workgroup,
+    each on its own waves.  With an odd head count a live unit shares its
+    workgroup with a skipped one (a negative input slot, an out-of-range
+    output slot), and the last workgroup holds a single unit; T = 6 spans two
+    groups of staged tokens.  Live units match the oracle, skipped outputs
+    and every row no live unit writes stay as they were."""
+    dev = need_gpu()
+    B, H, d, n_slots, T = 5, 3, 128, 11, 6
+    pool, s_in, s_out = pool_and_slots(B, H, d, n_slots, dev, seed=41)
+    s_in = s_in.clone()
+    s_out = s_out.clone()
+    s_in[1] = -1
+    s_out[3] = n_slots
+    live = [0, 2, 4]
+    gen, A, _ = decode_state(B, H, d, d, seed=42, device=dev)
+    x = prefill_inputs(B, T, H, d, d, torch.bfloat16, seed=43, device=dev)
+    pool0 = pool.clone()
+    S_in = pool[s_in[live].long()].clone()
+    o = torch.full((B, T, H, d), 7.0, dtype=torch.bfloat16, device=dev)
+    kda.kda_decode_tokens_paged(x["q"], x["k"], x["v"], x["z"], x["beta"], A, -5.0, pool, s_in,
+                                s_out, o)
+    torch.cuda.synchronize()
+    sub = {kk: x[kk][live].contiguous() for kk in ("q", "k", "v", "z", "beta")}
+    o_ref, S_ref = oracle.prefill(sub["q"], sub["k"], sub["v"], sub["z"], sub["beta"], A, -5.0, S_in)
+    eo, es = rel_err(o[live], o_ref), rel_err(pool[s_out[live].long()], S_ref)
+    say(f"paged verify, d=128 T={T}, skipped units in shared workgroups: o {eo:.2e} S {es:.2e}")
+    assert eo < TOL[torch.bfloat16] and es < 1e-4
+    assert torch.all(o[1] == 7.0) and torch.all(o[3] == 7.0)
+    kept = untouched_rows(n_slots, s_out[live])
+    assert torch.equal(pool[kept], pool0[kept])
+
+
 def test_decode_and_verify_paged_against_oracle():
     """Paged decode (two steps in place) and the paged 5-token verify step
     (snapshot kept) against the fp64 oracle directly, bf16 at d = 128."""
