@@ -477,11 +477,24 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
             rowD[kk][t][0] = *reinterpret_cast<const f32x4*>(dse + off);
             rowD[kk][t][1] = *reinterpret_cast<const f32x4*>(dse + off + 4);
         }
-    bwd_factors<true>(F, &sm.R, q, k, z, beta, gc, b, h, n, T, H, tri + id * 768, nullptr);
     const ChunkPos cp = chunk_pos<kD>(b, h, n, T, H);
     const int L = cp.L;
     const int rowb = (int)(cp.rstride * 2);
     const Rsrc rdo = chunk_rsrc<kD>(dO, cp, 2);
+    const Rsrc rv = chunk_rsrc<kD>(v, cp, 2);
+    // V and dO of the wave's two 16-column blocks (rows 4g + e, column
+    // 32 w + 16 jj + i), issued here so that they arrive while the factors
+    // are formed and S, dS pass through the staging tile
+    uint32_t vraw[2][4], doraw[2][4];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int jc = 32 * w + 16 * jj + i;
+            vraw[jj][e] = buf_load<unsigned short>(rv, (4 * g + e) * rowb + jc * 2);
+            doraw[jj][e] = buf_load<unsigned short>(rdo, (4 * g + e) * rowb + jc * 2);
+        }
+    bwd_factors<true>(F, &sm.R, q, k, z, beta, gc, b, h, n, T, H, tri + id * 768, nullptr);
     // dO row i, columns 32 t + 8 g .. + 7, as an exact bf16 A operand
     auto dO_row = [&](int t) {
         return __builtin_bit_cast(bf16x8, buf_load<u32x4>(rdo, i * rowb + (32 * t + 8 * g) * 2));
@@ -546,12 +559,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         const int j0 = 32 * w + 16 * jj, jc = j0 + i;
         const f32x4 X = Xa[jj], Y = Ya[jj];
         // V and dO in the accumulator layout (rows 4g + e, column jc)
-        const Rsrc rv = chunk_rsrc<kD>(v, cp, 2);
         f32x4 Vf, dOf;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            Vf[e] = bf16_bits_to_f32(buf_load<unsigned short>(rv, (4 * g + e) * rowb + jc * 2));
-            dOf[e] = bf16_bits_to_f32(buf_load<unsigned short>(rdo, (4 * g + e) * rowb + jc * 2));
+            Vf[e] = bf16_bits_to_f32(vraw[jj][e]);
+            dOf[e] = bf16_bits_to_f32(doraw[jj][e]);
         }
         // Tm = Ninv Diag(beta) and its transpose, Aqk^T, as K = 16 A operands
         f32x4 tmf, tmtf, aqtf;
