@@ -303,12 +303,29 @@ __global__ __launch_bounds__(256) void bwd_fac_kernel(const bf16* __restrict__ q
     }
 }
 
-// The state-gradient chain: one wave per (b, h, 16 value columns), chunks
-// last to first.  dSend[(u NC + n)][k][j] receives the gradient of chunk n's
-// end state (natural [D][D] layout); dS0 (if given) the gradient of S0.  The
-// operands of the next three chunks are in flight while a chunk computes
-// (a ring of three register sets, the loop unrolled three times).
-__global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__ fac,
+// Workgroup barrier that orders LDS accesses only: this wave's LDS writes
+// are done before it, and global stores still in flight stay in flight (a
+// workgroup fence would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The state-gradient chain: one workgroup per (b, h, 16 value columns),
+// chunks last to first.  dSend[(u NC + n)] receives the gradient of chunk n's
+// end state in 16-column blocks, [D / 16][D][16] (element (k, j) at
+// ((j / 16) D + k) 16 + j % 16), so that a chain's share of a chunk is 8 KB
+// in one piece; dS0 (if given) the gradient of S0 ([D][D]).  Wave 0 runs the
+// chain: the operands of the next three chunks are in flight while a chunk
+// computes (a ring of three register sets, the loop unrolled three times),
+// and each chunk's dS goes to one of two LDS tiles (eight 16-byte writes per
+// lane).  Wave 1 copies the tile to dSend, 1 KB per store instruction, while
+// the chain goes on; one workgroup barrier (LDS only) per chunk hands a tile
+// over.  Stored by the chain itself into the [D][D] layout, as 32 four-byte
+// stores per lane and chunk (64-byte pieces of rows), the state gradients
+// took more than half of the chain's time.
+__global__ __launch_bounds__(128) void bwd_dchain_kernel(const char* __restrict__ fac,
                                                         const bf16* __restrict__ dO,
                                                         const float* __restrict__ dST,
                                                         float* __restrict__ dSend,
@@ -322,6 +339,25 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
     const int b = u / H, h = u % H;
     const int lane = lane_id(), i = lane & 15, g = lane >> 4;
     const int j0 = 16 * jb;
+    // tile t: row 16 m + r4 (r4 < 16), column c at [t][m][c][r4]
+    __shared__ __attribute__((aligned(16))) float tile[2][8 * 256];
+    if (wave_id() == 1) {
+        // -------------------------------------------- store wave
+        for (int n = NC - 1; n >= 0; --n) {
+            lds_barrier();   // the chain has written chunk n's tile
+            const float* tl = tile[n & 1];
+            float* out = dSend + ((size_t)u * NC + n) * kD * kD + (size_t)jb * kD * 16 + 4 * (lane & 3);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int r4 = lane >> 2;
+                f32x4 x;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[c] = tl[m * 256 + (4 * (lane & 3) + c) * 16 + r4];
+                *reinterpret_cast<f32x4*>(out + (16 * m + r4) * 16) = x;
+            }
+        }
+        return;
+    }
     struct Ops {
         bf16x8 kd[4], qk[8];
         bf16x4 aqt, tmt;
@@ -359,12 +395,14 @@ __global__ __launch_bounds__(64) void bwd_dchain_kernel(const char* __restrict__
     // chunk n with the operands in c; then chunk n - 3's operands load into c
     auto step = [&](int n, Ops& c) {
         if (n < 0) return;
-        // the gradient of this chunk's end state, for the gradient kernel
-        float* out = dSend + ((size_t)u * NC + n) * kD * kD + j0 + i;
+        // the gradient of this chunk's end state, for the gradient kernel:
+        // to tile n & 1, which the store wave copies out after the barrier
+        // (it finished the tile's previous chunk, n + 2, before the barrier
+        // of chunk n + 1)
+        float* tl = tile[n & 1];
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[(size_t)(16 * m + 4 * g + e) * kD] = dS[m][e];
+        for (int m = 0; m < 8; ++m) *reinterpret_cast<f32x4*>(tl + m * 256 + i * 16 + 4 * g) = dS[m];
+        lds_barrier();
         // dU = Kd dS + Aqk^T dO (separate accumulators: no 16x16x32 result
         // feeds a 16x16x16 MFMA as its accumulator input)
         f32x4 x = zero4();
@@ -435,7 +473,7 @@ static_assert(sizeof(float) * 64 * kSS <= sizeof(float) * 4 * 16 * kRF, "staging
 }  // namespace
 
 // Every gradient of chunk n of (b, h), from the chunk's start state (ckpt)
-// and the gradient of its end state (dSend), both [D][D] per (b, h, chunk).  One workgroup of four waves; wave w owns value columns and
+// and the gradient of its end state (dSend, in 16-column blocks as bwd_dchain_kernel stores it), per (b, h, chunk).  One workgroup of four waves; wave w owns value columns and
 // key channels 32w .. 32w + 31.
 __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -473,7 +511,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const size_t off = (size_t)(32 * w + 16 * kk + i) * kD + 32 * t + 8 * g;
+            // dSend in 16-column blocks: columns 32 t + 8 g .. + 7 are in
+            // block 2 t + g / 2 at 8 (g % 2)
+            const size_t off = ((size_t)(2 * t + (g >> 1)) * kD + 32 * w + 16 * kk + i) * 16 + 8 * (g & 1);
             rowD[kk][t][0] = *reinterpret_cast<const f32x4*>(dse + off);
             rowD[kk][t][1] = *reinterpret_cast<const f32x4*>(dse + off + 4);
         }
@@ -753,7 +793,7 @@ hipError_t launch_bwd_chunk(const BackwardArgs& a, const float* ckpt, char* fac,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned chains = (unsigned)(((units + 7) / 8) * 8 * (kD / 16));
-    hipLaunchKernelGGL(bwd_dchain_kernel, dim3(chains), dim3(64), 0, stream, fac, dO, a.dST, dSend,
+    hipLaunchKernelGGL(bwd_dchain_kernel, dim3(chains), dim3(128), 0, stream, fac, dO, a.dST, dSend,
                        a.dS0, a.B, a.T, a.H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(units * NC)), dim3(256), 0, stream, q, k, v,
