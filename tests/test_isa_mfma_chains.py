@@ -62,14 +62,11 @@ def test_scanner_flags_a_planted_chain():
 
 @pytest.mark.parametrize("source", ["kda_prefill.hip", "kda_pair.hip", "kda_bwd_chunk.hip"])
 def test_prefill_kernels_have_no_mixed_shape_srcc_chain(tmp_path, source):
-    cmd = kbuild.hipcc_command(str(tmp_path / "unused.so"))
-    # same flags, device-only assembly of one prefill translation unit
-    flags = [c for c in cmd[1:] if c not in ("-shared",) and not c.endswith(".hip")]
-    out_i = flags.index("-o")
-    flags = flags[:out_i] + flags[out_i + 2:]
+    # the flags the library build gives this source, device-only assembly
+    hipcc = os.environ.get("HIPCC", "hipcc")
     src = os.path.join(kbuild.CSRC, source)
     asm = tmp_path / "prefill.s"
-    subprocess.run([cmd[0], *flags, "--cuda-device-only", "-S", src, "-o", str(asm)],
+    subprocess.run([hipcc, *kbuild.source_flags(source), "--cuda-device-only", "-S", src, "-o", str(asm)],
                    check=True, capture_output=True)
     text = asm.read_text().split("\n")
     assert any("v_mfma_f32_16x16x32_bf16" in l for l in text)
